@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size workload (seconds to a minute)")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    lib = oracle.lib()
+    assert lib is not None
+    assert oracle.fpenv_ok(), "host FTZ/DAZ is on; binary32 reference arithmetic would be wrong"
+    return oracle
