@@ -632,8 +632,13 @@ size_t orc_bucket_plan(const size_t* counts, size_t nt, int dt, size_t cap_bytes
   return nb;
 }
 
+/* Offset of each tensor inside its bucket: tensors are laid end to end, each
+ * starting on a 16-byte boundary; the gap after a tensor is zero. */
+static size_t padded_elems(size_t count, size_t es) { return (count * es + 15) / 16 * 16 / es; }
+
 /* tensors[r * nt + t] is rank r's tensor t.  Each bucket is packed into a
- * flat buffer per rank, ring-allreduced, and unpacked. */
+ * flat buffer per rank (16-byte aligned tensor offsets, zero gaps),
+ * ring-allreduced, and unpacked. */
 int orc_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt, int n, int dt,
                            size_t cap_bytes, uint64_t* sent, uint64_t* recv) {
   if (n < 1 || n > ORC_MAXN || !dtype_ok(dt)) return ORC_EINVAL;
@@ -644,13 +649,13 @@ int orc_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt
   void* flat[ORC_MAXN];
   for (size_t b = 0; b < nb; ++b) {
     size_t t1 = t0, total = 0;
-    while (t1 < nt && bof[t1] == (int)b) total += counts[t1++];
+    while (t1 < nt && bof[t1] == (int)b) total += padded_elems(counts[t1++], es);
     for (int r = 0; r < n; ++r) {
-      flat[r] = malloc(total * es + 1);
+      flat[r] = calloc(total * es + 1, 1);
       size_t off = 0;
       for (size_t t = t0; t < t1; ++t) {
         memcpy((char*)flat[r] + off * es, tensors[(size_t)r * nt + t], counts[t] * es);
-        off += counts[t];
+        off += padded_elems(counts[t], es);
       }
     }
     orc_ring_allreduce(flat, n, total, dt, sent, recv);
@@ -658,7 +663,7 @@ int orc_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt
       size_t off = 0;
       for (size_t t = t0; t < t1; ++t) {
         memcpy(tensors[(size_t)r * nt + t], (char*)flat[r] + off * es, counts[t] * es);
-        off += counts[t];
+        off += padded_elems(counts[t], es);
       }
       free(flat[r]);
     }

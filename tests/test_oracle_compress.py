@@ -391,7 +391,7 @@ def test_bucketed_allreduce_integer_exact(orc):
     for r in range(n):
         tot_r = 0
         for b in range(nb):
-            tot = sum(s for s, p in zip(sizes, plan) if p == b)
+            tot = sum((s * 4 + 15) // 16 * 4 for s, p in zip(sizes, plan) if p == b)  # 16-byte aligned offsets
             L = math.ceil(math.ceil(tot / n) / 128) * 128
 
             def ch(c):
