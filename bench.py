@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring all-reduce hot path on one MI355X.
+
+Headline: ring allreduce, N=8 simulated ranks, T=64M fp32 per rank (256 MiB),
+gradient-like values N(0, 1e-3) with 1% outliers x100, fused schedule.  The
+metric is the per-rank bus bandwidth 2*S*(N-1)/N / t (S = bytes per rank)
+and the fraction of the HBM roofline the fused kernel reaches.  A second
+leg times the BFP-8 compressed allreduce (N=8, T=128M fp16, 128-element
+blocks, block-scaled values).  Inputs are generated on the host once, copied
+into a pool of device sets, and every timed step runs on a fresh set, so no
+restore happens inside the timed region.
+
+Prints ONE JSON line.  --gpus above 1 is refused: all simulated ranks share
+one GPU's HBM.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "all-reduce bus GB/s (2T(N-1)/N per rank) and % of HBM peak, fp32 & BFP8"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def host_info():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_threads": os.cpu_count()}
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(key, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def make_sets(pristine, nsets):
+    """nsets device copies of the rank buffers (one allocation per set)."""
+    import torch
+    n, count = len(pristine), pristine[0].numel()
+    sets = []
+    for _ in range(nsets):
+        big = torch.empty(n * count, dtype=pristine[0].dtype, device=pristine[0].device)
+        views = [big[r * count:(r + 1) * count] for r in range(n)]
+        for v, p in zip(views, pristine):
+            v.copy_(p)
+        sets.append(views)
+    return sets
+
+
+def time_leg(run, sets, warmup, steps):
+    """Warm up on set 0, then time `steps` calls, each on a fresh set.
+    Returns wall ms per step and the HIP-event kernel ms (mean, min)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run(sets[0])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        run(sets[1 + i % (len(sets) - 1)])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return (t1 - t0) * 1e3 / steps, sum(ev) / len(ev), min(ev)
+
+
+def busbw(bytes_per_rank, n, ms):
+    return 2.0 * bytes_per_rank * (n - 1) / n / (ms * 1e-3) / 1e9
+
+
+def fp32_leg(args):
+    import numpy as np
+    import torch
+
+    import ring_all_reduce_scatter_amd as rar
+    from ring_all_reduce_scatter_amd import inputs
+
+    w = inputs.WORKLOADS["ring_grad"]
+    n, count = w["n"], w["count"]
+    log(f"[bench] fp32 leg: generating N={n} x T={count} inputs")
+    xs = inputs.gradient_like(n, count)
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xs]
+    nsets = 1 + min(args.steps, args.max_sets)
+    sets = make_sets(pristine, nsets)
+    del pristine
+    S = count * 4
+    log(f"[bench] fp32 leg: timing {args.steps} steps on {nsets - 1} sets")
+    ms, kern_ms, kern_min = time_leg(lambda bufs: rar.ring_allreduce(bufs), sets, args.warmup, args.steps)
+    first = [t.cpu().numpy() for t in sets[1]]
+    del sets
+    torch.cuda.empty_cache()
+    alg_bytes = 2 * n * S  # every rank's input read once and output written once
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    sources = ["ring_all_reduce_scatter_amd/csrc/ring_kernels.hip", "ring_all_reduce_scatter_amd/csrc/common.hpp"]
+    res = {
+        "n": n, "count": count, "S": S, "ms": ms, "kern_ms": kern_ms, "kern_min_ms": kern_min,
+        "busbw": busbw(S, n, ms),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("ring_fold_f32_n8", sources),
+                     "kernel": "ring_fold_kernel<f32, N=8>", "algorithmic_bytes_per_launch": alg_bytes},
+    }
+    parity = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] fp32 leg: oracle on the full workload (single thread), 3 runs")
+        times = []
+        ref = None
+        for _ in range(3):
+            bufs = [x.copy() for x in xs]
+            t = time.perf_counter()
+            oracle.ring_allreduce(bufs)
+            times.append(time.perf_counter() - t)
+            ref = bufs
+        med = sorted(times)[1]
+        cpu = {"value": round(busbw(S, n, med * 1e3), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole workload (N={n}, T={count} fp32 per rank), median of 3 single-thread runs "
+                         f"({med:.2f} s each)", **host_info()}
+        parity = all(np.array_equal(first[r].view(np.uint32), ref[r].view(np.uint32)) for r in range(n))
+    if parity is None:
+        parity = sampled_fp32_parity(xs, first, rar.chunk_len(count, n))
+        res["parity_first_timed_output"] = parity
+    else:
+        res["parity_first_timed_output"] = "bit-exact (all elements)" if parity else "MISMATCH"
+    res["cpu_baseline"] = cpu
+    return res
+
+
+def sampled_fp32_parity(xs, first, L, K=4096):
+    """Windows of K elements from every chunk re-run in a small ring where
+    each window keeps its chunk index (elements are independent)."""
+    import numpy as np
+
+    import oracle
+    n, count = len(xs), xs[0].size
+    g = np.random.default_rng(5)
+    mini = [np.zeros(n * K, dtype=np.float32) for _ in range(n)]
+    offs = []
+    for c in range(n):
+        hi = min((c + 1) * L, count)
+        o = c * L + int(g.integers(0, max(1, hi - c * L - K)))
+        offs.append(o)
+        for r in range(n):
+            mini[r][c * K:(c + 1) * K] = xs[r][o:o + K]
+    oracle.ring_allreduce(mini)
+    for c in range(n):
+        for r in range(n):
+            if not np.array_equal(first[r][offs[c]:offs[c] + K].view(np.uint32), mini[r][c * K:(c + 1) * K].view(np.uint32)):
+                return "MISMATCH"
+    return f"bit-exact on {n} sampled windows of {K} elements on every rank"
+
+
+def bfp8_leg(args):
+    import numpy as np
+    import torch
+
+    import ring_all_reduce_scatter_amd as rar
+    from ring_all_reduce_scatter_amd import inputs
+
+    w = inputs.WORKLOADS["bfp8"]
+    n, count, mbits, block = w["n"], w["count"], w["mbits"], w["block"]
+    log(f"[bench] bfp8 leg: generating N={n} x T={count} fp16 inputs")
+    xs = inputs.block_scaled(n, count)
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xs]
+    nsets = 1 + min(args.steps, args.max_sets)
+    sets = make_sets(pristine, nsets)
+    del pristine
+    cfg = rar.compress_cfg(block=block, mbits=mbits, unit_bytes=w["unit_bytes"], schedule=rar.SCHED_FUSED)
+    ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
+    S = count * 2
+    log(f"[bench] bfp8 leg: timing {args.steps} steps")
+    ms, kern_ms, kern_min = time_leg(lambda bufs: rar.ring_allreduce_compressed(bufs, cfg, ws), sets,
+                                     args.warmup, args.steps)
+    sent, _ = rar.compressed_traffic(ws, n)
+    got0 = sets[1][0].cpu().numpy()
+    same = all(torch.equal(sets[1][r].view(torch.int16), sets[1][0].view(torch.int16)) for r in range(n))
+    del sets
+    torch.cuda.empty_cache()
+    alg_bytes = 2 * n * S
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    sources = ["ring_all_reduce_scatter_amd/csrc/bfp_kernels.hip", "ring_all_reduce_scatter_amd/csrc/common.hpp"]
+    res = {
+        "metric": "BFP-8 compressed all-reduce effective bus GB/s (2T(N-1)/N fp16 bytes per rank)",
+        "value": round(busbw(S, n, ms), 2), "unit": "GB/s", "ms_per_step": round(ms, 4),
+        "dtype": "f16 buffers, 8-bit BFP messages",
+        "wire_busbw_GBs": round(sent[0] / (ms * 1e-3) / 1e9, 2),
+        "wire_bytes_per_rank": sent[0],
+        "config": {"workload": f"compressed ring allreduce, N={n} ranks, T={count} fp16 per rank (256 MiB), "
+                               f"block {block}, {mbits}-bit mantissas, x = s_b*N(0,1e-3), s_b=2^U(-12,0)",
+                   "schedule": "fused"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("bfp_ring_fold_f16_n8", sources),
+                     "kernel": "bfp_ring_fold_kernel<f16, N=8, block 128>", "algorithmic_bytes_per_launch": alg_bytes},
+        "ranks_identical": bool(same),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = count // 16
+        log(f"[bench] bfp8 leg: oracle on a sample of T={sample} per rank")
+        xs_s = inputs.block_scaled(n, sample, salt=1)
+        t = time.perf_counter()
+        oracle.ring_allreduce_compressed(xs_s, mbits=mbits, unit=w["unit_bytes"] // 2)
+        dt = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": round(busbw(sample * 2, n, dt * 1e3), 5), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"N={n}, T={sample} fp16 per rank (1/16 of the workload, same value "
+                                         f"recipe), one single-thread run ({dt:.1f} s)"}
+    res["parity_first_timed_output"] = sampled_bfp_parity(xs, got0, rar.compressed_chunk_len(count, n, block), mbits)
+    return res
+
+
+def sampled_bfp_parity(xs, got0, L, mbits, per_chunk=64):
+    """Re-run sampled blocks through the oracle in a small ring where each
+    block keeps its chunk index (blocks are independent in the BFP ring)."""
+    import numpy as np
+
+    import oracle
+    n, count = len(xs), xs[0].size
+    g = np.random.default_rng(7)
+    K = per_chunk
+    mini = [np.zeros(n * K * 128, dtype=np.float16) for _ in range(n)]
+    picks = []
+    for c in range(n):
+        nblk = (min((c + 1) * L, count) - c * L) // 128
+        bl = np.sort(g.choice(nblk, size=K, replace=False)) + c * L // 128
+        picks.append(bl)
+        for r in range(n):
+            for k, b in enumerate(bl):
+                mini[r][(c * K + k) * 128:(c * K + k + 1) * 128] = xs[r][b * 128:(b + 1) * 128]
+    oracle.ring_allreduce_compressed(mini, mbits=mbits, unit=K * 128)
+    for c in range(n):
+        for k, b in enumerate(picks[c]):
+            a = got0[b * 128:(b + 1) * 128].view(np.uint16)
+            e = mini[0][(c * K + k) * 128:(c * K + k + 1) * 128].view(np.uint16)
+            if not np.array_equal(a, e):
+                return "MISMATCH"
+    return f"bit-exact on {n * K} sampled blocks"
+
+
+def extra_legs(args):
+    """Secondary schedules and collectives (reported, not the headline)."""
+    import torch
+
+    import ring_all_reduce_scatter_amd as rar
+    from ring_all_reduce_scatter_amd import inputs
+
+    out = {}
+    steps = max(3, min(args.steps, 10))
+    w = inputs.WORKLOADS["ring_grad"]
+    n, count = w["n"], w["count"]
+    xs = inputs.gradient_like(n, count)
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xs]
+    sets = make_sets(pristine, 1 + steps)
+    S = count * 4
+    ms, k, _ = time_leg(lambda b: rar.ring_allreduce_ex(b, rar.ALGO_STEPWISE), sets, 2, steps)
+    out["fp32_allreduce_stepwise"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S, n, ms), 1),
+                                      "frac_of_roofline": round(2 * n * S / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms, k, _ = time_leg(lambda b: rar.reduce_scatter(b), sets, 2, steps)
+    out["fp32_reduce_scatter_fused"] = {"ms": round(ms, 4),
+                                        "busbw_GBs": round(S * (n - 1) / n / (ms * 1e-3) / 1e9, 1),
+                                        "frac_of_roofline": round((n * S + S) / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, pristine
+    torch.cuda.empty_cache()
+    wb = inputs.WORKLOADS["bfp8"]
+    xb = inputs.block_scaled(wb["n"], wb["count"])
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xb]
+    sets = make_sets(pristine, 1 + steps)
+    cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"], schedule=rar.SCHED_STAGED)
+    ws = torch.empty(rar.compressed_workspace_bytes(wb["n"], wb["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    ms, k, _ = time_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, 2, steps)
+    Sb = wb["count"] * 2
+    out["bfp8_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
+                                    "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, pristine, ws
+    torch.cuda.empty_cache()
+    w5 = inputs.WORKLOADS["sparse_bfp4"]
+    for name, fn, cnt in (("fp32_broadcast_fused", lambda b: rar.broadcast(b, 0), w5["bcast_count"]),
+                          ("fp32_allgather_fused", lambda b: rar.allgather(b), w5["ag_shard"] * 8)):
+        xf = inputs.filler(8, cnt)
+        pristine = [torch.from_numpy(x).to("cuda:0") for x in xf]
+        sets = make_sets(pristine, 1 + steps)
+        ms, k, _ = time_leg(fn, sets, 2, steps)
+        Sx = cnt * 4
+        moved = 8 * Sx if name.endswith("broadcast_fused") else 2 * 8 * Sx * 7 // 8 + Sx
+        bus = Sx / (ms * 1e-3) / 1e9 if "broadcast" in name else Sx * 7 / 8 / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "busbw_GBs": round(bus, 1),
+                     "frac_of_roofline": round(moved / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del sets, pristine
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--max-sets", type=int, default=24, help="device input sets per leg (2 GiB each)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-bfp8", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also time stepwise, staged and other collectives")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the N simulated ranks share one MI355X's HBM, so --gpus "
+              f"{args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ring_all_reduce_scatter_amd as rar
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rar.lib()
+
+    f = fp32_leg(args)
+    line = {
+        "metric": METRIC,
+        "value": round(f["busbw"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1e-3) gradients, 1% outliers x100)",
+        "config": {"workload": f"ring allreduce, N={f['n']} simulated ranks on one GPU, T={f['count']} fp32 per rank "
+                               f"(256 MiB), fused schedule", "n_ranks": f["n"], "count_per_rank": f["count"],
+                   "schedule": "fused"},
+        "busbw_aggregate_GBs": round(f["busbw"] * f["n"], 1),
+        "pct_hbm_peak": round(100 * f["roofline"]["frac"], 2),
+        "kernel_ms": round(f["kern_ms"], 4),
+        "roofline": f["roofline"],
+        "cpu_baseline": f["cpu_baseline"],
+        "parity": f["parity_first_timed_output"],
+    }
+    if not args.skip_bfp8:
+        line["bfp8"] = bfp8_leg(args)
+    if args.extra:
+        line["extra"] = extra_legs(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

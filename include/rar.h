@@ -1,0 +1,257 @@
+/*
+ * rar.h -- C-ABI of the MI355X ring all-reduce library (librar.so).
+ *
+ * N simulated data-parallel ranks live in one GPU's HBM: rank r's tensor is
+ * the device buffer bufs[r].  Every collective works on the array of N rank
+ * buffers at once and does one GPU's share of the ring's work at its real
+ * shape.
+ *
+ * Sources (page title, section):
+ *  [P2] "从零实现集合通信" (collective ops from scratch): two-pass ring
+ *       allreduce (reduce-scatter then allgather over T/N chunks), the
+ *       per-primitive byte table, broadcast over a log2(N) tree, allgather by
+ *       N-1 rotations, reduce_scatter as the first half of the allreduce,
+ *       bucketing gradients into ~25 MB buckets (production patterns).
+ *  [P4] "CCCL通信压缩库：突破LLM训练通信墙的工程实践": section 2.1 layered
+ *       compression (sparse value+index when sparsity exceeds a threshold;
+ *       block floating point with a shared exponent per block of e.g. 128
+ *       elements and 8- or 4-bit mantissas; operator-aware choice), section
+ *       2.2 chunked compress -> communicate -> decompress -> reduce pipeline on
+ *       separate streams synchronised by events, section 3.3 configuration
+ *       (compression type, sparsity threshold, collective filter, 1-4 MB
+ *       chunks), section 4.3 (compressed staging buffers cost memory).
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device addresses, 16-byte aligned.  Host arrays
+ *    (the `bufs` pointer table, counts, configs, outputs of *_traffic) are
+ *    read or written during the call only and may be reused on return.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously and is stream-ordered: buffers must stay alive until the
+ *    stream has executed it.  The library allocates no device memory; where
+ *    scratch is needed the caller passes a workspace.
+ *  - Errors in the arguments are reported synchronously, before anything is
+ *    enqueued, by a nonzero rar_status; nothing is modified then.  A failed
+ *    kernel launch returns RAR_EHIP.  No call aborts or throws.
+ *  - count == 0 and nranks == 1 are valid and leave the buffers unchanged.
+ *  - Element types: RAR_F32 (binary32), RAR_F16 (binary16), RAR_BF16
+ *    (bfloat16).  The reduce op is SUM.  fp32 adds are IEEE binary32
+ *    round-to-nearest-even with subnormals kept; fp16/bf16 adds widen both
+ *    operands to binary32, add, and round back to nearest-even.  No FMA
+ *    contraction, no reassociation.
+ *  - Chunk rule: chunk c of a T-element buffer is [c*L, min((c+1)*L, T)) with
+ *    L = rar_chunk_len(T, N) = roundup(ceil(T/N), 128); trailing chunks may be
+ *    short or empty.  This fixes each element's summation order, so results
+ *    are deterministic and identical across schedules.
+ */
+#ifndef RAR_H
+#define RAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RAR_MAX_RANKS 64
+
+typedef enum rar_status {
+  RAR_OK = 0,
+  RAR_EINVAL = 1,     /* bad size, rank count, root, step, block, mbits, config */
+  RAR_EDTYPE = 2,     /* unknown element type */
+  RAR_EALIGN = 3,     /* a device pointer is not 16-byte aligned */
+  RAR_EWORKSPACE = 4, /* workspace missing or smaller than required */
+  RAR_EHIP = 5,       /* the HIP runtime reported an error (launch, event, stream) */
+  RAR_ENOTSUP = 6,    /* valid request that this library does not implement */
+  RAR_EOVERLAP = 7    /* two rank buffers overlap, or a buffer is NULL */
+} rar_status;
+
+typedef enum rar_dtype { RAR_F32 = 0, RAR_F16 = 1, RAR_BF16 = 2 } rar_dtype;
+
+/* Schedules.  Both give bit-identical results.
+ * FUSED: one launch; each chunk's ring-ordered fold is kept in registers and
+ *        stored once per rank (reads N*S, writes N*S bytes of HBM).
+ * STEPWISE: one launch per ring step, every step materialised in the rank
+ *        buffers exactly as the ring's sends and receives would leave them. */
+typedef enum rar_algo { RAR_ALGO_FUSED = 0, RAR_ALGO_STEPWISE = 1 } rar_algo;
+
+/* Elements per chunk for a T-element buffer split over N ranks
+ * (roundup(ceil(T/N), 128)); 0 if nranks is out of range. */
+size_t rar_chunk_len(size_t count, int nranks);
+
+/* ---------------------------------------------------------------------- */
+/* Uncompressed collectives ([P2] two-pass ring and byte table).           */
+/* bufs: host array of nranks device pointers, each to `count` elements.  */
+/* ---------------------------------------------------------------------- */
+
+/* Ring allreduce, in place: afterwards every rank holds the same sum.
+ * Chunk c's sum is the fold, in ring order, of ranks c+1, c+2, ..., c+N-1, c
+ * (mod N): the order the reduce-scatter steps produce.  FUSED schedule. */
+int rar_ring_allreduce(void* const* bufs, int nranks, size_t count, int dtype, void* stream);
+int rar_ring_allreduce_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo,
+                          void* stream);
+
+/* Reduce-scatter, in place: afterwards chunk r of rank r holds the full sum
+ * of chunk r.  Other chunks are left unspecified (FUSED leaves them as they
+ * were; STEPWISE leaves the ring's partial sums). */
+int rar_reduce_scatter(void* const* bufs, int nranks, size_t count, int dtype, void* stream);
+int rar_reduce_scatter_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo,
+                          void* stream);
+
+/* Allgather, in place: each buffer holds N shards of count/N elements
+ * (count must be divisible by nranks); rank r's own shard is shard r.
+ * Afterwards every buffer holds all N shards.  STEPWISE = N-1 rotations. */
+int rar_allgather(void* const* bufs, int nranks, size_t count, int dtype, void* stream);
+int rar_allgather_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo,
+                     void* stream);
+
+/* Broadcast of bufs[root] to every rank.  STEPWISE = binomial tree: in round
+ * k every rank at distance < 2^k from the root sends to distance + 2^k
+ * (ceil(log2 N) rounds); FUSED = one read of the root, N-1 writes. */
+int rar_broadcast(void* const* bufs, int nranks, size_t count, int dtype, int root, void* stream);
+int rar_broadcast_ex(void* const* bufs, int nranks, size_t count, int dtype, int root, int algo,
+                     void* stream);
+
+/* Single ring steps (the schedule's building blocks), step = 1..N-1.
+ * RS step s: every rank r adds chunk (r-s-1) mod N received from rank
+ * (r-1) mod N into its own copy (local + received).
+ * AG step s: every rank r stores chunk (r-s) mod N received from rank
+ * (r-1) mod N.  Running RS steps 1..N-1 then AG steps 1..N-1 equals
+ * rar_ring_allreduce. */
+int rar_rs_step(void* const* bufs, int nranks, size_t count, int dtype, int step, void* stream);
+int rar_ag_step(void* const* bufs, int nranks, size_t count, int dtype, int step, void* stream);
+
+/* Logical bytes each rank sent and received in the last collective issued
+ * by the calling host thread (uncompressed calls; the counters of the
+ * compressed allreduce are read with rar_compressed_traffic).  sent/recv:
+ * host arrays of at least nranks entries.  Matches [P2]'s byte table:
+ * allreduce 2T(N-1)/N, reduce-scatter and allgather T(N-1)/N, broadcast T
+ * received per non-root rank (bytes; exact when chunks are equal). */
+int rar_last_traffic(uint64_t* sent, uint64_t* recv, int nranks);
+
+/* ---------------------------------------------------------------------- */
+/* Block floating point ([P4] section 2.1, numeric-precision layer).       */
+/* A block of `block` consecutive elements (power of two, 16..512; 128 on  */
+/* the pages) shares E, the biased binary32 exponent of its largest        */
+/* magnitude; with e = max(E,1) - 127 each element is stored as            */
+/*   q = clamp(round_half_even(x * 2^(m-2-e)), -(2^(m-1)-1), 2^(m-1)-1)    */
+/* and stands for q * 2^(e+2-m).  m = mbits (2..8) counts the sign bit.    */
+/* Per element |decoded - x| <= 2^-(m-1) * max|x over the block|.          */
+/* Blocks holding Inf or NaN get E = 255 and decode to NaN.                */
+/* Message layout: uint8 E[nblocks] zero-padded to a multiple of 16 bytes, */
+/* then the mantissas: one int8 per element for m > 4, else two's-         */
+/* complement nibbles (element 2j in bits 3:0, element 2j+1 in bits 7:4,   */
+/* an odd tail's high nibble zero).  The last block may be partial.        */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of a message for `count` elements; 0 if block/mbits are invalid. */
+size_t rar_bfp_bytes(size_t count, int block, int mbits);
+
+/* Encode src (count elements of src_dtype) into dst (rar_bfp_bytes bytes). */
+int rar_bfp_compress(const void* src, int src_dtype, size_t count, int block, int mbits, void* dst,
+                     void* stream);
+
+/* acc[i] <- acc[i] (+) decoded[i]: binary32 add of the exact decoded value,
+ * rounded to acc_dtype. */
+int rar_bfp_decompress_accumulate(const void* src, size_t count, int block, int mbits, void* acc,
+                                  int acc_dtype, void* stream);
+
+/* dst[i] <- decoded[i] rounded to dst_dtype. */
+int rar_bfp_decompress(const void* src, size_t count, int block, int mbits, void* dst,
+                       int dst_dtype, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Compression-coupled ring allreduce ([P4] sections 2.1-2.2, 3.3, 4.3).   */
+/* ---------------------------------------------------------------------- */
+
+typedef enum rar_comp {
+  RAR_COMP_NONE = 0,        /* plain ring allreduce */
+  RAR_COMP_BFP = 1,         /* every message block floating point */
+  RAR_COMP_SPARSE_AUTO = 2  /* per message: values + uint32 indices when
+                               zeros > threshold * len, else BFP */
+} rar_comp;
+
+enum { RAR_OP_ALLREDUCE = 1u, RAR_OP_ALLGATHER = 2u, RAR_OP_BROADCAST = 4u };
+
+typedef enum rar_sched {
+  RAR_SCHED_FUSED = 0,  /* one launch, per-block hop chain in registers (BFP only) */
+  RAR_SCHED_STAGED = 1  /* messages materialised per pipeline unit; encode and
+                           decode on two streams ordered by events */
+} rar_sched;
+
+typedef struct rar_compress_cfg {
+  int method;                /* rar_comp */
+  int block;                 /* elements per BFP block: power of two, 16..512 */
+  int mbits;                 /* mantissa bits incl. sign, 2..8 */
+  float sparsity_threshold;  /* SPARSE_AUTO: sparse iff zeros > threshold * len */
+  size_t unit_bytes;         /* pipeline unit, bytes of the uncompressed dtype;
+                                unit_bytes/elem_size must be a multiple of block */
+  unsigned collective_mask;  /* RAR_OP_* bits allowed to compress; without
+                                RAR_OP_ALLREDUCE the call runs uncompressed */
+  int schedule;              /* rar_sched */
+} rar_compress_cfg;
+
+/* Fill cfg with the pages' starting point: BFP, block 128, 8 bits,
+ * threshold 0.5, 4 MiB units, allreduce only, fused schedule. */
+void rar_compress_cfg_default(rar_compress_cfg* cfg);
+
+/* Chunk length of the compressed ring: roundup(ceil(T/N), max(128, block)). */
+size_t rar_compressed_chunk_len(size_t count, int nranks, int block);
+
+/* Device workspace bytes the compressed allreduce needs (0 on bad args). */
+size_t rar_compressed_workspace_bytes(int nranks, size_t count, int dtype,
+                                      const rar_compress_cfg* cfg);
+
+/* In-place compressed ring allreduce.  Reduce-scatter hop s: the sender
+ * (rank r-1) encodes its current partial of chunk (r-s-1) mod N one unit at
+ * a time, rank r decodes each message and adds it to its own copy.
+ * Allgather: the owner encodes each finished unit once, the bytes travel
+ * unchanged, and every rank (owner included) stores the decoded unit, so all
+ * ranks end bit-identical.  Deterministic: the same inputs always give the
+ * same bits, whatever the schedule.  The wire byte counters are left in the
+ * workspace (see rar_compressed_traffic). */
+int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, int dtype,
+                                  const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/* Wire bytes each rank sent and received in the last compressed allreduce
+ * that used this workspace.  Synchronises `stream` first. */
+int rar_compressed_traffic(const void* workspace, int nranks, uint64_t* sent, uint64_t* recv,
+                           void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Gradient bucketing ([P2] production patterns: fuse small gradients     */
+/* into ~25 MB buckets, one allreduce per bucket).                        */
+/* ---------------------------------------------------------------------- */
+
+/* Greedy plan in tensor order: a bucket is closed when the next tensor
+ * would push it past cap_bytes; a tensor larger than the cap travels alone.
+ * bucket_of[t] receives tensor t's bucket.  Returns the bucket count. */
+size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t cap_bytes,
+                       int* bucket_of);
+
+/* Workspace for rar_bucketed_allreduce (0 on bad args). */
+size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
+                                    size_t cap_bytes);
+
+/* tensors: host array of nranks*ntensors device pointers, rank-major
+ * (tensors[r*ntensors + t] is rank r's tensor t of counts[t] elements).
+ * Each bucket is packed into a flat per-rank buffer in the workspace,
+ * ring-allreduced (chunk rule on the bucket), and unpacked in place. */
+int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors,
+                           int nranks, int dtype, size_t cap_bytes, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+
+/* Static description of a status code. */
+const char* rar_status_string(int status);
+
+/* Library version string. */
+const char* rar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAR_H */

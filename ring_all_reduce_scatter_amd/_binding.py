@@ -1,0 +1,297 @@
+"""ctypes binding of librar.so (the C-ABI declared in include/rar.h).
+
+Argument marshalling only: torch tensors supply device pointers and HIP
+streams, and every step of every collective runs in the library's kernels.
+Python names are the C names without the ``rar_`` prefix.  If the library is
+not built, every call raises RuntimeError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librar.so")
+
+F32, F16, BF16 = 0, 1, 2
+ALGO_FUSED, ALGO_STEPWISE = 0, 1
+COMP_NONE, COMP_BFP, COMP_SPARSE_AUTO = 0, 1, 2
+OP_ALLREDUCE, OP_ALLGATHER, OP_BROADCAST = 1, 2, 4
+SCHED_FUSED, SCHED_STAGED = 0, 1
+MAX_RANKS = 64
+
+_c_vp = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+_c_int = ctypes.c_int
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+
+
+class CompressCfg(ctypes.Structure):
+    """Mirror of rar_compress_cfg."""
+    _fields_ = [
+        ("method", ctypes.c_int),
+        ("block", ctypes.c_int),
+        ("mbits", ctypes.c_int),
+        ("sparsity_threshold", ctypes.c_float),
+        ("unit_bytes", ctypes.c_size_t),
+        ("collective_mask", ctypes.c_uint),
+        ("schedule", ctypes.c_int),
+    ]
+
+
+class RarError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_SIGS = {
+    "rar_chunk_len": (_c_size, [_c_size, _c_int]),
+    "rar_ring_allreduce": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_vp]),
+    "rar_ring_allreduce_ex": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_reduce_scatter": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_vp]),
+    "rar_reduce_scatter_ex": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_allgather": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_vp]),
+    "rar_allgather_ex": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_broadcast": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_broadcast_ex": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_int, _c_vp]),
+    "rar_rs_step": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_ag_step": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_last_traffic": (_c_int, [_u64p, _u64p, _c_int]),
+    "rar_bfp_bytes": (_c_size, [_c_size, _c_int, _c_int]),
+    "rar_bfp_compress": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp, _c_vp]),
+    "rar_bfp_decompress_accumulate": (_c_int, [_c_vp, _c_size, _c_int, _c_int, _c_vp, _c_int, _c_vp]),
+    "rar_bfp_decompress": (_c_int, [_c_vp, _c_size, _c_int, _c_int, _c_vp, _c_int, _c_vp]),
+    "rar_compress_cfg_default": (None, [ctypes.POINTER(CompressCfg)]),
+    "rar_compressed_chunk_len": (_c_size, [_c_size, _c_int, _c_int]),
+    "rar_compressed_workspace_bytes": (_c_size, [_c_int, _c_size, _c_int, ctypes.POINTER(CompressCfg)]),
+    "rar_ring_allreduce_compressed": (_c_int, [_c_vp, _c_int, _c_size, _c_int, ctypes.POINTER(CompressCfg),
+                                               _c_vp, _c_size, _c_vp]),
+    "rar_compressed_traffic": (_c_int, [_c_vp, _c_int, _u64p, _u64p, _c_vp]),
+    "rar_bucket_plan": (_c_size, [_c_vp, _c_size, _c_int, _c_size, _c_vp]),
+    "rar_bucketed_workspace_bytes": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size]),
+    "rar_bucketed_allreduce": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_vp, _c_size,
+                                        _c_vp]),
+    "rar_status_string": (ctypes.c_char_p, [_c_int]),
+    "rar_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises RuntimeError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m ring_all_reduce_scatter_amd.build)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rar_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().rar_version().decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RarError(rc, what)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(stream, t):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream) if isinstance(stream, int) else stream.cuda_stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rank_ptrs(bufs: Sequence):
+    if len(bufs) < 1:
+        raise ValueError("need at least one rank buffer")
+    t0 = bufs[0]
+    for b in bufs:
+        if b.dtype != t0.dtype or b.numel() != t0.numel() or b.device != t0.device:
+            raise ValueError("rank buffers must share dtype, size and device")
+        if not b.is_contiguous():
+            raise ValueError("rank buffers must be contiguous")
+    return (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+
+
+def _call_bufs(name: str, bufs, *extra, stream=None):
+    rc = getattr(lib(), name)(_rank_ptrs(bufs), len(bufs), bufs[0].numel(), dtype_code(bufs[0]), *extra,
+                              _stream(stream, bufs[0]))
+    _check(rc, name)
+
+
+# ------------------------------------------------------------------ uncompressed collectives
+
+def chunk_len(count: int, nranks: int) -> int:
+    return lib().rar_chunk_len(count, nranks)
+
+
+def ring_allreduce(bufs, stream=None):
+    _call_bufs("rar_ring_allreduce", bufs, stream=stream)
+
+
+def ring_allreduce_ex(bufs, algo: int, stream=None):
+    _call_bufs("rar_ring_allreduce_ex", bufs, algo, stream=stream)
+
+
+def reduce_scatter(bufs, stream=None):
+    _call_bufs("rar_reduce_scatter", bufs, stream=stream)
+
+
+def reduce_scatter_ex(bufs, algo: int, stream=None):
+    _call_bufs("rar_reduce_scatter_ex", bufs, algo, stream=stream)
+
+
+def allgather(bufs, stream=None):
+    _call_bufs("rar_allgather", bufs, stream=stream)
+
+
+def allgather_ex(bufs, algo: int, stream=None):
+    _call_bufs("rar_allgather_ex", bufs, algo, stream=stream)
+
+
+def broadcast(bufs, root: int = 0, stream=None):
+    _call_bufs("rar_broadcast", bufs, root, stream=stream)
+
+
+def broadcast_ex(bufs, root: int, algo: int, stream=None):
+    _call_bufs("rar_broadcast_ex", bufs, root, algo, stream=stream)
+
+
+def rs_step(bufs, step: int, stream=None):
+    _call_bufs("rar_rs_step", bufs, step, stream=stream)
+
+
+def ag_step(bufs, step: int, stream=None):
+    _call_bufs("rar_ag_step", bufs, step, stream=stream)
+
+
+def last_traffic(nranks: int):
+    sent = (ctypes.c_uint64 * nranks)()
+    recv = (ctypes.c_uint64 * nranks)()
+    _check(lib().rar_last_traffic(sent, recv, nranks), "rar_last_traffic")
+    return list(sent), list(recv)
+
+
+# ------------------------------------------------------------------ BFP
+
+def bfp_bytes(count: int, block: int = 128, mbits: int = 8) -> int:
+    return lib().rar_bfp_bytes(count, block, mbits)
+
+
+def bfp_compress(src, block: int, mbits: int, dst, stream=None):
+    rc = lib().rar_bfp_compress(src.data_ptr(), dtype_code(src), src.numel(), block, mbits, dst.data_ptr(),
+                                _stream(stream, src))
+    _check(rc, "rar_bfp_compress")
+
+
+def bfp_decompress_accumulate(msg, count: int, block: int, mbits: int, acc, stream=None):
+    rc = lib().rar_bfp_decompress_accumulate(msg.data_ptr(), count, block, mbits, acc.data_ptr(),
+                                             dtype_code(acc), _stream(stream, acc))
+    _check(rc, "rar_bfp_decompress_accumulate")
+
+
+def bfp_decompress(msg, count: int, block: int, mbits: int, dst, stream=None):
+    rc = lib().rar_bfp_decompress(msg.data_ptr(), count, block, mbits, dst.data_ptr(), dtype_code(dst),
+                                  _stream(stream, dst))
+    _check(rc, "rar_bfp_decompress")
+
+
+# ------------------------------------------------------------------ compressed allreduce
+
+def compress_cfg_default() -> CompressCfg:
+    cfg = CompressCfg()
+    lib().rar_compress_cfg_default(ctypes.byref(cfg))
+    return cfg
+
+
+def compress_cfg(**kw) -> CompressCfg:
+    cfg = compress_cfg_default()
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+def compressed_chunk_len(count: int, nranks: int, block: int = 128) -> int:
+    return lib().rar_compressed_chunk_len(count, nranks, block)
+
+
+def compressed_workspace_bytes(nranks: int, count: int, dtype: int, cfg: CompressCfg) -> int:
+    return lib().rar_compressed_workspace_bytes(nranks, count, dtype, ctypes.byref(cfg))
+
+
+def ring_allreduce_compressed(bufs, cfg: CompressCfg, workspace, stream=None):
+    rc = lib().rar_ring_allreduce_compressed(
+        _rank_ptrs(bufs), len(bufs), bufs[0].numel(), dtype_code(bufs[0]), ctypes.byref(cfg),
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream, bufs[0]))
+    _check(rc, "rar_ring_allreduce_compressed")
+
+
+def compressed_traffic(workspace, nranks: int, stream=None):
+    sent = (ctypes.c_uint64 * nranks)()
+    recv = (ctypes.c_uint64 * nranks)()
+    _check(lib().rar_compressed_traffic(workspace.data_ptr(), nranks, sent, recv, _stream(stream, workspace)),
+           "rar_compressed_traffic")
+    return list(sent), list(recv)
+
+
+# ------------------------------------------------------------------ bucketing
+
+def _sizes(counts):
+    return (ctypes.c_size_t * len(counts))(*[int(c) for c in counts])
+
+
+def bucket_plan(counts, dtype: int, cap_bytes: int):
+    out = (ctypes.c_int * max(1, len(counts)))()
+    nb = lib().rar_bucket_plan(_sizes(counts), len(counts), dtype, cap_bytes, out)
+    return int(nb), list(out)[:len(counts)]
+
+
+def bucketed_workspace_bytes(counts, nranks: int, dtype: int, cap_bytes: int) -> int:
+    return lib().rar_bucketed_workspace_bytes(_sizes(counts), len(counts), nranks, dtype, cap_bytes)
+
+
+def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None):
+    """tensors[r][t]: rank r's gradient tensor t (device tensors, in place)."""
+    n, nt = len(tensors), len(tensors[0])
+    t0 = tensors[0][0]
+    flat = [tensors[r][t] for r in range(n) for t in range(nt)]
+    for r in range(n):
+        for t in range(nt):
+            x = tensors[r][t]
+            if x.dtype != t0.dtype or x.numel() != tensors[0][t].numel() or not x.is_contiguous():
+                raise ValueError("tensor t must have the same size and dtype on every rank")
+    ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() for x in flat])
+    counts = [tensors[0][t].numel() for t in range(nt)]
+    rc = lib().rar_bucketed_allreduce(ptrs, _sizes(counts), nt, n, dtype_code(t0), cap_bytes,
+                                      workspace.data_ptr() if workspace is not None else None,
+                                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                      _stream(stream, t0))
+    _check(rc, "rar_bucketed_allreduce")

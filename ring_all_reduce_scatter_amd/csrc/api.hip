@@ -1,0 +1,739 @@
+// C-ABI of librar.so: argument checking, the ring's chunk scheduler, byte
+// accounting and the staged compress/decompress pipeline.  Kernels live in
+// ring_kernels.hip and bfp_kernels.hip; this file only plans and launches.
+//
+// Ring schedule (page "从零实现集合通信", two-pass ring allreduce section):
+// reduce-scatter step s = 1..N-1: rank r receives chunk (r-s-1) mod N from
+// rank r-1 and adds it to its copy; allgather step s: rank r receives chunk
+// (r-s) mod N.  Byte table of the same page: allreduce 2T(N-1)/N per rank,
+// reduce-scatter and allgather T(N-1)/N, broadcast T.
+//
+// Compressed pipeline (page "CCCL通信压缩库：突破LLM训练通信墙的工程实践",
+// section 2.2): chunks are cut into units; unit u is compressed on one
+// stream, and after an event the receiver's decompress + reduce of unit u
+// runs on a second stream while unit u+1 is being compressed.
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "launch.hpp"
+#include "rar.h"
+
+using namespace rar;
+
+namespace {
+
+constexpr size_t kTrafficBytes = 2 * RAR_MAX_RANKS * sizeof(uint64_t);
+constexpr size_t kAlign = 256;
+constexpr int kMaxEvents = 64;
+
+struct Traffic {
+  int n = 0;
+  uint64_t sent[RAR_MAX_RANKS] = {};
+  uint64_t recv[RAR_MAX_RANKS] = {};
+  void reset(int nr) {
+    n = nr;
+    std::memset(sent, 0, sizeof sent);
+    std::memset(recv, 0, sizeof recv);
+  }
+  void add(int from, int to, uint64_t bytes) {
+    sent[from] += bytes;
+    recv[to] += bytes;
+  }
+};
+
+thread_local Traffic g_last;
+
+size_t es_of(int dt) { return dt == RAR_F32 ? 4 : 2; }
+bool dt_ok(int dt) { return dt == RAR_F32 || dt == RAR_F16 || dt == RAR_BF16; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int modn(int a, int n) { return ((a % n) + n) % n; }
+
+size_t chunk_len_aligned(size_t count, int n, size_t align) {
+  if (n < 1 || n > RAR_MAX_RANKS) return 0;
+  return round_up((count + (size_t)n - 1) / (size_t)n, align);
+}
+
+void chunk_range(size_t count, size_t L, int c, size_t* lo, size_t* hi) {
+  size_t a = (size_t)c * L, b = a + L;
+  *lo = std::min(a, count);
+  *hi = std::min(b, count);
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? RAR_OK : RAR_EHIP; }
+
+// N distinct, non-null, 16-byte aligned, non-overlapping buffers of `bytes`.
+int check_bufs(void* const* bufs, int n, int dt, size_t bytes) {
+  if (n < 1 || n > RAR_MAX_RANKS) return RAR_EINVAL;
+  if (!dt_ok(dt)) return RAR_EDTYPE;
+  if (!bufs) return RAR_EOVERLAP;
+  std::vector<uintptr_t> a((size_t)n);
+  for (int r = 0; r < n; ++r) {
+    if (!bufs[r]) return RAR_EOVERLAP;
+    if ((uintptr_t)bufs[r] & 15u) return RAR_EALIGN;
+    a[(size_t)r] = (uintptr_t)bufs[r];
+  }
+  std::sort(a.begin(), a.end());
+  for (int r = 0; r + 1 < n; ++r) {
+    if (a[(size_t)r] == a[(size_t)r + 1] && bytes > 0) return RAR_EOVERLAP;
+    if (a[(size_t)r + 1] - a[(size_t)r] < bytes) return RAR_EOVERLAP;
+  }
+  return RAR_OK;
+}
+
+RankPtrs make_ptrs(void* const* bufs, int n) {
+  RankPtrs p{};
+  for (int r = 0; r < n; ++r) p.p[r] = (char*)bufs[r];
+  return p;
+}
+
+// Ring traffic of one pass: rank r sends chunk (r-s+shift) mod N at step s.
+void ring_pass_traffic(Traffic& t, int n, size_t count, size_t L, size_t es, int shift) {
+  for (int s = 1; s <= n - 1; ++s)
+    for (int r = 0; r < n; ++r) {
+      size_t lo, hi;
+      chunk_range(count, L, modn(r - s + shift, n), &lo, &hi);
+      t.add(r, (r + 1) % n, (uint64_t)(hi - lo) * es);
+    }
+}
+
+void tree_traffic(Traffic& t, int n, int root, uint64_t bytes) {
+  for (int span = 1; span < n; span *= 2)
+    for (int rel = 0; rel < span && rel + span < n; ++rel) t.add((root + rel) % n, (root + rel + span) % n, bytes);
+}
+
+// ------------------------------------------------------------------ uncompressed steps
+
+int run_rs_step(const RankPtrs& p, int n, size_t count, size_t L, int dt, int s, hipStream_t st) {
+  return hip_rc(launch_rs_step(p, n, count, L, dt, s, st));
+}
+
+int run_ag_step(const RankPtrs& p, int n, size_t count, size_t L, size_t es, int s, hipStream_t st) {
+  CopyJobs jobs{};
+  jobs.ptrs = p;
+  int j = 0;
+  for (int r = 0; r < n; ++r) {
+    size_t lo, hi;
+    chunk_range(count, L, modn(r - s, n), &lo, &hi);
+    if (hi == lo) continue;
+    jobs.lo[j] = lo * es;
+    jobs.len[j] = (hi - lo) * es;
+    jobs.dstmask[j] = 1ull << r;
+    jobs.src[j] = (int8_t)modn(r - 1, n);
+    ++j;
+  }
+  jobs.njobs = j;
+  return hip_rc(launch_copy_jobs(jobs, st));
+}
+
+int allreduce_impl(void* const* bufs, int n, size_t count, int dt, int algo, bool full,
+                   hipStream_t st) {
+  const size_t es = es_of(dt);
+  int rc = check_bufs(bufs, n, dt, count * es);
+  if (rc) return rc;
+  if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_STEPWISE) return RAR_EINVAL;
+  const size_t L = chunk_len_aligned(count, n, 128);
+  g_last.reset(n);
+  ring_pass_traffic(g_last, n, count, L, es, 0);
+  if (full) ring_pass_traffic(g_last, n, count, L, es, 1);
+  if (n == 1 || count == 0) return RAR_OK;
+  RankPtrs p = make_ptrs(bufs, n);
+  if (algo == RAR_ALGO_FUSED) return hip_rc(launch_ring_fold(p, n, count, L, dt, full, st));
+  for (int s = 1; s <= n - 1; ++s)
+    if ((rc = run_rs_step(p, n, count, L, dt, s, st))) return rc;
+  if (full)
+    for (int s = 1; s <= n - 1; ++s)
+      if ((rc = run_ag_step(p, n, count, L, es, s, st))) return rc;
+  return RAR_OK;
+}
+
+// ------------------------------------------------------------------ per-device pipeline state
+
+struct DevCtx {
+  bool ready = false;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t evE[kMaxEvents] = {}, evD[kMaxEvents] = {};
+};
+
+std::mutex g_ctx_mu;
+DevCtx g_ctx[64];
+
+int get_ctx(DevCtx** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RAR_EHIP;
+  DevCtx& c = g_ctx[dev];
+  if (!c.ready) {
+    if (hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking) != hipSuccess) return RAR_EHIP;
+    if (hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess) return RAR_EHIP;
+    if (hipEventCreateWithFlags(&c.join, hipEventDisableTiming) != hipSuccess) return RAR_EHIP;
+    for (int i = 0; i < kMaxEvents; ++i) {
+      if (hipEventCreateWithFlags(&c.evE[i], hipEventDisableTiming) != hipSuccess) return RAR_EHIP;
+      if (hipEventCreateWithFlags(&c.evD[i], hipEventDisableTiming) != hipSuccess) return RAR_EHIP;
+    }
+    c.ready = true;
+  }
+  *out = &c;
+  return RAR_OK;
+}
+
+// ------------------------------------------------------------------ compressed allreduce
+
+struct CompPlan {
+  int n, dt, method, block, mbits, sched;
+  size_t count, es, L, U, upc, slot;
+  float theta;
+};
+
+int cfg_check(const rar_compress_cfg* cfg, int dt, CompPlan* pl) {
+  if (!cfg) return RAR_EINVAL;
+  if (cfg->method < RAR_COMP_NONE || cfg->method > RAR_COMP_SPARSE_AUTO) return RAR_EINVAL;
+  if (cfg->mbits < 2 || cfg->mbits > 8) return RAR_EINVAL;
+  if (cfg->block < 16 || cfg->block > 512 || (cfg->block & (cfg->block - 1))) return RAR_EINVAL;
+  if (cfg->schedule != RAR_SCHED_FUSED && cfg->schedule != RAR_SCHED_STAGED) return RAR_EINVAL;
+  const size_t es = es_of(dt);
+  if (cfg->unit_bytes == 0 || cfg->unit_bytes % es) return RAR_EINVAL;
+  const size_t U = cfg->unit_bytes / es;
+  if (U % (size_t)cfg->block || U > 0xffffffffull) return RAR_EINVAL;
+  if (!(cfg->sparsity_threshold >= 0.0f && cfg->sparsity_threshold <= 1.0f)) return RAR_EINVAL;
+  pl->method = cfg->method;
+  pl->block = cfg->block;
+  pl->mbits = cfg->mbits;
+  pl->sched = cfg->method == RAR_COMP_BFP ? cfg->schedule : RAR_SCHED_STAGED;
+  pl->U = U;
+  pl->es = es;
+  pl->theta = cfg->sparsity_threshold;
+  return RAR_OK;
+}
+
+void plan_sizes(CompPlan* pl, int n, size_t count, int dt) {
+  pl->n = n;
+  pl->count = count;
+  pl->dt = dt;
+  pl->L = chunk_len_aligned(count, n, (size_t)std::max(128, pl->block));
+  pl->upc = pl->L ? (pl->L + pl->U - 1) / pl->U : 0;
+  size_t slot = bfp_msg_bytes(pl->U, pl->block, pl->mbits);
+  if (pl->method == RAR_COMP_SPARSE_AUTO) {
+    const size_t sparse_max = 16 + round_up(pl->U * pl->es, 16) + 4 * pl->U;
+    slot = std::max(16 + slot, sparse_max);
+  }
+  pl->slot = round_up(slot, kAlign);
+}
+
+size_t workspace_need(const CompPlan& pl) {
+  if (pl.method == RAR_COMP_NONE || pl.sched == RAR_SCHED_FUSED) return kTrafficBytes;
+  size_t need = round_up(kTrafficBytes, kAlign) + (size_t)pl.n * pl.upc * pl.slot;
+  return need;
+}
+
+int write_traffic(const Traffic& t, void* ws, hipStream_t st) {
+  uint64_t vals[2 * RAR_MAX_RANKS] = {};
+  for (int r = 0; r < t.n; ++r) {
+    vals[r] = t.sent[r];
+    vals[RAR_MAX_RANKS + r] = t.recv[r];
+  }
+  return hip_rc(launch_fill_u64((uint64_t*)ws, vals, 2 * RAR_MAX_RANKS, st));
+}
+
+// Staged BFP ring: messages materialised per (sender, unit) in the workspace.
+int staged_bfp(const CompPlan& pl, void* const* bufs, char* ws, Traffic& tr, hipStream_t st) {
+  DevCtx* ctx = nullptr;
+  std::lock_guard<std::mutex> lock(g_ctx_mu);
+  int rc = get_ctx(&ctx);
+  if (rc) return rc;
+  const int n = pl.n;
+  char* slots = ws + round_up(kTrafficBytes, kAlign);
+  auto slot = [&](int rank, size_t u) { return (uint8_t*)(slots + ((size_t)rank * pl.upc + u) * pl.slot); };
+  hipStream_t E = st, D = ctx->side;
+  if (hipEventRecord(ctx->fork, E) != hipSuccess || hipStreamWaitEvent(D, ctx->fork, 0) != hipSuccess)
+    return RAR_EHIP;
+  // reduce-scatter hops
+  for (int s = 1; s <= n - 1; ++s) {
+    for (size_t u = 0; u < pl.upc; ++u) {
+      BfpJobs enc{}, dec{};
+      int j = 0;
+      for (int r = 0; r < n; ++r) {
+        const int src = modn(r - 1, n), c = modn(r - s - 1, n);
+        size_t lo, hi;
+        chunk_range(pl.count, pl.L, c, &lo, &hi);
+        const size_t ulo = lo + u * pl.U;
+        if (ulo >= hi) continue;
+        const size_t len = std::min(pl.U, hi - ulo);
+        enc.src[j] = (const char*)bufs[src] + ulo * pl.es;
+        enc.msg[j] = slot(src, u);
+        enc.len[j] = len;
+        dec.dst[j] = (char*)bufs[r] + ulo * pl.es;
+        dec.msg[j] = slot(src, u);
+        dec.len[j] = len;
+        tr.add(src, r, bfp_msg_bytes(len, pl.block, pl.mbits));
+        ++j;
+      }
+      if (!j) continue;
+      enc.njobs = dec.njobs = j;
+      hipEvent_t eE = ctx->evE[u % kMaxEvents], eD = ctx->evD[u % kMaxEvents];
+      if (s > 1 && hipStreamWaitEvent(E, eD, 0) != hipSuccess) return RAR_EHIP;
+      if ((rc = hip_rc(launch_bfp_encode(enc, pl.dt, pl.block, pl.mbits, E)))) return rc;
+      if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
+      if ((rc = hip_rc(launch_bfp_decode(dec, pl.dt, pl.block, pl.mbits, true, D)))) return rc;
+      if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;
+    }
+  }
+  // allgather: each owner encodes its finished unit once; every rank stores
+  // the decoded unit (the relayed bytes are the owner's message unchanged)
+  RankPtrs fan = make_ptrs(bufs, n);
+  for (size_t u = 0; u < pl.upc; ++u) {
+    BfpJobs enc{};
+    uint64_t off[kMaxRanks] = {};
+    int j = 0;
+    for (int c = 0; c < n; ++c) {
+      size_t lo, hi;
+      chunk_range(pl.count, pl.L, c, &lo, &hi);
+      const size_t ulo = lo + u * pl.U;
+      if (ulo >= hi) continue;
+      const size_t len = std::min(pl.U, hi - ulo);
+      enc.src[j] = (const char*)bufs[c] + ulo * pl.es;
+      enc.msg[j] = slot(c, u);
+      enc.len[j] = len;
+      off[j] = ulo;
+      const uint64_t bytes = bfp_msg_bytes(len, pl.block, pl.mbits);
+      for (int s = 1; s <= n - 1; ++s) tr.add(modn(c + s - 1, n), modn(c + s, n), bytes);
+      ++j;
+    }
+    if (!j) continue;
+    enc.njobs = j;
+    hipEvent_t eE = ctx->evE[u % kMaxEvents], eD = ctx->evD[u % kMaxEvents];
+    if (hipStreamWaitEvent(E, eD, 0) != hipSuccess) return RAR_EHIP;
+    if ((rc = hip_rc(launch_bfp_encode(enc, pl.dt, pl.block, pl.mbits, E)))) return rc;
+    if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
+    if ((rc = hip_rc(launch_bfp_decode_fanout(enc, fan, n, off, pl.dt, pl.block, pl.mbits, D)))) return rc;
+    if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;
+  }
+  if (hipEventRecord(ctx->join, D) != hipSuccess || hipStreamWaitEvent(E, ctx->join, 0) != hipSuccess)
+    return RAR_EHIP;
+  return RAR_OK;
+}
+
+void fused_bfp_traffic(const CompPlan& pl, Traffic& tr) {
+  const int n = pl.n;
+  for (int s = 1; s <= n - 1; ++s)
+    for (int r = 0; r < n; ++r) {
+      size_t lo, hi;
+      chunk_range(pl.count, pl.L, modn(r - s - 1, n), &lo, &hi);
+      for (size_t u = lo; u < hi; u += pl.U)
+        tr.add(modn(r - 1, n), r, bfp_msg_bytes(std::min(pl.U, hi - u), pl.block, pl.mbits));
+    }
+  for (int c = 0; c < n; ++c) {
+    size_t lo, hi;
+    chunk_range(pl.count, pl.L, c, &lo, &hi);
+    for (size_t u = lo; u < hi; u += pl.U) {
+      const uint64_t bytes = bfp_msg_bytes(std::min(pl.U, hi - u), pl.block, pl.mbits);
+      for (int s = 1; s <= n - 1; ++s) tr.add(modn(c + s - 1, n), modn(c + s, n), bytes);
+    }
+  }
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+size_t rar_chunk_len(size_t count, int nranks) { return chunk_len_aligned(count, nranks, 128); }
+
+int rar_ring_allreduce_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo, void* stream) {
+  return allreduce_impl(bufs, nranks, count, dtype, algo, true, (hipStream_t)stream);
+}
+
+int rar_ring_allreduce(void* const* bufs, int nranks, size_t count, int dtype, void* stream) {
+  return rar_ring_allreduce_ex(bufs, nranks, count, dtype, RAR_ALGO_FUSED, stream);
+}
+
+int rar_reduce_scatter_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo, void* stream) {
+  return allreduce_impl(bufs, nranks, count, dtype, algo, false, (hipStream_t)stream);
+}
+
+int rar_reduce_scatter(void* const* bufs, int nranks, size_t count, int dtype, void* stream) {
+  return rar_reduce_scatter_ex(bufs, nranks, count, dtype, RAR_ALGO_FUSED, stream);
+}
+
+int rar_rs_step(void* const* bufs, int nranks, size_t count, int dtype, int step, void* stream) {
+  int rc = check_bufs(bufs, nranks, dtype, count * es_of(dtype));
+  if (rc) return rc;
+  if (step < 1 || step > nranks - 1) return RAR_EINVAL;
+  const size_t L = chunk_len_aligned(count, nranks, 128);
+  g_last.reset(nranks);
+  for (int r = 0; r < nranks; ++r) {
+    size_t lo, hi;
+    chunk_range(count, L, modn(r - step, nranks), &lo, &hi);
+    g_last.add(r, (r + 1) % nranks, (uint64_t)(hi - lo) * es_of(dtype));
+  }
+  if (count == 0) return RAR_OK;
+  return run_rs_step(make_ptrs(bufs, nranks), nranks, count, L, dtype, step, (hipStream_t)stream);
+}
+
+int rar_ag_step(void* const* bufs, int nranks, size_t count, int dtype, int step, void* stream) {
+  int rc = check_bufs(bufs, nranks, dtype, count * es_of(dtype));
+  if (rc) return rc;
+  if (step < 1 || step > nranks - 1) return RAR_EINVAL;
+  const size_t L = chunk_len_aligned(count, nranks, 128);
+  g_last.reset(nranks);
+  for (int r = 0; r < nranks; ++r) {
+    size_t lo, hi;
+    chunk_range(count, L, modn(r - step + 1, nranks), &lo, &hi);
+    g_last.add(r, (r + 1) % nranks, (uint64_t)(hi - lo) * es_of(dtype));
+  }
+  if (count == 0) return RAR_OK;
+  return run_ag_step(make_ptrs(bufs, nranks), nranks, count, L, es_of(dtype), step, (hipStream_t)stream);
+}
+
+int rar_allgather_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo, void* stream) {
+  const size_t es = es_of(dtype);
+  int rc = check_bufs(bufs, nranks, dtype, count * es);
+  if (rc) return rc;
+  if (count % (size_t)nranks) return RAR_EINVAL;
+  if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_STEPWISE) return RAR_EINVAL;
+  const size_t shard = count / (size_t)nranks;
+  g_last.reset(nranks);
+  ring_pass_traffic(g_last, nranks, count, shard, es, 1);
+  if (nranks == 1 || count == 0) return RAR_OK;
+  RankPtrs p = make_ptrs(bufs, nranks);
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == RAR_ALGO_STEPWISE) {
+    for (int s = 1; s <= nranks - 1; ++s)
+      if ((rc = run_ag_step(p, nranks, count, shard, es, s, st))) return rc;
+    return RAR_OK;
+  }
+  CopyJobs jobs{};
+  jobs.ptrs = p;
+  const uint64_t all = nranks == 64 ? ~0ull : ((1ull << nranks) - 1);
+  for (int c = 0; c < nranks; ++c) {
+    jobs.lo[c] = (uint64_t)c * shard * es;
+    jobs.len[c] = shard * es;
+    jobs.dstmask[c] = all & ~(1ull << c);
+    jobs.src[c] = (int8_t)c;
+  }
+  jobs.njobs = nranks;
+  return hip_rc(launch_copy_jobs(jobs, st));
+}
+
+int rar_allgather(void* const* bufs, int nranks, size_t count, int dtype, void* stream) {
+  return rar_allgather_ex(bufs, nranks, count, dtype, RAR_ALGO_FUSED, stream);
+}
+
+int rar_broadcast_ex(void* const* bufs, int nranks, size_t count, int dtype, int root, int algo,
+                     void* stream) {
+  const size_t es = es_of(dtype);
+  int rc = check_bufs(bufs, nranks, dtype, count * es);
+  if (rc) return rc;
+  if (root < 0 || root >= nranks) return RAR_EINVAL;
+  if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_STEPWISE) return RAR_EINVAL;
+  g_last.reset(nranks);
+  tree_traffic(g_last, nranks, root, (uint64_t)count * es);
+  if (nranks == 1 || count == 0) return RAR_OK;
+  RankPtrs p = make_ptrs(bufs, nranks);
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == RAR_ALGO_FUSED) {
+    CopyJobs jobs{};
+    jobs.ptrs = p;
+    const uint64_t all = nranks == 64 ? ~0ull : ((1ull << nranks) - 1);
+    jobs.lo[0] = 0;
+    jobs.len[0] = count * es;
+    jobs.dstmask[0] = all & ~(1ull << root);
+    jobs.src[0] = (int8_t)root;
+    jobs.njobs = 1;
+    return hip_rc(launch_copy_jobs(jobs, st));
+  }
+  for (int span = 1; span < nranks; span *= 2) {
+    CopyJobs jobs{};
+    jobs.ptrs = p;
+    int j = 0;
+    for (int rel = 0; rel < span && rel + span < nranks; ++rel) {
+      jobs.lo[j] = 0;
+      jobs.len[j] = count * es;
+      jobs.dstmask[j] = 1ull << ((root + rel + span) % nranks);
+      jobs.src[j] = (int8_t)((root + rel) % nranks);
+      ++j;
+    }
+    jobs.njobs = j;
+    if ((rc = hip_rc(launch_copy_jobs(jobs, st)))) return rc;
+  }
+  return RAR_OK;
+}
+
+int rar_broadcast(void* const* bufs, int nranks, size_t count, int dtype, int root, void* stream) {
+  return rar_broadcast_ex(bufs, nranks, count, dtype, root, RAR_ALGO_FUSED, stream);
+}
+
+int rar_last_traffic(uint64_t* sent, uint64_t* recv, int nranks) {
+  if (!sent || !recv || nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
+  for (int r = 0; r < nranks; ++r) {
+    sent[r] = r < g_last.n ? g_last.sent[r] : 0;
+    recv[r] = r < g_last.n ? g_last.recv[r] : 0;
+  }
+  return RAR_OK;
+}
+
+// ------------------------------------------------------------------ BFP
+
+size_t rar_bfp_bytes(size_t count, int block, int mbits) {
+  if (mbits < 2 || mbits > 8 || block < 16 || block > 512 || (block & (block - 1))) return 0;
+  return bfp_msg_bytes(count, block, mbits);
+}
+
+static int bfp_args(const void* a, const void* b, int dt, int block, int mbits) {
+  if (!a || !b) return RAR_EINVAL;
+  if (!dt_ok(dt)) return RAR_EDTYPE;
+  if (rar_bfp_bytes(1, block, mbits) == 0) return RAR_EINVAL;
+  if (((uintptr_t)a & 15u) || ((uintptr_t)b & 15u)) return RAR_EALIGN;
+  return RAR_OK;
+}
+
+int rar_bfp_compress(const void* src, int src_dtype, size_t count, int block, int mbits, void* dst,
+                     void* stream) {
+  int rc = bfp_args(src, dst, src_dtype, block, mbits);
+  if (rc) return rc;
+  if (count == 0) return RAR_OK;
+  BfpJobs jobs{};
+  jobs.src[0] = (const char*)src;
+  jobs.msg[0] = (uint8_t*)dst;
+  jobs.len[0] = count;
+  jobs.njobs = 1;
+  return hip_rc(launch_bfp_encode(jobs, src_dtype, block, mbits, (hipStream_t)stream));
+}
+
+static int bfp_decode_entry(const void* src, size_t count, int block, int mbits, void* dst, int dt,
+                            bool acc, void* stream) {
+  int rc = bfp_args(src, dst, dt, block, mbits);
+  if (rc) return rc;
+  if (count == 0) return RAR_OK;
+  BfpJobs jobs{};
+  jobs.msg[0] = (uint8_t*)src;
+  jobs.dst[0] = (char*)dst;
+  jobs.len[0] = count;
+  jobs.njobs = 1;
+  return hip_rc(launch_bfp_decode(jobs, dt, block, mbits, acc, (hipStream_t)stream));
+}
+
+int rar_bfp_decompress_accumulate(const void* src, size_t count, int block, int mbits, void* acc,
+                                  int acc_dtype, void* stream) {
+  return bfp_decode_entry(src, count, block, mbits, acc, acc_dtype, true, stream);
+}
+
+int rar_bfp_decompress(const void* src, size_t count, int block, int mbits, void* dst, int dst_dtype,
+                       void* stream) {
+  return bfp_decode_entry(src, count, block, mbits, dst, dst_dtype, false, stream);
+}
+
+// ------------------------------------------------------------------ compressed allreduce
+
+void rar_compress_cfg_default(rar_compress_cfg* cfg) {
+  if (!cfg) return;
+  cfg->method = RAR_COMP_BFP;
+  cfg->block = 128;
+  cfg->mbits = 8;
+  cfg->sparsity_threshold = 0.5f;
+  cfg->unit_bytes = (size_t)4 << 20;
+  cfg->collective_mask = RAR_OP_ALLREDUCE;
+  cfg->schedule = RAR_SCHED_FUSED;
+}
+
+size_t rar_compressed_chunk_len(size_t count, int nranks, int block) {
+  if (block < 16 || block > 512 || (block & (block - 1))) return 0;
+  return chunk_len_aligned(count, nranks, (size_t)std::max(128, block));
+}
+
+size_t rar_compressed_workspace_bytes(int nranks, size_t count, int dtype, const rar_compress_cfg* cfg) {
+  if (nranks < 1 || nranks > RAR_MAX_RANKS || !dt_ok(dtype)) return 0;
+  CompPlan pl{};
+  if (cfg_check(cfg, dtype, &pl)) return 0;
+  if (!(cfg->collective_mask & RAR_OP_ALLREDUCE)) pl.method = RAR_COMP_NONE;
+  plan_sizes(&pl, nranks, count, dtype);
+  return workspace_need(pl);
+}
+
+int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, int dtype,
+                                  const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  const size_t es = es_of(dtype);
+  int rc = check_bufs(bufs, nranks, dtype, count * es);
+  if (rc) return rc;
+  CompPlan pl{};
+  if ((rc = cfg_check(cfg, dtype, &pl))) return rc;
+  if (!(cfg->collective_mask & RAR_OP_ALLREDUCE)) pl.method = RAR_COMP_NONE;
+  plan_sizes(&pl, nranks, count, dtype);
+  if (!workspace || ws_bytes < workspace_need(pl)) return RAR_EWORKSPACE;
+  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  Traffic tr;
+  tr.reset(nranks);
+  if (pl.method == RAR_COMP_NONE) {
+    if ((rc = allreduce_impl(bufs, nranks, count, dtype, RAR_ALGO_FUSED, true, st))) return rc;
+    return write_traffic(g_last, workspace, st);
+  }
+  if (pl.method == RAR_COMP_SPARSE_AUTO) return RAR_ENOTSUP;
+  if (nranks > 1 && count > 0) {
+    if (pl.sched == RAR_SCHED_FUSED) {
+      fused_bfp_traffic(pl, tr);
+      if ((rc = hip_rc(launch_bfp_ring_fold(make_ptrs(bufs, nranks), nranks, count, pl.L, dtype, pl.block,
+                                            pl.mbits, st))))
+        return rc;
+    } else {
+      if ((rc = staged_bfp(pl, bufs, (char*)workspace, tr, st))) return rc;
+    }
+  }
+  return write_traffic(tr, workspace, st);
+}
+
+int rar_compressed_traffic(const void* workspace, int nranks, uint64_t* sent, uint64_t* recv, void* stream) {
+  if (!workspace || !sent || !recv || nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return RAR_EHIP;
+  uint64_t vals[2 * RAR_MAX_RANKS];
+  if (hipMemcpy(vals, workspace, sizeof vals, hipMemcpyDeviceToHost) != hipSuccess) return RAR_EHIP;
+  for (int r = 0; r < nranks; ++r) {
+    sent[r] = vals[r];
+    recv[r] = vals[RAR_MAX_RANKS + r];
+  }
+  return RAR_OK;
+}
+
+// ------------------------------------------------------------------ bucketing
+
+size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t cap_bytes, int* bucket_of) {
+  if (!dt_ok(dtype) || (ntensors && (!counts || !bucket_of))) return 0;
+  const size_t es = es_of(dtype);
+  size_t nb = 0, cur = 0;
+  bool open = false;
+  for (size_t t = 0; t < ntensors; ++t) {
+    const size_t b = counts[t] * es;
+    if (b > cap_bytes) {  // an oversize tensor travels alone
+      if (open) ++nb;
+      bucket_of[t] = (int)nb++;
+      open = false;
+      cur = 0;
+      continue;
+    }
+    if (open && cur + b > cap_bytes) {
+      ++nb;
+      open = false;
+      cur = 0;
+    }
+    bucket_of[t] = (int)nb;
+    cur += b;
+    open = true;
+  }
+  return nb + (open ? 1 : 0);
+}
+
+static size_t padded_elems(size_t count, size_t es) { return round_up(count * es, 16) / es; }
+
+static size_t bucket_flat_bytes(const size_t* counts, size_t nt, int dtype, size_t cap, std::vector<int>& plan,
+                                size_t* nb_out) {
+  const size_t es = es_of(dtype);
+  plan.assign(nt ? nt : 1, 0);
+  const size_t nb = rar_bucket_plan(counts, nt, dtype, cap, plan.data());
+  size_t maxb = 0, cur = 0;
+  for (size_t t = 0; t < nt; ++t) {
+    if (t > 0 && plan[t] != plan[t - 1]) cur = 0;
+    cur += padded_elems(counts[t], es) * es;
+    maxb = std::max(maxb, cur);
+  }
+  *nb_out = nb;
+  return round_up(maxb, kAlign);
+}
+
+size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
+                                    size_t cap_bytes) {
+  if (nranks < 1 || nranks > RAR_MAX_RANKS || !dt_ok(dtype) || (ntensors && !counts)) return 0;
+  std::vector<int> plan;
+  size_t nb = 0;
+  const size_t per = bucket_flat_bytes(counts, ntensors, dtype, cap_bytes, plan, &nb);
+  return std::max<size_t>((size_t)nranks * per, 16);
+}
+
+int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,
+                           int dtype, size_t cap_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  if (nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
+  if (!dt_ok(dtype)) return RAR_EDTYPE;
+  if (ntensors && (!tensors || !counts)) return RAR_EINVAL;
+  const size_t es = es_of(dtype);
+  for (size_t i = 0; i < (size_t)nranks * ntensors; ++i) {
+    if (!tensors[i]) return RAR_EOVERLAP;
+    if ((uintptr_t)tensors[i] & 15u) return RAR_EALIGN;
+  }
+  std::vector<int> plan;
+  size_t nb = 0;
+  const size_t per = bucket_flat_bytes(counts, ntensors, dtype, cap_bytes, plan, &nb);
+  if (!workspace || ws_bytes < (size_t)nranks * per) return RAR_EWORKSPACE;
+  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  Traffic total;
+  total.reset(nranks);
+  void* flat[RAR_MAX_RANKS];
+  for (int r = 0; r < nranks; ++r) flat[r] = (char*)workspace + (size_t)r * per;
+  size_t t0 = 0;
+  int rc = RAR_OK;
+  for (size_t b = 0; b < nb; ++b) {
+    size_t t1 = t0, elems = 0;
+    std::vector<size_t> off;
+    while (t1 < ntensors && plan[t1] == (int)b) {
+      off.push_back(elems);
+      elems += padded_elems(counts[t1++], es);
+    }
+    // pack: every (rank, tensor) segment into the rank's flat bucket
+    SegJobs jobs{};
+    auto flush = [&]() -> int {
+      if (!jobs.njobs) return RAR_OK;
+      int r2 = hip_rc(launch_seg_copy(jobs, st));
+      jobs = SegJobs{};
+      return r2;
+    };
+    for (int r = 0; r < nranks; ++r)
+      for (size_t t = t0; t < t1; ++t) {
+        jobs.src[jobs.njobs] = (const char*)tensors[(size_t)r * ntensors + t];
+        jobs.dst[jobs.njobs] = (char*)flat[r] + off[t - t0] * es;
+        jobs.bytes[jobs.njobs] = counts[t] * es;
+        jobs.zero_to[jobs.njobs] = padded_elems(counts[t], es) * es;
+        if (++jobs.njobs == kMaxRanks && (rc = flush())) return rc;
+      }
+    if ((rc = flush())) return rc;
+    if ((rc = allreduce_impl(flat, nranks, elems, dtype, RAR_ALGO_FUSED, true, st))) return rc;
+    for (int r = 0; r < nranks; ++r) {
+      total.sent[r] += g_last.sent[r];
+      total.recv[r] += g_last.recv[r];
+    }
+    // unpack: the reduced bucket back into every rank's tensors
+    for (int r = 0; r < nranks; ++r)
+      for (size_t t = t0; t < t1; ++t) {
+        jobs.src[jobs.njobs] = (const char*)flat[r] + off[t - t0] * es;
+        jobs.dst[jobs.njobs] = (char*)tensors[(size_t)r * ntensors + t];
+        jobs.bytes[jobs.njobs] = counts[t] * es;
+        jobs.zero_to[jobs.njobs] = counts[t] * es;
+        if (++jobs.njobs == kMaxRanks && (rc = flush())) return rc;
+      }
+    if ((rc = flush())) return rc;
+    t0 = t1;
+  }
+  g_last = total;
+  return RAR_OK;
+}
+
+// ------------------------------------------------------------------ misc
+
+const char* rar_status_string(int status) {
+  switch (status) {
+    case RAR_OK: return "ok";
+    case RAR_EINVAL: return "invalid argument";
+    case RAR_EDTYPE: return "unsupported element type";
+    case RAR_EALIGN: return "device pointer not 16-byte aligned";
+    case RAR_EWORKSPACE: return "workspace missing or too small";
+    case RAR_EHIP: return "HIP runtime error";
+    case RAR_ENOTSUP: return "not supported";
+    case RAR_EOVERLAP: return "rank buffers overlap or are NULL";
+    default: return "unknown status";
+  }
+}
+
+const char* rar_version(void) { return "rar 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,421 @@
+// Block-floating-point kernels for gfx950 (page "CCCL通信压缩库：突破LLM训练通信墙
+// 的工程实践", section 2.1: a block of elements shares one exponent and each
+// element keeps a scaled 8- or 4-bit mantissa; section 2.2: compress ->
+// communicate -> decompress -> reduce).
+//
+// Lane layout: a lane owns 8 consecutive elements, so a block of B elements
+// is B/8 consecutive lanes (16 lanes = one DPP row for B = 128).  The block's
+// exponent is the max of |x| bit patterns, reduced across those lanes with
+// DPP (group_max_u32): E = bits >> 23 (255 when an Inf/NaN is present).
+// With e = max(E,1) - 127 and k = m - 2 - e every element is
+//   q = clamp(rne(x * 2^k), +-(2^(m-1)-1)),  decoded as q * 2^-k,
+// both scalings exact (v_ldexp_f32), rne = v_rndne_f32.
+//
+// Message layout: uint8 E[nblocks] zero-padded to 16 bytes, then one int8
+// per element (m > 4) or two's-complement nibbles (element 2j in bits 3:0,
+// 2j+1 in bits 7:4).  A lane's 8 mantissas are one 8-byte (or 4-byte) store.
+#include "launch.hpp"
+
+namespace rar {
+
+namespace {
+
+constexpr int kEncBlocksPerJob = 1024;  // grid-stride cap per job
+
+// Cross-lane max for a runtime lanes-per-block (power of two, 2..64).
+__device__ __forceinline__ uint32_t group_max_dyn(uint32_t v, int lpb) {
+  switch (lpb) {
+    case 2: return group_max_u32<2>(v);
+    case 4: return group_max_u32<4>(v);
+    case 8: return group_max_u32<8>(v);
+    case 16: return group_max_u32<16>(v);
+    case 32: return group_max_u32<32>(v);
+    default: return group_max_u32<64>(v);
+  }
+}
+
+template <int LPB>
+__device__ __forceinline__ uint32_t group_max_sel(uint32_t v, int lpb) {
+  if constexpr (LPB > 0) return group_max_u32<LPB>(v);
+  else return group_max_dyn(v, lpb);
+}
+
+__device__ __forceinline__ uint32_t lane_absmax(const G8& x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, absbits(x.v[i]));
+  return m;
+}
+
+// Quantise-dequantise a lane's 8 elements with the block's scale.
+__device__ __forceinline__ G8 qdq8(const G8& x, const BfpScale& sc, float qmax) {
+  G8 d;
+  const float nanv = __builtin_nanf("");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = bfp_dq(bfp_q(x.v[i], sc.k, qmax), sc.k);
+    d.v[i] = sc.nan ? nanv : v;
+  }
+  return d;
+}
+
+template <int DT>
+__device__ __forceinline__ G8 load_group(const char* base, uint64_t elem, int nv) {
+  return nv == 8 ? unpack8<DT>(load_raw8<DT, false>(base, elem)) : load_part8<DT>(base, elem, nv);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_group(char* base, uint64_t elem, int nv, const G8& g) {
+  if (nv == 8) store_raw8<DT, false>(base, elem, pack8<DT>(g));
+  else store_part8<DT>(base, elem, nv, g);
+}
+
+// ---------------------------------------------------------------- encode (K4)
+// grid: njobs x blocks_per_job; grid-stride over the job's 8-element groups.
+// The loop bound is rounded up to whole workgroups so every lane of a wave
+// takes part in the cross-lane max; lanes past the end hold zeros.
+template <int DT, int LPB>
+__global__ __launch_bounds__(kThreads) void bfp_encode_kernel(BfpJobs jobs, int lpb_rt, int mbits,
+                                                               uint32_t blocks_per_job) {
+  const int j = (int)(blockIdx.x / blocks_per_job);
+  const uint32_t b = blockIdx.x - (uint32_t)j * blocks_per_job;
+  const int lpb = LPB > 0 ? LPB : lpb_rt;
+  const uint64_t block = (uint64_t)lpb * 8;
+  const uint64_t count = jobs.len[j];
+  const char* src = jobs.src[j];
+  uint8_t* msg = jobs.msg[j];
+  const uint64_t nb = (count + block - 1) / block;
+  const uint64_t eb = (nb + 15) / 16 * 16;
+  uint8_t* mant = msg + eb;
+  const float qmax = (float)((1 << (mbits - 1)) - 1);
+  if (b == 0 && threadIdx.x < eb - nb) msg[nb + threadIdx.x] = 0;  // exponent padding
+  const uint64_t ngroups = (count + 7) / 8;
+  const uint64_t stride = (uint64_t)blocks_per_job * kThreads;
+  for (uint64_t g0 = (uint64_t)b * kThreads; g0 < ngroups; g0 += stride) {
+    const uint64_t elem = (g0 + threadIdx.x) * 8;
+    const int nv = elem >= count ? 0 : (count - elem >= 8 ? 8 : (int)(count - elem));
+    G8 x = load_group<DT>(src, elem, nv);
+    const uint32_t m = group_max_sel<LPB>(lane_absmax(x), lpb);
+    const BfpScale sc = bfp_scale(m, mbits);
+    if (nv > 0 && (threadIdx.x & (lpb - 1)) == 0) msg[elem / block] = (uint8_t)(m >> 23);
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = sc.nan ? 0 : (int)bfp_q(x.v[i], sc.k, qmax);
+    if (mbits > 4) {
+      u32x2 w;
+      w[0] = (uint32_t)(q[0] & 0xff) | (uint32_t)(q[1] & 0xff) << 8 | (uint32_t)(q[2] & 0xff) << 16 |
+             (uint32_t)(q[3] & 0xff) << 24;
+      w[1] = (uint32_t)(q[4] & 0xff) | (uint32_t)(q[5] & 0xff) << 8 | (uint32_t)(q[6] & 0xff) << 16 |
+             (uint32_t)(q[7] & 0xff) << 24;
+      if (nv == 8) {
+        *(u32x2*)(mant + elem) = w;
+      } else {
+        for (int i = 0; i < nv; ++i) mant[elem + i] = (uint8_t)q[i];
+      }
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)(q[i] & 0xf) << (4 * i);
+      if (nv == 8) {
+        *(uint32_t*)(mant + elem / 2) = w;
+      } else {
+        for (int i = 0; i < (nv + 1) / 2; ++i) mant[elem / 2 + i] = (uint8_t)(w >> (8 * i));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode (K5)
+__device__ __forceinline__ G8 dequant_group(const uint8_t* msg, uint64_t eb, uint64_t elem, int nv,
+                                            uint64_t block, int mbits) {
+  const int E = msg[elem / block];
+  const int e = (E < 1 ? 1 : E) - 127;
+  const int k = mbits - 2 - e;
+  const uint8_t* mant = msg + eb;
+  int q[8];
+  if (mbits > 4) {
+    if (nv == 8) {
+      u32x2 w = *(const u32x2*)(mant + elem);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[i] = (int)(int8_t)(w[0] >> (8 * i));
+        q[4 + i] = (int)(int8_t)(w[1] >> (8 * i));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = i < nv ? (int)(int8_t)mant[elem + i] : 0;
+    }
+  } else {
+    uint32_t w = 0;
+    if (nv == 8) {
+      w = *(const uint32_t*)(mant + elem / 2);
+    } else {
+      for (int i = 0; i < (nv + 1) / 2; ++i) w |= (uint32_t)mant[elem / 2 + i] << (8 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = ((int)(w << (28 - 4 * i))) >> 28;  // sign-extend nibble i
+  }
+  G8 d;
+  const float nanv = __builtin_nanf("");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) d.v[i] = E == 255 ? nanv : bfp_dq((float)q[i], k);
+  return d;
+}
+
+template <int DT, bool ACC>
+__global__ __launch_bounds__(kThreads) void bfp_decode_kernel(BfpJobs jobs, int block, int mbits,
+                                                               uint32_t blocks_per_job) {
+  const int j = (int)(blockIdx.x / blocks_per_job);
+  const uint32_t b = blockIdx.x - (uint32_t)j * blocks_per_job;
+  const uint64_t count = jobs.len[j];
+  const uint8_t* msg = jobs.msg[j];
+  char* dst = jobs.dst[j];
+  const uint64_t eb = bfp_exp_bytes(count, block);
+  const uint64_t ngroups = (count + 7) / 8;
+  const uint64_t stride = (uint64_t)blocks_per_job * kThreads;
+  for (uint64_t g = (uint64_t)b * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    const uint64_t elem = g * 8;
+    const int nv = count - elem >= 8 ? 8 : (int)(count - elem);
+    G8 d = dequant_group(msg, eb, elem, nv, (uint64_t)block, mbits);
+    if constexpr (ACC) {
+      G8 a = load_group<DT>(dst, elem, nv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d.v[i] = round_to<DT>(a.v[i] + d.v[i]);
+    }
+    store_group<DT>(dst, elem, nv, d);
+  }
+}
+
+// Decode once, store to `nfan` rank buffers at elem_off[j] + element.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void bfp_decode_fanout_kernel(BfpJobs jobs, RankPtrs fan,
+                                                                      int nfan, int block, int mbits,
+                                                                      uint32_t blocks_per_job) {
+  const int j = (int)(blockIdx.x / blocks_per_job);
+  const uint32_t b = blockIdx.x - (uint32_t)j * blocks_per_job;
+  const uint64_t count = jobs.len[j];
+  const uint8_t* msg = jobs.msg[j];
+  const uint64_t off = (uint64_t)(uintptr_t)jobs.dst[j];  // element offset carried in dst
+  const uint64_t eb = bfp_exp_bytes(count, block);
+  const uint64_t ngroups = (count + 7) / 8;
+  const uint64_t stride = (uint64_t)blocks_per_job * kThreads;
+  for (uint64_t g = (uint64_t)b * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    const uint64_t elem = g * 8;
+    const int nv = count - elem >= 8 ? 8 : (int)(count - elem);
+    G8 d = dequant_group(msg, eb, elem, nv, (uint64_t)block, mbits);
+    if (nv == 8) {
+      Raw8<DT> r = pack8<DT>(d);
+      for (int f = 0; f < nfan; ++f) store_raw8<DT, true>(fan.p[f], off + elem, r);
+    } else {
+      for (int f = 0; f < nfan; ++f) store_part8<DT>(fan.p[f], off + elem, nv, d);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fused compressed ring (K6)
+// Workgroup = tile of one chunk c (chunk length L is a multiple of the block,
+// so lanes [j*LPB, (j+1)*LPB) always hold one whole block).  Per block:
+//   p = x_{c+1};  p = round(x_{c+k} + qdq(p)) for k = 2..N;  y = round(qdq(p))
+// and y goes to every rank.  All lanes stay active through the cross-lane
+// maxima; lanes past the end of the data hold zeros and store nothing.
+template <int DT, int NR, int LPB, int G>
+__global__ __launch_bounds__(kThreads) void bfp_ring_fold_kernel(RankPtrs bufs, int nranks,
+                                                                  uint64_t count, uint64_t L,
+                                                                  uint32_t tiles_per_chunk, int lpb_rt,
+                                                                  int mbits) {
+  const int N = NR > 0 ? NR : nranks;
+  const int lpb = LPB > 0 ? LPB : lpb_rt;
+  const uint32_t c = blockIdx.x / tiles_per_chunk;
+  const uint32_t t = blockIdx.x - c * tiles_per_chunk;
+  const uint64_t lo = (uint64_t)c * L;
+  if (lo >= count) return;
+  const uint64_t hi = lo + L < count ? lo + L : count;
+  constexpr uint64_t kTile = (uint64_t)kThreads * kGroupElems * G;
+  const uint64_t tile0 = lo + (uint64_t)t * kTile;
+  if (tile0 >= hi) return;
+  const uint64_t e0 = tile0 + (uint64_t)threadIdx.x * kGroupElems;
+  const int first = (int)c + 1 < N ? (int)c + 1 : 0;
+  const float qmax = (float)((1 << (mbits - 1)) - 1);
+
+  int nv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
+    nv[g] = e >= hi ? 0 : (hi - e >= 8 ? 8 : (int)(hi - e));
+  }
+  const bool full = tile0 + kTile <= hi;
+
+  auto load = [&](int rank, int g) -> G8 {
+    const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
+    if (full) return unpack8<DT>(load_raw8<DT, true>(bufs.p[rank], e));
+    return load_part8<DT>(bufs.p[rank], e, nv[g]);
+  };
+  auto qdq = [&](const G8& p) -> G8 {
+    const uint32_t m = group_max_sel<LPB>(lane_absmax(p), lpb);
+    return qdq8(p, bfp_scale(m, mbits), qmax);
+  };
+
+  G8 p[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) p[g] = load(first, g);
+  int r = first;
+  auto hop = [&]() {
+    r = r + 1 == N ? 0 : r + 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      G8 x = load(r, g);
+      G8 d = qdq(p[g]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[g].v[i] = round_to<DT>(x.v[i] + d.v[i]);
+    }
+  };
+  if constexpr (NR > 0) {
+#pragma unroll
+    for (int k = 2; k <= NR; ++k) hop();
+  } else {
+    for (int k = 2; k <= N; ++k) hop();
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    G8 y = qdq(p[g]);
+    const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
+    if (full) {
+      Raw8<DT> out = pack8<DT>(y);
+      for (int d = 0; d < N; ++d) store_raw8<DT, true>(bufs.p[d], e, out);
+    } else if (nv[g] > 0) {
+      for (int d = 0; d < N; ++d) store_part8<DT>(bufs.p[d], e, nv[g], y);
+    }
+  }
+}
+
+struct U64Vals {
+  uint64_t v[2 * kMaxRanks];
+};
+
+__global__ void fill_u64_kernel(uint64_t* dst, int n, U64Vals vals) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = vals.v[i];
+}
+
+uint32_t blocks_for(uint64_t maxlen) {
+  const uint64_t groups = (maxlen + 7) / 8;
+  uint64_t blocks = (groups + kThreads - 1) / kThreads;
+  if (blocks > kEncBlocksPerJob) blocks = kEncBlocksPerJob;
+  return (uint32_t)(blocks ? blocks : 1);
+}
+
+uint64_t max_len(const BfpJobs& jobs) {
+  uint64_t m = 0;
+  for (int j = 0; j < jobs.njobs; ++j) m = jobs.len[j] > m ? jobs.len[j] : m;
+  return m;
+}
+
+template <int DT>
+void encode_dispatch(const BfpJobs& jobs, int block, int mbits, dim3 grid, uint32_t bpj,
+                     hipStream_t stream) {
+  if (block == 128)
+    hipLaunchKernelGGL((bfp_encode_kernel<DT, 16>), grid, dim3(kThreads), 0, stream, jobs, 16, mbits, bpj);
+  else
+    hipLaunchKernelGGL((bfp_encode_kernel<DT, 0>), grid, dim3(kThreads), 0, stream, jobs, block / 8, mbits,
+                       bpj);
+}
+
+template <int DT, int NR>
+void fold_dispatch_lpb(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
+                       uint32_t tiles, hipStream_t stream) {
+  dim3 grid((unsigned)((uint64_t)n * tiles));
+  if (block == 128)
+    hipLaunchKernelGGL((bfp_ring_fold_kernel<DT, NR, 16, 1>), grid, dim3(kThreads), 0, stream, bufs, n, count,
+                       L, tiles, 16, mbits);
+  else
+    hipLaunchKernelGGL((bfp_ring_fold_kernel<DT, NR, 0, 1>), grid, dim3(kThreads), 0, stream, bufs, n, count,
+                       L, tiles, block / 8, mbits);
+}
+
+template <int DT>
+void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
+                      uint32_t tiles, hipStream_t stream) {
+  if (n == 8) fold_dispatch_lpb<DT, 8>(bufs, n, count, L, block, mbits, tiles, stream);
+  else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, tiles, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
+  const uint64_t ml = max_len(jobs);
+  if (jobs.njobs == 0 || ml == 0) return hipSuccess;
+  const uint32_t bpj = blocks_for(ml);
+  dim3 grid((unsigned)(jobs.njobs * bpj));
+  switch (dt) {
+    case DT_F32: encode_dispatch<DT_F32>(jobs, block, mbits, grid, bpj, stream); break;
+    case DT_F16: encode_dispatch<DT_F16>(jobs, block, mbits, grid, bpj, stream); break;
+    default: encode_dispatch<DT_BF16>(jobs, block, mbits, grid, bpj, stream); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bfp_decode(const BfpJobs& jobs, int dt, int block, int mbits, bool accumulate,
+                             hipStream_t stream) {
+  const uint64_t ml = max_len(jobs);
+  if (jobs.njobs == 0 || ml == 0) return hipSuccess;
+  const uint32_t bpj = blocks_for(ml);
+  dim3 grid((unsigned)(jobs.njobs * bpj)), blk(kThreads);
+#define RAR_DEC(DTV)                                                                                   \
+  if (accumulate)                                                                                      \
+    hipLaunchKernelGGL((bfp_decode_kernel<DTV, true>), grid, blk, 0, stream, jobs, block, mbits, bpj); \
+  else                                                                                                 \
+    hipLaunchKernelGGL((bfp_decode_kernel<DTV, false>), grid, blk, 0, stream, jobs, block, mbits, bpj);
+  switch (dt) {
+    case DT_F32: RAR_DEC(DT_F32) break;
+    case DT_F16: RAR_DEC(DT_F16) break;
+    default: RAR_DEC(DT_BF16) break;
+  }
+#undef RAR_DEC
+  return hipGetLastError();
+}
+
+hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan, int nfan,
+                                    uint64_t elem_off[kMaxRanks], int dt, int block, int mbits,
+                                    hipStream_t stream) {
+  BfpJobs jobs = jobs_in;
+  for (int j = 0; j < jobs.njobs; ++j) jobs.dst[j] = (char*)(uintptr_t)elem_off[j];
+  const uint64_t ml = max_len(jobs);
+  if (jobs.njobs == 0 || ml == 0) return hipSuccess;
+  const uint32_t bpj = blocks_for(ml);
+  dim3 grid((unsigned)(jobs.njobs * bpj)), blk(kThreads);
+  switch (dt) {
+    case DT_F32:
+      hipLaunchKernelGGL((bfp_decode_fanout_kernel<DT_F32>), grid, blk, 0, stream, jobs, fan, nfan, block, mbits, bpj);
+      break;
+    case DT_F16:
+      hipLaunchKernelGGL((bfp_decode_fanout_kernel<DT_F16>), grid, blk, 0, stream, jobs, fan, nfan, block, mbits, bpj);
+      break;
+    default:
+      hipLaunchKernelGGL((bfp_decode_fanout_kernel<DT_BF16>), grid, blk, 0, stream, jobs, fan, nfan, block, mbits, bpj);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
+                                int block, int mbits, hipStream_t stream) {
+  const uint64_t tile = (uint64_t)kThreads * kGroupElems;
+  const uint32_t tiles = (uint32_t)((L + tile - 1) / tile);
+  if (tiles == 0) return hipSuccess;
+  switch (dt) {
+    case DT_F32: fold_dispatch_nr<DT_F32>(bufs, n, count, L, block, mbits, tiles, stream); break;
+    case DT_F16: fold_dispatch_nr<DT_F16>(bufs, n, count, L, block, mbits, tiles, stream); break;
+    default: fold_dispatch_nr<DT_BF16>(bufs, n, count, L, block, mbits, tiles, stream); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u64(uint64_t* dst, const uint64_t* host_vals, int nvals, hipStream_t stream) {
+  U64Vals vals{};
+  if (nvals > 2 * kMaxRanks) nvals = 2 * kMaxRanks;
+  for (int i = 0; i < nvals; ++i) vals.v[i] = host_vals[i];
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(2 * kMaxRanks), 0, stream, dst, nvals, vals);
+  return hipGetLastError();
+}
+
+}  // namespace rar

@@ -1,0 +1,88 @@
+// Host-side launchers of the gfx950 kernels (internal to librar.so).
+// Every launcher enqueues asynchronously on `stream` and returns a
+// hipError_t from hipGetLastError() after the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace rar {
+
+// -------------------------------------------------------------- ring (ring_kernels.hip)
+
+// Fused ring fold over all chunks: chunk c of every element position gets
+// the fold of ranks c+1, ..., c+N-1, c (mod N); stored to every rank
+// (store_all) or to the owner c only (reduce-scatter).
+hipError_t launch_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
+                            bool store_all, hipStream_t stream);
+
+// One reduce-scatter step s: rank r <- rank r (+) rank r-1 on chunk (r-s-1) mod N.
+hipError_t launch_rs_step(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt, int s,
+                          hipStream_t stream);
+
+// Byte-range copies from one rank buffer to a set of rank buffers, at the
+// same offset in each.  Up to kMaxRanks jobs per launch.
+struct CopyJobs {
+  RankPtrs ptrs;
+  uint64_t lo[kMaxRanks];       // byte offset of the range
+  uint64_t len[kMaxRanks];      // bytes (a multiple of 2)
+  uint64_t dstmask[kMaxRanks];  // bit d set: write rank d
+  int8_t src[kMaxRanks];        // source rank
+  int njobs;
+};
+hipError_t launch_copy_jobs(const CopyJobs& jobs, hipStream_t stream);
+
+// -------------------------------------------------------------- BFP (bfp_kernels.hip)
+
+// One contiguous message job: `len` elements at `data` <-> message at `msg`.
+struct BfpJobs {
+  const char* src[kMaxRanks];  // encode: elements to encode
+  char* dst[kMaxRanks];        // decode: elements to write / accumulate into
+  uint8_t* msg[kMaxRanks];     // message base (exponents, then mantissas)
+  uint64_t len[kMaxRanks];     // elements
+  int njobs;
+};
+
+hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
+// accumulate: dst <- dst (+) decoded; otherwise dst <- decoded.
+hipError_t launch_bfp_decode(const BfpJobs& jobs, int dt, int block, int mbits, bool accumulate,
+                             hipStream_t stream);
+// Decode each job's message once and store it to the same element range of
+// every rank in `fan` (allgather of the compressed ring).
+hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs, const RankPtrs& fan, int nfan,
+                                    uint64_t elem_off[kMaxRanks], int dt, int block, int mbits,
+                                    hipStream_t stream);
+
+// Fused compressed ring fold: per block, the RS hop chain with an encode /
+// decode per hop kept in registers, then the allgather encode / decode;
+// the result is stored to every rank.
+hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
+                                int block, int mbits, hipStream_t stream);
+
+// -------------------------------------------------------------- buckets (bucket_kernels.hip)
+
+// Segment copies: dst[0, bytes) <- src[0, bytes), then dst[bytes, zero_to) <- 0.
+// src and dst 16-byte aligned, bytes a multiple of 2, zero_to - bytes < 16.
+struct SegJobs {
+  const char* src[kMaxRanks];
+  char* dst[kMaxRanks];
+  uint64_t bytes[kMaxRanks];
+  uint64_t zero_to[kMaxRanks];
+  int njobs;
+};
+hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream);
+
+// Small utility kernels.
+hipError_t launch_fill_u64(uint64_t* dst, const uint64_t* host_vals, int nvals, hipStream_t stream);
+
+__host__ __device__ inline uint64_t bfp_exp_bytes(uint64_t count, int block) {
+  uint64_t nb = (count + (uint64_t)block - 1) / (uint64_t)block;
+  return (nb + 15) / 16 * 16;
+}
+__host__ __device__ inline uint64_t bfp_msg_bytes(uint64_t count, int block, int mbits) {
+  return bfp_exp_bytes(count, block) + (mbits > 4 ? count : (count + 1) / 2);
+}
+
+}  // namespace rar

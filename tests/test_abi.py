@@ -1,0 +1,155 @@
+"""The C-ABI library loads and exports every symbol include/rar.h declares;
+host-only entry points (sizes, plans, argument checks) behave.  CPU only: no
+call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ring_all_reduce_scatter_amd as rar
+from ring_all_reduce_scatter_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "rar.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rar_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rar.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in rar._binding._SIGS, f"binding lacks {name}"
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in rar.version()
+    assert rar.status_string(0) == "ok"
+    assert "workspace" in rar.status_string(4)
+    assert rar.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("count,n", [(0, 1), (1, 4), (1 << 20, 4), (64 << 20, 8), (1000, 3), (12345, 16)])
+def test_chunk_len_matches_oracle(orc, count, n):
+    assert rar.chunk_len(count, n) == orc.chunk_len(count, n)
+    assert rar.chunk_len(count, n) % 128 == 0
+    assert rar.compressed_chunk_len(count, n, 512) == orc.comp_chunk_len(count, n, 512)
+
+
+@pytest.mark.parametrize("count", [0, 1, 127, 128, 2097152, 1000003])
+@pytest.mark.parametrize("block,mbits", [(128, 8), (128, 4), (16, 2), (512, 5)])
+def test_bfp_bytes_matches_oracle(orc, count, block, mbits):
+    assert rar.bfp_bytes(count, block, mbits) == orc.bfp_bytes(count, block, mbits)
+
+
+def test_bfp_bytes_rejects_bad_args():
+    assert rar.bfp_bytes(100, 100, 8) == 0
+    assert rar.bfp_bytes(100, 128, 9) == 0
+    assert rar.bfp_bytes(100, 8, 8) == 0
+
+
+def test_compress_cfg_default_is_the_pages_starting_point():
+    cfg = rar.compress_cfg_default()
+    assert cfg.method == rar.COMP_BFP and cfg.block == 128 and cfg.mbits == 8
+    assert cfg.sparsity_threshold == 0.5 and cfg.unit_bytes == 4 << 20
+    assert cfg.collective_mask == rar.OP_ALLREDUCE and cfg.schedule == rar.SCHED_FUSED
+
+
+def test_compressed_workspace_sizes():
+    cfg = rar.compress_cfg_default()
+    assert rar.compressed_workspace_bytes(8, 128 << 20, rar.F16, cfg) == 1024
+    cfg.schedule = rar.SCHED_STAGED
+    ws = rar.compressed_workspace_bytes(8, 128 << 20, rar.F16, cfg)
+    slot = (16384 + 2097152 + 255) // 256 * 256
+    assert ws == 1024 + 8 * 8 * slot
+    cfg.unit_bytes = 1000  # not a multiple of the block
+    assert rar.compressed_workspace_bytes(8, 1 << 20, rar.F16, cfg) == 0
+
+
+def test_bucket_plan_matches_oracle(orc):
+    sizes = inputs.bucket_sizes(200)
+    for cap in (25 << 20, 1 << 20, 4 << 20):
+        nb, plan = rar.bucket_plan(sizes, rar.BF16, cap)
+        onb, oplan = orc.bucket_plan(sizes, orc.BF16, cap)
+        assert nb == onb and plan == list(oplan)
+    assert rar.bucket_plan([10, 20, 5, 100, 3, 3], rar.BF16, 60) == (4, [0, 0, 1, 2, 3, 3])
+
+
+class _FakeTensor:
+    """Stands in for a device tensor in argument-error tests (never launched)."""
+
+    def __init__(self, ptr, numel, dtype):
+        import torch
+        self._ptr, self._n, self.dtype = ptr, numel, dtype
+        self.device = torch.device("cpu")
+
+    def data_ptr(self):
+        return self._ptr
+
+    def numel(self):
+        return self._n
+
+    def is_contiguous(self):
+        return True
+
+
+def _fake(ptrs, numel=1024):
+    import torch
+    return [_FakeTensor(p, numel, torch.float32) for p in ptrs]
+
+
+def test_argument_errors_are_reported_before_any_launch():
+    base = 1 << 40
+    with pytest.raises(rar.RarError) as e:
+        rar.ring_allreduce(_fake([base + 8, base + 65536]), stream=0)
+    assert e.value.status == 3  # misaligned
+    with pytest.raises(rar.RarError) as e:
+        rar.ring_allreduce(_fake([base, base + 1024]), stream=0)  # 4 KiB buffers 1 KiB apart
+    assert e.value.status == 7
+    with pytest.raises(rar.RarError) as e:
+        rar.rs_step(_fake([base, base + 65536]), 2, stream=0)  # step must be 1..N-1
+    assert e.value.status == 1
+    with pytest.raises(rar.RarError) as e:
+        rar.broadcast(_fake([base, base + 65536]), root=2, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(rar.RarError) as e:
+        rar.allgather(_fake([base, base + 65536, base + 131072], numel=1000), stream=0)
+    assert e.value.status == 1
+    # 65 ranks is beyond the limit
+    lib = rar.lib()
+    ptrs = (ctypes.c_void_p * 65)(*[base + i * 65536 for i in range(65)])
+    assert lib.rar_ring_allreduce(ptrs, 65, 16, 0, None) == 1
+    assert lib.rar_ring_allreduce(ptrs, 2, 16, 7, None) == 2  # dtype
+    assert lib.rar_ring_allreduce_ex(ptrs, 2, 16, 0, 5, None) == 1  # algo
+
+
+def test_noop_cases_need_no_device():
+    base = 1 << 40
+    rar.ring_allreduce(_fake([base, base + 65536], numel=0), stream=0)
+    rar.ring_allreduce(_fake([base], numel=4096), stream=0)
+    sent, recv = rar.last_traffic(1)
+    assert sent == [0] and recv == [0]
+
+
+def test_compressed_rejects_small_workspace():
+    base = 1 << 40
+    lib = rar.lib()
+    ptrs = (ctypes.c_void_p * 2)(base, base + (1 << 20))
+    cfg = rar.compress_cfg(schedule=rar.SCHED_STAGED)
+    rc = lib.rar_ring_allreduce_compressed(ptrs, 2, 4096, rar.F16, ctypes.byref(cfg), base + (4 << 20), 64, None)
+    assert rc == 4
+
+
+def test_traffic_of_noop_allreduce_follows_byte_table():
+    """count=0 still records the (zero) byte table; a valid count records it
+    host-side before launching, which the GPU tests check against the oracle."""
+    base = 1 << 40
+    rar.ring_allreduce(_fake([base, base + 65536, base + 131072], numel=0), stream=0)
+    assert rar.last_traffic(3) == ([0, 0, 0], [0, 0, 0])

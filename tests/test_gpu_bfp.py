@@ -1,0 +1,233 @@
+"""GPU parity of block floating point and the compressed ring allreduce.
+
+Encoded bytes, decoded values and the compressed ring's results must equal
+the oracle's bit for bit (the compressed ring is deterministic).  At the full
+N=8, T=128M fp16 size the fused launch the benchmark times is checked on
+sampled blocks: every block's hop chain depends only on that block's N
+inputs and on its chunk's ring order, so the oracle re-runs the sampled
+blocks in a small ring where each sits in the same chunk index.  The result
+must also lie within the stated bound of the exact sum.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_all_reduce_scatter_amd as rar
+from ring_all_reduce_scatter_amd import inputs
+
+from gpu_util import DT_NAMES, as_f64, assert_bits_equal, nan_mask, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _src(dt, count, salt, kind="scaled"):
+    if kind == "scaled":
+        x = inputs.block_scaled(1, count, dtype=dt, salt=salt)[0]
+    else:
+        x = inputs.gradient_like(1, count, dtype=dt, salt=salt)[0]
+    return x
+
+
+def _msg_dev(nbytes):
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda:0")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("block", [16, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("mbits", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("count", [1, 128 * 37 + 5, 262_147])
+def test_compress_bytes_match_oracle(dt, block, mbits, count):
+    x = _src(dt, count, salt=block + mbits + count, kind="grad" if dt == "f32" else "scaled")
+    ref = oracle.bfp_encode(x, block=block, mbits=mbits, dt=DT_NAMES[dt])
+    nbytes = rar.bfp_bytes(count, block, mbits)
+    assert nbytes == ref.size
+    src = to_dev([x], dt)[0]
+    msg = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda:0")  # poison: padding must be written
+    rar.bfp_compress(src, block, mbits, msg)
+    got = msg.cpu().numpy()
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[0]}: {got[bad[0]]} vs {ref[bad[0]]}"
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("block,mbits", [(128, 8), (128, 4), (16, 3), (512, 6)])
+def test_decompress_and_accumulate_match_oracle(dt, block, mbits):
+    count = 200_003
+    x = _src(dt, count, salt=11)
+    acc0 = _src(dt, count, salt=12)
+    msg = oracle.bfp_encode(x, block=block, mbits=mbits, dt=DT_NAMES[dt])
+    ref_acc = acc0.copy()
+    oracle.bfp_decode_acc(msg, ref_acc, block=block, mbits=mbits, dt=DT_NAMES[dt])
+    odt = {"f16": np.float16, "f32": np.float32, "bf16": np.uint16}[dt]
+    ref_dec = oracle.bfp_decode(msg, count, block=block, mbits=mbits, out_dtype=odt, dt=DT_NAMES[dt])
+    m = torch.from_numpy(msg).to("cuda:0")
+    acc = to_dev([acc0], dt)[0]
+    rar.bfp_decompress_accumulate(m, count, block, mbits, acc)
+    assert_bits_equal(to_host([acc], dt)[0], ref_acc, "accumulate")
+    out = to_dev([np.zeros_like(acc0)], dt)[0]
+    rar.bfp_decompress(m, count, block, mbits, out)
+    assert_bits_equal(to_host([out], dt)[0], ref_dec, "decode")
+
+
+def test_special_blocks_match_oracle():
+    x = np.zeros(5 * 128, dtype=np.float32)
+    x[0:128] = -0.0
+    x[128:256] = 1.0
+    x[130] = np.inf
+    x[256:384] = np.linspace(-3, 3, 128)
+    x[300] = np.nan
+    x[384:512] = np.float32(2.0 ** -130)
+    x[512:640] = np.linspace(-1e-6, 1.0, 128)
+    ref = oracle.bfp_encode(x)
+    src = to_dev([x], "f32")[0]
+    msg = _msg_dev(ref.size)
+    rar.bfp_compress(src, 128, 8, msg)
+    assert np.array_equal(msg.cpu().numpy()[:ref.size], ref)
+    out = torch.zeros(x.size, dtype=torch.float32, device="cuda:0")
+    rar.bfp_decompress(msg, x.size, 128, 8, out)
+    got = out.cpu().numpy()
+    dec = oracle.bfp_decode(ref, x.size)
+    nan = np.isnan(dec)
+    assert np.array_equal(np.isnan(got), nan)
+    assert_bits_equal(got[~nan], dec[~nan], "non-NaN blocks")
+
+
+# ------------------------------------------------------------------ compressed ring
+
+SCHEDS = {"fused": rar.SCHED_FUSED, "staged": rar.SCHED_STAGED}
+
+
+def _run_compressed(xs, dt, sched, block=128, mbits=8, unit_elems=4096, method=rar.COMP_BFP):
+    n, count = len(xs), xs[0].size
+    es = 4 if dt == "f32" else 2
+    cfg = rar.compress_cfg(method=method, block=block, mbits=mbits, unit_bytes=unit_elems * es,
+                           schedule=SCHEDS[sched])
+    ws_bytes = rar.compressed_workspace_bytes(n, count, DT_NAMES[dt], cfg)
+    assert ws_bytes > 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    bufs = to_dev(xs, dt)
+    rar.ring_allreduce_compressed(bufs, cfg, ws)
+    sent, recv = rar.compressed_traffic(ws, n)
+    return to_host(bufs, dt), sent, recv
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("sched", ["fused", "staged"])
+@pytest.mark.parametrize("mbits", [8, 4])
+def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
+    count = n * 4096 * 2 + 1000  # several units per chunk and a ragged last chunk
+    xs = inputs.block_scaled(n, count, dtype=dt, salt=n * 10 + mbits)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce_compressed(ref, mbits=mbits, unit=4096, dt=DT_NAMES[dt])
+    got, sent, recv = _run_compressed(xs, dt, sched, mbits=mbits)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+    assert sent == osent and recv == orecv
+
+
+@pytest.mark.parametrize("block", [16, 64, 256, 512])
+@pytest.mark.parametrize("sched", ["fused", "staged"])
+def test_compressed_allreduce_other_blocks(block, sched):
+    n, count = 4, 4 * 8192 + 900
+    xs = inputs.block_scaled(n, count, block=block, salt=block)
+    ref = [x.copy() for x in xs]
+    oracle.ring_allreduce_compressed(ref, block=block, mbits=6, unit=8192)
+    got, _, _ = _run_compressed(xs, "f16", sched, block=block, mbits=6, unit_elems=8192)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+
+
+def test_compressed_integer_inputs_are_exact():
+    n, count = 8, 8 * 4096
+    xs = inputs.integers(n, count, dtype="f16", salt=5)
+    exact = sum(x.astype(np.float64) for x in xs)
+    for sched in ("fused", "staged"):
+        got, _, _ = _run_compressed(xs, "f16", sched)
+        for g in got:
+            assert np.array_equal(g.astype(np.float64), exact)
+
+
+def test_collective_mask_without_allreduce_runs_uncompressed():
+    n, count = 4, 10_000
+    xs = inputs.gradient_like(n, count, dtype="f16", salt=9)
+    ref = [x.copy() for x in xs]
+    oracle.ring_allreduce(ref)
+    cfg = rar.compress_cfg(collective_mask=rar.OP_BROADCAST)
+    ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
+    bufs = to_dev(xs, "f16")
+    rar.ring_allreduce_compressed(bufs, cfg, ws)
+    for r, g in enumerate(to_host(bufs, "f16")):
+        assert_bits_equal(g, ref[r], f"rank {r}")
+
+
+def _sampled_blocks_check(xs, got_rank0, got_ranks_equal, L, mbits, nsamp_per_chunk, seed):
+    """Re-run sampled blocks in the oracle; returns the max error ratio to the bound."""
+    n, count = len(xs), xs[0].size
+    g = np.random.default_rng(seed)
+    K = nsamp_per_chunk
+    mini = [np.zeros(n * K * 128, dtype=np.float16) for _ in range(n)]
+    picks = []
+    for c in range(n):
+        nblk = (min((c + 1) * L, count) - c * L) // 128
+        bl = np.sort(g.choice(nblk, size=K, replace=False)) + c * L // 128
+        picks.append(bl)
+        for r in range(n):
+            for k, b in enumerate(bl):
+                mini[r][(c * K + k) * 128:(c * K + k + 1) * 128] = xs[r][b * 128:(b + 1) * 128]
+    raw = [m.copy() for m in mini]
+    _, _, bm = oracle.ring_allreduce_compressed(mini, mbits=mbits, unit=K * 128, with_blockmax=True)
+    worst = 0.0
+    for c in range(n):
+        for k, b in enumerate(picks[c]):
+            sl = slice((c * K + k) * 128, (c * K + k + 1) * 128)
+            gsl = slice(b * 128, (b + 1) * 128)
+            assert_bits_equal(got_rank0[gsl], mini[0][sl], f"block {b}")
+            exact = sum(r_[sl].astype(np.float64) for r_ in raw)
+            err = np.abs(got_rank0[gsl].astype(np.float64) - exact)
+            bound = n * 2.0 ** -(mbits - 1) * bm[c * K + k]
+            if bound > 0:
+                worst = max(worst, float(err.max() / bound))
+            else:
+                assert err.max() == 0
+    return worst
+
+
+@pytest.mark.slow
+def test_bfp8_workload_full_size_sampled():
+    """N=8, T=128M fp16, 128-element blocks, 8-bit mantissas: the fused launch
+    the benchmark times.  All ranks bit-identical; sampled blocks bit-exact
+    against the oracle and within N * 2^-(m-1) * blockmax of the exact sum."""
+    w = inputs.WORKLOADS["bfp8"]
+    n, count, mbits = w["n"], w["count"], w["mbits"]
+    xs = inputs.block_scaled(n, count)
+    cfg = rar.compress_cfg(mbits=mbits, unit_bytes=w["unit_bytes"])
+    ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
+    bufs = to_dev(xs, "f16")
+    rar.ring_allreduce_compressed(bufs, cfg, ws)
+    for r in range(1, n):
+        assert torch.equal(bufs[r].view(torch.int16), bufs[0].view(torch.int16)), f"rank {r} differs"
+    got0 = to_host(bufs[:1], "f16")[0]
+    del bufs
+    L = rar.compressed_chunk_len(count, n, 128)
+    worst = _sampled_blocks_check(xs, got0, True, L, mbits, nsamp_per_chunk=256, seed=1)
+    assert worst <= 1.0, worst
+
+
+@pytest.mark.slow
+def test_bfp8_staged_equals_fused_full_size():
+    """The staged two-stream pipeline (4 MiB units) gives the fused kernel's bits."""
+    w = inputs.WORKLOADS["bfp8"]
+    n, count = w["n"], w["count"] // 4
+    xs = inputs.block_scaled(n, count, salt=3)
+    outs = []
+    for sched in (rar.SCHED_FUSED, rar.SCHED_STAGED):
+        cfg = rar.compress_cfg(mbits=8, unit_bytes=w["unit_bytes"], schedule=sched)
+        ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8,
+                         device="cuda:0")
+        bufs = to_dev(xs, "f16")
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+        outs.append(bufs)
+    for r in range(n):
+        assert torch.equal(outs[0][r].view(torch.int16), outs[1][r].view(torch.int16)), f"rank {r}"
