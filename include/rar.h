@@ -32,7 +32,8 @@
  *  - Errors in the arguments are reported synchronously, before anything is
  *    enqueued, by a nonzero rar_status; nothing is modified then.  A failed
  *    kernel launch returns RAR_EHIP.  No call aborts or throws.
- *  - count == 0 and nranks == 1 are valid and leave the buffers unchanged.
+ *  - count == 0 and nranks == 1 are valid and leave the buffers unchanged;
+ *    with count == 0 the buffer pointers are not inspected (NULL is fine).
  *  - Element types: RAR_F32 (binary32), RAR_F16 (binary16), RAR_BF16
  *    (bfloat16).  The reduce op is SUM.  fp32 adds are IEEE binary32
  *    round-to-nearest-even with subnormals kept; fp16/bf16 adds widen both

@@ -64,10 +64,12 @@ void chunk_range(size_t count, size_t L, int c, size_t* lo, size_t* hi) {
 int hip_rc(hipError_t e) { return e == hipSuccess ? RAR_OK : RAR_EHIP; }
 
 // N distinct, non-null, 16-byte aligned, non-overlapping buffers of `bytes`.
+// Zero-byte buffers touch no memory, so any pointer (NULL included) is fine.
 int check_bufs(void* const* bufs, int n, int dt, size_t bytes) {
   if (n < 1 || n > RAR_MAX_RANKS) return RAR_EINVAL;
   if (!dt_ok(dt)) return RAR_EDTYPE;
   if (!bufs) return RAR_EOVERLAP;
+  if (bytes == 0) return RAR_OK;
   std::vector<uintptr_t> a((size_t)n);
   for (int r = 0; r < n; ++r) {
     if (!bufs[r]) return RAR_EOVERLAP;
