@@ -326,7 +326,7 @@ def extra_legs(args):
         sets = make_sets(pristine, 1 + steps)
         ms, k, _ = time_leg(fn, sets, 2, steps)
         Sx = cnt * 4
-        moved = 8 * Sx if name.endswith("broadcast_fused") else 2 * 8 * Sx * 7 // 8 + Sx
+        moved = 8 * Sx  # broadcast: read S once, write 7 S; allgather: read S (all shards), write 7 S
         bus = Sx / (ms * 1e-3) / 1e9 if "broadcast" in name else Sx * 7 / 8 / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "busbw_GBs": round(bus, 1),
                      "frac_of_roofline": round(moved / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

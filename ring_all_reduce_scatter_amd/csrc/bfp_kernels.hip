@@ -220,13 +220,13 @@ __global__ __launch_bounds__(kThreads) void bfp_decode_fanout_kernel(BfpJobs job
 // maxima; lanes past the end of the data hold zeros and store nothing.
 template <int DT, int NR, int LPB, int G>
 __global__ __launch_bounds__(kThreads) void bfp_ring_fold_kernel(RankPtrs bufs, int nranks,
-                                                                  uint64_t count, uint64_t L,
-                                                                  uint32_t tiles_per_chunk, int lpb_rt,
+                                                                  uint64_t count, uint64_t L, int lpb_rt,
                                                                   int mbits) {
   const int N = NR > 0 ? NR : nranks;
   const int lpb = LPB > 0 ? LPB : lpb_rt;
-  const uint32_t c = blockIdx.x / tiles_per_chunk;
-  const uint32_t t = blockIdx.x - c * tiles_per_chunk;
+  // chunk fastest: resident workgroups cover every chunk's ring rotation
+  const uint32_t c = blockIdx.x % (uint32_t)N;
+  const uint32_t t = blockIdx.x / (uint32_t)N;
   const uint64_t lo = (uint64_t)c * L;
   if (lo >= count) return;
   const uint64_t hi = lo + L < count ? lo + L : count;
@@ -320,23 +320,32 @@ void encode_dispatch(const BfpJobs& jobs, int block, int mbits, dim3 grid, uint3
                        bpj);
 }
 
+// 8-element groups per thread in the fused compressed fold.
+template <int DT>
+struct BfpFoldGroups {
+  static constexpr int value = 1;
+};
+
 template <int DT, int NR>
 void fold_dispatch_lpb(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
-                       uint32_t tiles, hipStream_t stream) {
+                       hipStream_t stream) {
+  constexpr int G = BfpFoldGroups<DT>::value;
+  const uint64_t tile = (uint64_t)kThreads * kGroupElems * G;
+  const uint64_t tiles = (L + tile - 1) / tile;
   dim3 grid((unsigned)((uint64_t)n * tiles));
   if (block == 128)
-    hipLaunchKernelGGL((bfp_ring_fold_kernel<DT, NR, 16, 1>), grid, dim3(kThreads), 0, stream, bufs, n, count,
-                       L, tiles, 16, mbits);
+    hipLaunchKernelGGL((bfp_ring_fold_kernel<DT, NR, 16, G>), grid, dim3(kThreads), 0, stream, bufs, n, count,
+                       L, 16, mbits);
   else
-    hipLaunchKernelGGL((bfp_ring_fold_kernel<DT, NR, 0, 1>), grid, dim3(kThreads), 0, stream, bufs, n, count,
-                       L, tiles, block / 8, mbits);
+    hipLaunchKernelGGL((bfp_ring_fold_kernel<DT, NR, 0, G>), grid, dim3(kThreads), 0, stream, bufs, n, count,
+                       L, block / 8, mbits);
 }
 
 template <int DT>
 void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
-                      uint32_t tiles, hipStream_t stream) {
-  if (n == 8) fold_dispatch_lpb<DT, 8>(bufs, n, count, L, block, mbits, tiles, stream);
-  else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, tiles, stream);
+                      hipStream_t stream) {
+  if (n == 8) fold_dispatch_lpb<DT, 8>(bufs, n, count, L, block, mbits, stream);
+  else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, stream);
 }
 
 }  // namespace
@@ -399,13 +408,11 @@ hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan,
 
 hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
                                 int block, int mbits, hipStream_t stream) {
-  const uint64_t tile = (uint64_t)kThreads * kGroupElems;
-  const uint32_t tiles = (uint32_t)((L + tile - 1) / tile);
-  if (tiles == 0) return hipSuccess;
+  if (L == 0 || count == 0) return hipSuccess;
   switch (dt) {
-    case DT_F32: fold_dispatch_nr<DT_F32>(bufs, n, count, L, block, mbits, tiles, stream); break;
-    case DT_F16: fold_dispatch_nr<DT_F16>(bufs, n, count, L, block, mbits, tiles, stream); break;
-    default: fold_dispatch_nr<DT_BF16>(bufs, n, count, L, block, mbits, tiles, stream); break;
+    case DT_F32: fold_dispatch_nr<DT_F32>(bufs, n, count, L, block, mbits, stream); break;
+    case DT_F16: fold_dispatch_nr<DT_F16>(bufs, n, count, L, block, mbits, stream); break;
+    default: fold_dispatch_nr<DT_BF16>(bufs, n, count, L, block, mbits, stream); break;
   }
   return hipGetLastError();
 }

@@ -140,6 +140,57 @@ __device__ __forceinline__ Raw8<DT> pack8(const G8& g) {
   return r;
 }
 
+// 16-byte vectors: 4 fp32 or 8 fp16/bf16 elements.  In the streaming
+// kernels lane t of a workgroup touches bytes [16 t, 16 t + 16) of each
+// 16*kThreads-byte slab, so every load or store instruction of a wavefront
+// covers 1 KiB of contiguous memory.
+template <int DT>
+struct Vec {
+  static constexpr int E = 16 / DtypeSize<DT>::value;
+  float v[E];
+};
+
+template <int DT>
+__device__ __forceinline__ Vec<DT> unpack16(u32x4 w) {
+  Vec<DT> x;
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.v[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x.v[2 * i] = widen16<DT>(w[i] & 0xffffu);
+      x.v[2 * i + 1] = widen16<DT>(w[i] >> 16);
+    }
+  }
+  return x;
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 pack16(const Vec<DT>& x) {
+  u32x4 w;
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(x.v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = narrow16<DT>(x.v[2 * i]) | (narrow16<DT>(x.v[2 * i + 1]) << 16);
+  }
+  return w;
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const char* base, uint64_t i) {
+  if constexpr (DT == DT_F32) return ((const float*)base)[i];
+  else return widen16<DT>(((const uint16_t*)base)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(char* base, uint64_t i, float x) {
+  if constexpr (DT == DT_F32) ((float*)base)[i] = x;
+  else ((uint16_t*)base)[i] = (uint16_t)narrow16<DT>(x);
+}
+
 // Element-wise access for ragged tails (elements [elem, elem+n), n < 8);
 // missing elements read as +0.
 template <int DT>

@@ -10,6 +10,16 @@
 
 namespace rar {
 
+// -------------------------------------------------------------- residency control
+// Streaming kernels keep most HBM efficiency with about 64 KiB of loads in
+// flight per CU; at full occupancy the memory controllers see too many
+// outstanding requests and throughput drops (measured on MI355X: the fp32
+// N=8 fold moves 5.7 TB/s at 8 workgroups per CU, 6.1 TB/s at 1).  A launch
+// caps its workgroups per CU by reserving dynamic LDS it does not use:
+// residency_lds(w) is just over 1/(w+1) of the CU's LDS, so w workgroups fit
+// and w+1 do not.  0 = no cap.
+size_t residency_lds(int wgs_per_cu);
+
 // -------------------------------------------------------------- ring (ring_kernels.hip)
 
 // Fused ring fold over all chunks: chunk c of every element position gets

@@ -15,126 +15,166 @@
 //    order the reduce-scatter steps produce (ranks c+1, c+2, ..., c+N-1, c),
 //    and stores the sum to every rank.  HBM traffic is the minimum: N*S read,
 //    N*S written.
+#include <atomic>
+
 #include "launch.hpp"
 
 namespace rar {
 
 namespace {
 
-constexpr int kFoldGroups = 2;  // 8-element groups per thread in ring_fold
-constexpr int kStepGroups = 2;  // ... in rs_step
-constexpr int kCopyVecs = 4;    // 16-byte vectors per thread in copy_jobs
+// 16-byte vectors per thread and workgroups per CU of the fused fold, tuned
+// for N = 8 on MI355X (about 64 KiB of loads in flight per CU).  bf16 spends
+// more ALU per byte on its software rounding, so it keeps one vector per rank
+// and two workgroups per CU to hide that latency.
+template <int DT>
+struct FoldVecs {
+  static constexpr int value = DT == DT_BF16 ? 1 : 2;
+};
+// Workgroups per CU for the fold over n ranks: keeps n * vectors * waves
+// (the loads in flight per CU) at its N = 8 optimum; 0 = no cap.
+int fold_wgs_per_cu(int dt, int n) {
+  const int at8 = dt == DT_BF16 ? 2 : 1;
+  const int w = n > 0 ? at8 * 8 / n : at8;
+  return w < 1 ? 1 : (w >= 8 ? 0 : w);
+}
+constexpr int kStepVecs = 4;  // ... in rs_step
+constexpr int kCopyVecs = 4;  // ... in copy_jobs
 
-template <int DT, int NR, int G, bool STORE_ALL>
+// Workgroup -> (chunk, tile) with the chunk fastest: workgroups resident at
+// the same time cover every chunk (and the ring rotation of every chunk), and
+// the launch order spreads each chunk over all XCDs alike.
+__device__ __forceinline__ void chunk_tile(int N, uint32_t* c, uint32_t* t) {
+  *c = blockIdx.x % (uint32_t)N;
+  *t = blockIdx.x / (uint32_t)N;
+}
+
+template <int DT, int NR, int V, bool STORE_ALL>
 __global__ __launch_bounds__(kThreads) void ring_fold_kernel(RankPtrs bufs, int nranks,
-                                                              uint64_t count, uint64_t L,
-                                                              uint32_t tiles_per_chunk) {
+                                                              uint64_t count, uint64_t L) {
+  constexpr int E = Vec<DT>::E;
+  constexpr int ES = DtypeSize<DT>::value;
   const int N = NR > 0 ? NR : nranks;
-  const uint32_t c = blockIdx.x / tiles_per_chunk;
-  const uint32_t t = blockIdx.x - c * tiles_per_chunk;
+  uint32_t c, t;
+  chunk_tile(N, &c, &t);
   const uint64_t lo = (uint64_t)c * L;
   if (lo >= count) return;
   const uint64_t hi = lo + L < count ? lo + L : count;
-  constexpr uint64_t kTile = (uint64_t)kThreads * kGroupElems * G;
+  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
   const uint64_t tile0 = lo + (uint64_t)t * kTile;
   if (tile0 >= hi) return;
-  const uint64_t e0 = tile0 + (uint64_t)threadIdx.x * kGroupElems;
   const int first = (int)c + 1 < N ? (int)c + 1 : 0;
+  auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
 
   if (tile0 + kTile <= hi) {
-    // Full tile: vector loads, fold in ring order in registers.
-    G8 acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      acc[g] = unpack8<DT>(load_raw8<DT, true>(bufs.p[first], e0 + (uint64_t)g * kThreads * kGroupElems));
-    int r = first;
-    auto hop = [&]() {
-      r = r + 1 == N ? 0 : r + 1;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        G8 x = unpack8<DT>(load_raw8<DT, true>(bufs.p[r], e0 + (uint64_t)g * kThreads * kGroupElems));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[g].v[i] = round_to<DT>(x.v[i] + acc[g].v[i]);
-      }
-    };
+    // Full tile: every rank's vectors are loaded before the fold, which runs
+    // in ring order (ranks c+1, ..., c+N-1, c) in registers.
+    Vec<DT> acc[V];
     if constexpr (NR > 0) {
+      u32x4 x[NR][V];
+      int r = first;
 #pragma unroll
-      for (int k = 2; k <= NR; ++k) hop();
+      for (int k = 0; k < NR; ++k) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[k][v] = ld16<true>(bufs.p[r] + elem(v) * ES);
+        r = r + 1 == NR ? 0 : r + 1;
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        acc[v] = unpack16<DT>(x[0][v]);
+#pragma unroll
+        for (int k = 1; k < NR; ++k) {
+          const Vec<DT> y = unpack16<DT>(x[k][v]);
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
+        }
+      }
     } else {
-      for (int k = 2; k <= N; ++k) hop();
+      int r = first;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = unpack16<DT>(ld16<true>(bufs.p[r] + elem(v) * ES));
+      for (int k = 1; k < N; ++k) {
+        r = r + 1 == N ? 0 : r + 1;
+        u32x4 x[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = ld16<true>(bufs.p[r] + elem(v) * ES);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const Vec<DT> y = unpack16<DT>(x[v]);
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
+        }
+      }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      Raw8<DT> out = pack8<DT>(acc[g]);
-      const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
+    for (int v = 0; v < V; ++v) {
+      const u32x4 out = pack16<DT>(acc[v]);
       if constexpr (STORE_ALL) {
-        for (int d = 0; d < N; ++d) store_raw8<DT, true>(bufs.p[d], e, out);
+        for (int d = 0; d < N; ++d) st16<true>(bufs.p[d] + elem(v) * ES, out);
       } else {
-        store_raw8<DT, true>(bufs.p[c], e, out);
+        st16<true>(bufs.p[c] + elem(v) * ES, out);
       }
     }
     return;
   }
 
-  // Ragged tile (only the last tile of the last non-empty chunk).
-  for (int g = 0; g < G; ++g) {
-    const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
-    if (e >= hi) break;
-    const int nv = hi - e >= 8 ? 8 : (int)(hi - e);
-    G8 acc = load_part8<DT>(bufs.p[first], e, nv);
-    int r = first;
-    for (int k = 2; k <= N; ++k) {
-      r = r + 1 == N ? 0 : r + 1;
-      G8 x = load_part8<DT>(bufs.p[r], e, nv);
-      for (int i = 0; i < 8; ++i) acc.v[i] = round_to<DT>(x.v[i] + acc.v[i]);
-    }
-    if constexpr (STORE_ALL) {
-      for (int d = 0; d < N; ++d) store_part8<DT>(bufs.p[d], e, nv, acc);
-    } else {
-      store_part8<DT>(bufs.p[c], e, nv, acc);
+  // Ragged tile (the last tile of a chunk): element by element.
+  for (int v = 0; v < V; ++v) {
+    const uint64_t e = elem(v);
+    for (int i = 0; i < E && e + i < hi; ++i) {
+      int r = first;
+      float acc = load_elem<DT>(bufs.p[r], e + i);
+      for (int k = 1; k < N; ++k) {
+        r = r + 1 == N ? 0 : r + 1;
+        acc = round_to<DT>(load_elem<DT>(bufs.p[r], e + i) + acc);
+      }
+      if constexpr (STORE_ALL) {
+        for (int d = 0; d < N; ++d) store_elem<DT>(bufs.p[d], e + i, acc);
+      } else {
+        store_elem<DT>(bufs.p[c], e + i, acc);
+      }
     }
   }
 }
 
-template <int DT, int G>
+template <int DT, int V>
 __global__ __launch_bounds__(kThreads) void rs_step_kernel(RankPtrs bufs, int N, uint64_t count,
-                                                            uint64_t L, int s,
-                                                            uint32_t tiles_per_chunk) {
-  const int r = (int)(blockIdx.x / tiles_per_chunk);
-  const uint32_t t = blockIdx.x - (uint32_t)r * tiles_per_chunk;
+                                                            uint64_t L, int s) {
+  constexpr int E = Vec<DT>::E;
+  constexpr int ES = DtypeSize<DT>::value;
+  uint32_t r_, t;
+  chunk_tile(N, &r_, &t);
+  const int r = (int)r_;
   const int c = ((r - s - 1) % N + N) % N;
   const int src = r == 0 ? N - 1 : r - 1;
   const uint64_t lo = (uint64_t)c * L;
   if (lo >= count) return;
   const uint64_t hi = lo + L < count ? lo + L : count;
-  constexpr uint64_t kTile = (uint64_t)kThreads * kGroupElems * G;
+  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
   const uint64_t tile0 = lo + (uint64_t)t * kTile;
   if (tile0 >= hi) return;
-  const uint64_t e0 = tile0 + (uint64_t)threadIdx.x * kGroupElems;
+  auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
   if (tile0 + kTile <= hi) {
-    Raw8<DT> mine[G], theirs[G];
+    u32x4 mine[V], theirs[V];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
-      mine[g] = load_raw8<DT, false>(bufs.p[r], e);
-      theirs[g] = load_raw8<DT, true>(bufs.p[src], e);
+    for (int v = 0; v < V; ++v) {
+      mine[v] = ld16<false>(bufs.p[r] + elem(v) * ES);
+      theirs[v] = ld16<true>(bufs.p[src] + elem(v) * ES);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      G8 a = unpack8<DT>(mine[g]), b = unpack8<DT>(theirs[g]);
+    for (int v = 0; v < V; ++v) {
+      Vec<DT> a = unpack16<DT>(mine[v]);
+      const Vec<DT> b = unpack16<DT>(theirs[v]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a.v[i] = round_to<DT>(a.v[i] + b.v[i]);
-      store_raw8<DT, false>(bufs.p[r], e0 + (uint64_t)g * kThreads * kGroupElems, pack8<DT>(a));
+      for (int i = 0; i < E; ++i) a.v[i] = round_to<DT>(a.v[i] + b.v[i]);
+      st16<false>(bufs.p[r] + elem(v) * ES, pack16<DT>(a));
     }
     return;
   }
-  for (int g = 0; g < G; ++g) {
-    const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
-    if (e >= hi) break;
-    const int nv = hi - e >= 8 ? 8 : (int)(hi - e);
-    G8 a = load_part8<DT>(bufs.p[r], e, nv), b = load_part8<DT>(bufs.p[src], e, nv);
-    for (int i = 0; i < 8; ++i) a.v[i] = round_to<DT>(a.v[i] + b.v[i]);
-    store_part8<DT>(bufs.p[r], e, nv, a);
+  for (int v = 0; v < V; ++v) {
+    const uint64_t e = elem(v);
+    for (int i = 0; i < E && e + i < hi; ++i)
+      store_elem<DT>(bufs.p[r], e + i, round_to<DT>(load_elem<DT>(bufs.p[r], e + i) + load_elem<DT>(bufs.p[src], e + i)));
   }
 }
 
@@ -179,61 +219,79 @@ __global__ __launch_bounds__(kThreads) void copy_jobs_kernel(CopyJobs jobs, uint
 
 template <int DT, int NR>
 hipError_t fold_dispatch_store(const RankPtrs& bufs, int n, uint64_t count, uint64_t L,
-                               bool store_all, uint32_t tiles, hipStream_t stream) {
+                               bool store_all, hipStream_t stream) {
+  constexpr int V = FoldVecs<DT>::value;
+  const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * V;
+  const uint64_t tiles = (L + tile - 1) / tile;
   dim3 grid((unsigned)((uint64_t)n * tiles)), block(kThreads);
+  const size_t lds = residency_lds(fold_wgs_per_cu(DT, n));
   if (store_all)
-    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, kFoldGroups, true>), grid, block, 0, stream, bufs, n,
-                       count, L, tiles);
+    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, true>), grid, block, lds, stream, bufs, n, count, L);
   else
-    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, kFoldGroups, false>), grid, block, 0, stream, bufs, n,
-                       count, L, tiles);
+    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, false>), grid, block, lds, stream, bufs, n, count, L);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t fold_dispatch_n(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, bool store_all,
-                           uint32_t tiles, hipStream_t stream) {
+                           hipStream_t stream) {
   switch (n) {
-    case 2: return fold_dispatch_store<DT, 2>(bufs, n, count, L, store_all, tiles, stream);
-    case 4: return fold_dispatch_store<DT, 4>(bufs, n, count, L, store_all, tiles, stream);
-    case 8: return fold_dispatch_store<DT, 8>(bufs, n, count, L, store_all, tiles, stream);
-    case 16: return fold_dispatch_store<DT, 16>(bufs, n, count, L, store_all, tiles, stream);
-    default: return fold_dispatch_store<DT, 0>(bufs, n, count, L, store_all, tiles, stream);
+    case 2: return fold_dispatch_store<DT, 2>(bufs, n, count, L, store_all, stream);
+    case 4: return fold_dispatch_store<DT, 4>(bufs, n, count, L, store_all, stream);
+    case 8: return fold_dispatch_store<DT, 8>(bufs, n, count, L, store_all, stream);
+    case 16: return fold_dispatch_store<DT, 16>(bufs, n, count, L, store_all, stream);
+    default: return fold_dispatch_store<DT, 0>(bufs, n, count, L, store_all, stream);
   }
+}
+
+template <int DT>
+hipError_t step_dispatch(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int s, hipStream_t stream) {
+  const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * kStepVecs;
+  const uint64_t tiles = (L + tile - 1) / tile;
+  dim3 grid((unsigned)((uint64_t)n * tiles)), block(kThreads);
+  hipLaunchKernelGGL((rs_step_kernel<DT, kStepVecs>), grid, block, 0, stream, bufs, n, count, L, s);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+size_t residency_lds(int wgs_per_cu) {
+  if (wgs_per_cu <= 0) return 0;
+  static std::atomic<uint64_t> cache[kMaxRanks];  // per device: LDS per CU << 32 | LDS per workgroup
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxRanks) return 0;
+  uint64_t c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int a = 0, b = 0;
+    if (hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || a <= 0 || b <= 0)
+      return 0;
+    c = (uint64_t)a << 32 | (uint64_t)b;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  const size_t per_cu = (size_t)(c >> 32), per_wg = (size_t)(c & 0xffffffffu);
+  const size_t want = per_cu / (size_t)(wgs_per_cu + 1) + 1024;
+  return want <= per_wg ? want : 0;
+}
+
 hipError_t launch_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
                             bool store_all, hipStream_t stream) {
-  const uint64_t tile = (uint64_t)kThreads * kGroupElems * kFoldGroups;
-  const uint32_t tiles = (uint32_t)((L + tile - 1) / tile);
-  if (tiles == 0) return hipSuccess;
+  if (L == 0 || count == 0) return hipSuccess;
   switch (dt) {
-    case DT_F32: return fold_dispatch_n<DT_F32>(bufs, n, count, L, store_all, tiles, stream);
-    case DT_F16: return fold_dispatch_n<DT_F16>(bufs, n, count, L, store_all, tiles, stream);
-    default: return fold_dispatch_n<DT_BF16>(bufs, n, count, L, store_all, tiles, stream);
+    case DT_F32: return fold_dispatch_n<DT_F32>(bufs, n, count, L, store_all, stream);
+    case DT_F16: return fold_dispatch_n<DT_F16>(bufs, n, count, L, store_all, stream);
+    default: return fold_dispatch_n<DT_BF16>(bufs, n, count, L, store_all, stream);
   }
 }
 
 hipError_t launch_rs_step(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt, int s,
                           hipStream_t stream) {
-  const uint64_t tile = (uint64_t)kThreads * kGroupElems * kStepGroups;
-  const uint32_t tiles = (uint32_t)((L + tile - 1) / tile);
-  if (tiles == 0) return hipSuccess;
-  dim3 grid((unsigned)((uint64_t)n * tiles)), block(kThreads);
+  if (L == 0 || count == 0) return hipSuccess;
   switch (dt) {
-    case DT_F32:
-      hipLaunchKernelGGL((rs_step_kernel<DT_F32, kStepGroups>), grid, block, 0, stream, bufs, n, count, L, s, tiles);
-      break;
-    case DT_F16:
-      hipLaunchKernelGGL((rs_step_kernel<DT_F16, kStepGroups>), grid, block, 0, stream, bufs, n, count, L, s, tiles);
-      break;
-    default:
-      hipLaunchKernelGGL((rs_step_kernel<DT_BF16, kStepGroups>), grid, block, 0, stream, bufs, n, count, L, s, tiles);
-      break;
+    case DT_F32: return step_dispatch<DT_F32>(bufs, n, count, L, s, stream);
+    case DT_F16: return step_dispatch<DT_F16>(bufs, n, count, L, s, stream);
+    default: return step_dispatch<DT_BF16>(bufs, n, count, L, s, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_copy_jobs(const CopyJobs& jobs, hipStream_t stream) {
