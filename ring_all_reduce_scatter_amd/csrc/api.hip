@@ -223,9 +223,14 @@ void plan_sizes(CompPlan* pl, int n, size_t count, int dt) {
   pl->slot = round_up(slot, kAlign);
 }
 
+size_t slots_offset() { return round_up(kTrafficBytes, kAlign); }
+size_t tiles_offset(const CompPlan& pl) { return slots_offset() + (size_t)pl.n * pl.upc * pl.slot; }
+size_t tiles_per_slot(const CompPlan& pl) { return 2 * (size_t)comp_tiles_per_unit(pl.U); }
+
 size_t workspace_need(const CompPlan& pl) {
   if (pl.method == RAR_COMP_NONE || pl.sched == RAR_SCHED_FUSED) return kTrafficBytes;
-  size_t need = round_up(kTrafficBytes, kAlign) + (size_t)pl.n * pl.upc * pl.slot;
+  size_t need = tiles_offset(pl);
+  if (pl.method == RAR_COMP_SPARSE_AUTO) need += (size_t)pl.n * pl.upc * tiles_per_slot(pl) * sizeof(uint32_t);
   return need;
 }
 
@@ -245,7 +250,7 @@ int staged_bfp(const CompPlan& pl, void* const* bufs, char* ws, Traffic& tr, hip
   int rc = get_ctx(&ctx);
   if (rc) return rc;
   const int n = pl.n;
-  char* slots = ws + round_up(kTrafficBytes, kAlign);
+  char* slots = ws + slots_offset();
   auto slot = [&](int rank, size_t u) { return (uint8_t*)(slots + ((size_t)rank * pl.upc + u) * pl.slot); };
   hipStream_t E = st, D = ctx->side;
   if (hipEventRecord(ctx->fork, E) != hipSuccess || hipStreamWaitEvent(D, ctx->fork, 0) != hipSuccess)
@@ -309,6 +314,97 @@ int staged_bfp(const CompPlan& pl, void* const* bufs, char* ws, Traffic& tr, hip
     if ((rc = hip_rc(launch_bfp_encode(enc, pl.dt, pl.block, pl.mbits, E)))) return rc;
     if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
     if ((rc = hip_rc(launch_bfp_decode_fanout(enc, fan, n, off, pl.dt, pl.block, pl.mbits, D)))) return rc;
+    if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;
+  }
+  if (hipEventRecord(ctx->join, D) != hipSuccess || hipStreamWaitEvent(E, ctx->join, 0) != hipSuccess)
+    return RAR_EHIP;
+  return RAR_OK;
+}
+
+// Staged SPARSE_AUTO ring: each unit message is sparse or BFP by the
+// threshold rule; sizes (and so the byte counters) are decided on the device.
+int staged_sparse(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t st) {
+  DevCtx* ctx = nullptr;
+  std::lock_guard<std::mutex> lock(g_ctx_mu);
+  int rc = get_ctx(&ctx);
+  if (rc) return rc;
+  const int n = pl.n;
+  char* slots = ws + slots_offset();
+  uint32_t* tiles = (uint32_t*)(ws + tiles_offset(pl));
+  const size_t tps = tiles_per_slot(pl);
+  auto slot = [&](int rank, size_t u) { return (uint8_t*)(slots + ((size_t)rank * pl.upc + u) * pl.slot); };
+  auto scratch = [&](int rank, size_t u) { return tiles + ((size_t)rank * pl.upc + u) * tps; };
+  uint64_t* traffic = (uint64_t*)ws;
+  hipStream_t E = st, D = ctx->side;
+  const uint64_t zeros[2 * RAR_MAX_RANKS] = {};
+  if ((rc = hip_rc(launch_fill_u64(traffic, zeros, 2 * RAR_MAX_RANKS, E)))) return rc;
+  if (hipEventRecord(ctx->fork, E) != hipSuccess || hipStreamWaitEvent(D, ctx->fork, 0) != hipSuccess)
+    return RAR_EHIP;
+  for (int s = 1; s <= n - 1; ++s) {
+    for (size_t u = 0; u < pl.upc; ++u) {
+      CompJobs enc{};
+      BfpJobs dec{};
+      int j = 0;
+      for (int r = 0; r < n; ++r) {
+        const int src = modn(r - 1, n), c = modn(r - s - 1, n);
+        size_t lo, hi;
+        chunk_range(pl.count, pl.L, c, &lo, &hi);
+        const size_t ulo = lo + u * pl.U;
+        if (ulo >= hi) continue;
+        const size_t len = std::min(pl.U, hi - ulo);
+        enc.src[j] = (const char*)bufs[src] + ulo * pl.es;
+        enc.msg[j] = slot(src, u);
+        enc.tiles[j] = scratch(src, u);
+        enc.len[j] = len;
+        enc.from[j] = (int8_t)src;
+        enc.hops[j] = 1;
+        dec.dst[j] = (char*)bufs[r] + ulo * pl.es;
+        dec.msg[j] = slot(src, u);
+        dec.len[j] = len;
+        ++j;
+      }
+      if (!j) continue;
+      enc.njobs = dec.njobs = j;
+      enc.nranks = n;
+      hipEvent_t eE = ctx->evE[u % kMaxEvents], eD = ctx->evD[u % kMaxEvents];
+      if (s > 1 && hipStreamWaitEvent(E, eD, 0) != hipSuccess) return RAR_EHIP;
+      if ((rc = hip_rc(launch_comp_encode(enc, pl.dt, pl.block, pl.mbits, pl.theta, traffic, E)))) return rc;
+      if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
+      if ((rc = hip_rc(launch_comp_decode_acc(dec, pl.dt, pl.block, pl.mbits, D)))) return rc;
+      if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;
+    }
+  }
+  RankPtrs fan = make_ptrs(bufs, n);
+  for (size_t u = 0; u < pl.upc; ++u) {
+    CompJobs enc{};
+    BfpJobs dec{};
+    uint64_t off[kMaxRanks] = {};
+    int j = 0;
+    for (int c = 0; c < n; ++c) {
+      size_t lo, hi;
+      chunk_range(pl.count, pl.L, c, &lo, &hi);
+      const size_t ulo = lo + u * pl.U;
+      if (ulo >= hi) continue;
+      const size_t len = std::min(pl.U, hi - ulo);
+      enc.src[j] = (const char*)bufs[c] + ulo * pl.es;
+      enc.msg[j] = slot(c, u);
+      enc.tiles[j] = scratch(c, u);
+      enc.len[j] = len;
+      enc.from[j] = (int8_t)c;
+      enc.hops[j] = (int8_t)(n - 1);
+      dec.msg[j] = slot(c, u);
+      dec.len[j] = len;
+      off[j] = ulo;
+      ++j;
+    }
+    if (!j) continue;
+    enc.njobs = dec.njobs = j;
+    enc.nranks = n;
+    hipEvent_t eE = ctx->evE[u % kMaxEvents], eD = ctx->evD[u % kMaxEvents];
+    if (hipStreamWaitEvent(E, eD, 0) != hipSuccess) return RAR_EHIP;
+    if ((rc = hip_rc(launch_comp_encode(enc, pl.dt, pl.block, pl.mbits, pl.theta, traffic, E)))) return rc;
+    if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
+    if ((rc = hip_rc(launch_comp_decode_fanout(dec, fan, n, off, pl.dt, pl.block, pl.mbits, D)))) return rc;
     if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;
   }
   if (hipEventRecord(ctx->join, D) != hipSuccess || hipStreamWaitEvent(E, ctx->join, 0) != hipSuccess)
@@ -573,7 +669,10 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
     if ((rc = allreduce_impl(bufs, nranks, count, dtype, RAR_ALGO_FUSED, true, st))) return rc;
     return write_traffic(g_last, workspace, st);
   }
-  if (pl.method == RAR_COMP_SPARSE_AUTO) return RAR_ENOTSUP;
+  if (pl.method == RAR_COMP_SPARSE_AUTO) {
+    if (nranks == 1 || count == 0) return write_traffic(tr, workspace, st);
+    return staged_sparse(pl, bufs, (char*)workspace, st);
+  }
   if (nranks > 1 && count > 0) {
     if (pl.sched == RAR_SCHED_FUSED) {
       fused_bfp_traffic(pl, tr);

@@ -71,6 +71,32 @@ hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs, const RankPtrs& fan, in
 hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
                                 int block, int mbits, hipStream_t stream);
 
+// -------------------------------------------------------------- sparse-or-BFP (sparse_kernels.hip)
+
+// Messages of the SPARSE_AUTO compressed ring (one per pipeline unit).
+struct CompJobs {
+  const char* src[kMaxRanks];  // unit data to encode
+  uint8_t* msg[kMaxRanks];     // message: 16-byte header + payload
+  uint32_t* tiles[kMaxRanks];  // scratch: per-tile non-zero counts, then offsets
+  uint64_t len[kMaxRanks];     // elements in the unit
+  int8_t from[kMaxRanks];      // first sender charged in the byte counters
+  int8_t hops[kMaxRanks];      // links the message crosses (1, or N-1 in the allgather)
+  int njobs;
+  int nranks;
+};
+
+// Tiles (2048 elements) per unit: the scratch needs 2 * this many uint32.
+uint64_t comp_tiles_per_unit(uint64_t unit_elems);
+// count -> plan (threshold, header, byte counters) -> write; traffic points
+// at u64 sent[kMaxRanks] followed by recv[kMaxRanks] in device memory.
+hipError_t launch_comp_encode(const CompJobs& jobs, int dt, int block, int mbits, float theta, uint64_t* traffic,
+                              hipStream_t stream);
+// dst <- dst (+) decoded message (job dst / msg / len).
+hipError_t launch_comp_decode_acc(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
+// Store each decoded message to elem_off[j] of every rank in `fan`.
+hipError_t launch_comp_decode_fanout(const BfpJobs& jobs, const RankPtrs& fan, int nfan, const uint64_t* elem_off,
+                                     int dt, int block, int mbits, hipStream_t stream);
+
 // -------------------------------------------------------------- buckets (bucket_kernels.hip)
 
 // Segment copies: dst[0, bytes) <- src[0, bytes), then dst[bytes, zero_to) <- 0.

@@ -1,0 +1,325 @@
+// Sparse-or-BFP messages of the compressed ring for gfx950 (page "CCCL通信压缩库
+// ：突破LLM训练通信墙的工程实践", section 2.1: when a tensor's sparsity exceeds a
+// threshold (e.g. 50%) only the non-zero values and their indices are sent
+// and the receiver puts them back in place, losslessly; denser data goes as
+// block floating point).
+//
+// A message describes one pipeline unit (`len` elements) and starts with a
+// 16-byte header {nnz, kind, len, 0}:
+//   kind 1 (sparse): values[nnz] in the element type, zero padding to 16
+//                    bytes, then uint32 idx[nnz], ascending, unit-relative;
+//   kind 0 (BFP):    nnz = 0, then the BFP layout of the whole unit.
+// A unit is sparse iff zeros > threshold * len (zeros are +0 and -0).
+//
+// Encoding takes three launches over 2048-element tiles (256 lanes x 8):
+//   count  - non-zeros per tile;
+//   plan   - one workgroup per message: exclusive scan of the tile counts,
+//            the threshold decision, the header, and the wire byte counters;
+//   write  - sparse: each tile compacts its non-zeros to the scanned offsets
+//            (ballot-free: a block-wide exclusive scan of per-lane counts
+//            keeps the indices ascending); BFP: the tile's blocks.
+// Decoding works per destination tile: a binary search finds the tile's
+// slice of the ascending index array, so no two workgroups touch the same
+// element and no atomics are needed.
+#include "bfp_device.hpp"
+
+namespace rar {
+
+namespace {
+
+constexpr uint64_t kTileElems = (uint64_t)kThreads * kGroupElems;  // 2048
+
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total) {
+  __shared__ uint32_t wsum[kThreads / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kThreads / 64; ++k) {
+    if (k < w) base += wsum[k];
+    tot += wsum[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+__device__ __forceinline__ uint64_t round16(uint64_t x) { return (x + 15) / 16 * 16; }
+
+template <int DT>
+__device__ __forceinline__ int nonzeros(const G8& x, int nv) {
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c += (i < nv && x.v[i] != 0.0f) ? 1 : 0;
+  return c;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void comp_count_kernel(CompJobs jobs, uint32_t tiles_max) {
+  const int j = (int)(blockIdx.x / tiles_max);
+  const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
+  const uint64_t len = jobs.len[j];
+  if ((uint64_t)t * kTileElems >= len) return;
+  const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
+  const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
+  const G8 x = load_group<DT>(jobs.src[j], elem, nv);
+  uint32_t total;
+  block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
+  if (threadIdx.x == 0) jobs.tiles[j][t] = total;
+}
+
+__global__ __launch_bounds__(kThreads) void comp_plan_kernel(CompJobs jobs, float theta, uint64_t* traffic,
+                                                              int block, int mbits, int es) {
+  const int j = blockIdx.x;
+  const uint64_t len = jobs.len[j];
+  const uint32_t T = (uint32_t)((len + kTileElems - 1) / kTileElems);
+  uint32_t* nnzs = jobs.tiles[j];
+  uint32_t* offs = jobs.tiles[j] + T;
+  const uint32_t per = (T + kThreads - 1) / kThreads;
+  const uint32_t lo = threadIdx.x * per < T ? threadIdx.x * per : T;
+  const uint32_t hi = lo + per < T ? lo + per : T;
+  uint32_t local = 0;
+  for (uint32_t t = lo; t < hi; ++t) local += nnzs[t];
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(local, &total);
+  for (uint32_t t = lo; t < hi; ++t) {
+    offs[t] = run;
+    run += nnzs[t];
+  }
+  if (threadIdx.x == 0) {
+    const uint64_t nnz = total;
+    const bool sparse = (double)(len - nnz) > (double)theta * (double)len;
+    uint32_t* hdr = (uint32_t*)jobs.msg[j];
+    hdr[0] = sparse ? (uint32_t)nnz : 0u;
+    hdr[1] = sparse ? 1u : 0u;
+    hdr[2] = (uint32_t)len;
+    hdr[3] = 0u;
+    const uint64_t bytes = sparse ? 16 + round16(nnz * (uint64_t)es) + 4 * nnz
+                                  : 16 + bfp_msg_bytes(len, block, mbits);
+    const int n = jobs.nranks;
+    for (int h = 0; h < jobs.hops[j]; ++h) {
+      atomicAdd((unsigned long long*)&traffic[(jobs.from[j] + h) % n], (unsigned long long)bytes);
+      atomicAdd((unsigned long long*)&traffic[kMaxRanks + (jobs.from[j] + h + 1) % n], (unsigned long long)bytes);
+    }
+  }
+}
+
+template <int DT, int LPB>
+__global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uint32_t tiles_max, int lpb_rt,
+                                                               int mbits) {
+  constexpr int ES = DtypeSize<DT>::value;
+  const int j = (int)(blockIdx.x / tiles_max);
+  const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
+  const uint64_t len = jobs.len[j];
+  if ((uint64_t)t * kTileElems >= len) return;
+  const uint32_t T = (uint32_t)((len + kTileElems - 1) / kTileElems);
+  const char* src = jobs.src[j];
+  uint8_t* msg = jobs.msg[j];
+  const uint32_t kind = ((const uint32_t*)msg)[1];
+  const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
+  const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
+  const G8 x = load_group<DT>(src, elem, nv);
+  if (kind == 1u) {
+    const uint64_t nnz = ((const uint32_t*)msg)[0];
+    uint8_t* vals = msg + 16;
+    uint32_t* idx = (uint32_t*)(msg + 16 + round16(nnz * ES));
+    uint32_t total;
+    uint64_t pos = jobs.tiles[j][T + t] + block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
+    for (int i = 0; i < nv; ++i) {
+      if (x.v[i] == 0.0f) continue;
+      if constexpr (ES == 4) ((uint32_t*)vals)[pos] = ((const uint32_t*)src)[elem + i];
+      else ((uint16_t*)vals)[pos] = ((const uint16_t*)src)[elem + i];
+      idx[pos] = (uint32_t)(elem + i);
+      ++pos;
+    }
+    if (t == 0 && threadIdx.x < 16) {
+      // zero padding between the values and the indices
+      const uint64_t pad0 = 16 + nnz * ES, pad1 = 16 + round16(nnz * ES);
+      if (pad0 + threadIdx.x < pad1) msg[pad0 + threadIdx.x] = 0;
+    }
+  } else {
+    const int lpb = LPB > 0 ? LPB : lpb_rt;
+    const uint64_t block = (uint64_t)lpb * 8;
+    uint8_t* payload = msg + 16;
+    const uint64_t nb = (len + block - 1) / block;
+    const uint64_t eb = (nb + 15) / 16 * 16;
+    if (t == 0 && threadIdx.x < eb - nb) payload[nb + threadIdx.x] = 0;
+    encode_group<DT, LPB>(x, nv, elem, payload, payload + eb, lpb, mbits, (float)((1 << (mbits - 1)) - 1));
+  }
+}
+
+// First position in idx[0, n) whose value is >= key.
+__device__ __forceinline__ uint64_t lower_bound_u32(const uint32_t* idx, uint64_t n, uint64_t key) {
+  uint64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const uint64_t mid = (lo + hi) / 2;
+    if ((uint64_t)idx[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Decode one tile of one message into `nfan` destinations (rank buffers at
+// elem_off, or the single job destination).  ACC: dst <- dst (+) value;
+// otherwise dst <- value (sparse: the tile is zeroed first).
+template <int DT, bool ACC>
+__device__ __forceinline__ void comp_decode_tile(const uint8_t* msg, uint64_t len, uint32_t t, char* const* dsts,
+                                                 int nfan, uint64_t elem_off, int block, int mbits) {
+  constexpr int ES = DtypeSize<DT>::value;
+  __shared__ uint64_t range[2];
+  const uint32_t* hdr = (const uint32_t*)msg;
+  const uint64_t tlo = (uint64_t)t * kTileElems;
+  const uint64_t thi = tlo + kTileElems < len ? tlo + kTileElems : len;
+  if (hdr[1] == 0u) {
+    const uint8_t* payload = msg + 16;
+    const uint64_t elem = tlo + (uint64_t)threadIdx.x * 8;
+    if (elem >= thi) return;
+    const int nv = thi - elem >= 8 ? 8 : (int)(thi - elem);
+    G8 d = dequant_group(payload, bfp_exp_bytes(len, block), elem, nv, (uint64_t)block, mbits);
+    for (int f = 0; f < nfan; ++f) {
+      G8 out = d;
+      if constexpr (ACC) {
+        const G8 a = load_group<DT>(dsts[f], elem_off + elem, nv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out.v[i] = round_to<DT>(a.v[i] + d.v[i]);
+      }
+      store_group<DT>(dsts[f], elem_off + elem, nv, out);
+    }
+    return;
+  }
+  const uint64_t nnz = hdr[0];
+  const uint8_t* vals = msg + 16;
+  const uint32_t* idx = (const uint32_t*)(msg + 16 + round16(nnz * ES));
+  if (threadIdx.x == 0) {
+    range[0] = lower_bound_u32(idx, nnz, tlo);
+    range[1] = lower_bound_u32(idx, nnz, thi);
+  }
+  if constexpr (!ACC) {
+    const uint64_t elem = tlo + (uint64_t)threadIdx.x * 8;
+    if (elem < thi) {
+      const int nv = thi - elem >= 8 ? 8 : (int)(thi - elem);
+      G8 z;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z.v[i] = 0.0f;
+      for (int f = 0; f < nfan; ++f) store_group<DT>(dsts[f], elem_off + elem, nv, z);
+    }
+  }
+  __syncthreads();
+  const uint64_t j0 = range[0], j1 = range[1];
+  for (uint64_t q = j0 + threadIdx.x; q < j1; q += kThreads) {
+    const uint64_t i = elem_off + idx[q];
+    if constexpr (ES == 4) {
+      const uint32_t raw = ((const uint32_t*)vals)[q];
+      for (int f = 0; f < nfan; ++f) {
+        float* p = (float*)dsts[f] + i;
+        *p = ACC ? *p + __uint_as_float(raw) : __uint_as_float(raw);
+      }
+    } else {
+      const uint16_t raw = ((const uint16_t*)vals)[q];
+      for (int f = 0; f < nfan; ++f) {
+        uint16_t* p = (uint16_t*)dsts[f] + i;
+        *p = ACC ? (uint16_t)narrow16<DT>(widen16<DT>(*p) + widen16<DT>(raw)) : raw;
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void comp_decode_acc_kernel(BfpJobs jobs, uint32_t tiles_max, int block,
+                                                                    int mbits) {
+  const int j = (int)(blockIdx.x / tiles_max);
+  const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
+  const uint64_t len = jobs.len[j];
+  if ((uint64_t)t * kTileElems >= len) return;
+  char* dst = jobs.dst[j];
+  comp_decode_tile<DT, true>(jobs.msg[j], len, t, &dst, 1, 0, block, mbits);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void comp_decode_fanout_kernel(BfpJobs jobs, RankPtrs fan, int nfan,
+                                                                       uint32_t tiles_max, int block, int mbits) {
+  const int j = (int)(blockIdx.x / tiles_max);
+  const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
+  const uint64_t len = jobs.len[j];
+  if ((uint64_t)t * kTileElems >= len) return;
+  comp_decode_tile<DT, false>(jobs.msg[j], len, t, fan.p, nfan, (uint64_t)(uintptr_t)jobs.dst[j], block, mbits);
+}
+
+uint32_t tiles_of(uint64_t len) { return (uint32_t)((len + kTileElems - 1) / kTileElems); }
+
+template <int DT>
+hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, uint64_t* traffic,
+                     hipStream_t stream) {
+  uint64_t ml = 0;
+  for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
+  const uint32_t tm = tiles_of(ml);
+  if (jobs.njobs == 0 || tm == 0) return hipSuccess;
+  dim3 grid((unsigned)(jobs.njobs * tm)), blk(kThreads);
+  hipLaunchKernelGGL((comp_count_kernel<DT>), grid, blk, 0, stream, jobs, tm);
+  hipLaunchKernelGGL(comp_plan_kernel, dim3((unsigned)jobs.njobs), blk, 0, stream, jobs, theta, traffic, block,
+                     mbits, (int)DtypeSize<DT>::value);
+  if (block == 128)
+    hipLaunchKernelGGL((comp_write_kernel<DT, 16>), grid, blk, 0, stream, jobs, tm, 16, mbits);
+  else
+    hipLaunchKernelGGL((comp_write_kernel<DT, 0>), grid, blk, 0, stream, jobs, tm, block / 8, mbits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+uint64_t comp_tiles_per_unit(uint64_t unit_elems) { return tiles_of(unit_elems); }
+
+hipError_t launch_comp_encode(const CompJobs& jobs, int dt, int block, int mbits, float theta, uint64_t* traffic,
+                              hipStream_t stream) {
+  switch (dt) {
+    case DT_F32: return encode_dt<DT_F32>(jobs, block, mbits, theta, traffic, stream);
+    case DT_F16: return encode_dt<DT_F16>(jobs, block, mbits, theta, traffic, stream);
+    default: return encode_dt<DT_BF16>(jobs, block, mbits, theta, traffic, stream);
+  }
+}
+
+hipError_t launch_comp_decode_acc(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
+  uint64_t ml = 0;
+  for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
+  const uint32_t tm = tiles_of(ml);
+  if (jobs.njobs == 0 || tm == 0) return hipSuccess;
+  dim3 grid((unsigned)(jobs.njobs * tm)), blk(kThreads);
+  switch (dt) {
+    case DT_F32: hipLaunchKernelGGL((comp_decode_acc_kernel<DT_F32>), grid, blk, 0, stream, jobs, tm, block, mbits); break;
+    case DT_F16: hipLaunchKernelGGL((comp_decode_acc_kernel<DT_F16>), grid, blk, 0, stream, jobs, tm, block, mbits); break;
+    default: hipLaunchKernelGGL((comp_decode_acc_kernel<DT_BF16>), grid, blk, 0, stream, jobs, tm, block, mbits); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_comp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan, int nfan,
+                                     const uint64_t* elem_off, int dt, int block, int mbits, hipStream_t stream) {
+  BfpJobs jobs = jobs_in;
+  for (int j = 0; j < jobs.njobs; ++j) jobs.dst[j] = (char*)(uintptr_t)elem_off[j];
+  uint64_t ml = 0;
+  for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
+  const uint32_t tm = tiles_of(ml);
+  if (jobs.njobs == 0 || tm == 0) return hipSuccess;
+  dim3 grid((unsigned)(jobs.njobs * tm)), blk(kThreads);
+  switch (dt) {
+    case DT_F32:
+      hipLaunchKernelGGL((comp_decode_fanout_kernel<DT_F32>), grid, blk, 0, stream, jobs, fan, nfan, tm, block, mbits);
+      break;
+    case DT_F16:
+      hipLaunchKernelGGL((comp_decode_fanout_kernel<DT_F16>), grid, blk, 0, stream, jobs, fan, nfan, tm, block, mbits);
+      break;
+    default:
+      hipLaunchKernelGGL((comp_decode_fanout_kernel<DT_BF16>), grid, blk, 0, stream, jobs, fan, nfan, tm, block, mbits);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rar
