@@ -133,7 +133,8 @@ def fp32_leg(args):
     torch.cuda.empty_cache()
     alg_bytes = 2 * n * S  # every rank's input read once and output written once
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    sources = ["ring_all_reduce_scatter_amd/csrc/ring_kernels.hip", "ring_all_reduce_scatter_amd/csrc/common.hpp"]
+    sources = ["ring_all_reduce_scatter_amd/csrc/ring_kernels.hip", "ring_all_reduce_scatter_amd/csrc/common.hpp",
+               "ring_all_reduce_scatter_amd/csrc/launch.hpp"]
     res = {
         "n": n, "count": count, "S": S, "ms": ms, "kern_ms": kern_ms, "kern_min_ms": kern_min,
         "busbw": busbw(S, n, ms),
@@ -221,7 +222,8 @@ def bfp8_leg(args):
     torch.cuda.empty_cache()
     alg_bytes = 2 * n * S
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    sources = ["ring_all_reduce_scatter_amd/csrc/bfp_kernels.hip", "ring_all_reduce_scatter_amd/csrc/common.hpp"]
+    sources = ["ring_all_reduce_scatter_amd/csrc/bfp_kernels.hip", "ring_all_reduce_scatter_amd/csrc/bfp_device.hpp",
+               "ring_all_reduce_scatter_amd/csrc/common.hpp", "ring_all_reduce_scatter_amd/csrc/launch.hpp"]
     res = {
         "metric": "BFP-8 compressed all-reduce effective bus GB/s (2T(N-1)/N fp16 bytes per rank)",
         "value": round(busbw(S, n, ms), 2), "unit": "GB/s", "ms_per_step": round(ms, 4),
@@ -283,6 +285,7 @@ def sampled_bfp_parity(xs, got0, L, mbits, per_chunk=64):
 
 def extra_legs(args):
     """Secondary schedules and collectives (reported, not the headline)."""
+    import numpy as np
     import torch
 
     import ring_all_reduce_scatter_amd as rar
@@ -319,6 +322,38 @@ def extra_legs(args):
     del sets, pristine, ws
     torch.cuda.empty_cache()
     w5 = inputs.WORKLOADS["sparse_bfp4"]
+    xsp = inputs.sparse_mix(w5["n"], w5["count"])
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xsp]
+    del xsp
+    sets = make_sets(pristine, 1 + steps)
+    cfg = rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=w5["mbits"], unit_bytes=w5["unit_bytes"],
+                           sparsity_threshold=w5["theta"], schedule=rar.SCHED_STAGED)
+    ws = torch.empty(rar.compressed_workspace_bytes(w5["n"], w5["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    ms, k, _ = time_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, 2, steps)
+    S5 = w5["count"] * 2
+    sent, _ = rar.compressed_traffic(ws, w5["n"])
+    out["sparse_bfp4_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S5, w5["n"], ms), 1),
+                                           "wire_bytes_rank0": sent[0],
+                                           "frac_of_roofline": round(2 * w5["n"] * S5 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, pristine, ws
+    torch.cuda.empty_cache()
+    wk = inputs.WORKLOADS["buckets"]
+    sizes = inputs.bucket_sizes(wk["ntensors"])
+    th = inputs.bucket_tensors(wk["n"], sizes)
+    dev = [[torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to("cuda:0") for t in th[r]]
+           for r in range(wk["n"])]
+    del th
+    ws = torch.empty(rar.bucketed_workspace_bytes(sizes, wk["n"], rar.BF16, wk["cap_bytes"]), dtype=torch.uint8,
+                     device="cuda:0")
+    ms, k, _ = time_leg(lambda d: rar.bucketed_allreduce(d, wk["cap_bytes"], ws), [dev, dev], 1, min(steps, 3))
+    S3 = sum(sizes) * 2
+    nb, _ = rar.bucket_plan(sizes, rar.BF16, wk["cap_bytes"])
+    out["buckets_bf16_allreduce"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S3, wk["n"], ms), 1),
+                                     "buckets": nb, "elements_per_rank": sum(sizes),
+                                     "frac_of_roofline_fold_only_bytes": round(2 * wk["n"] * S3 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dev, ws
+    torch.cuda.empty_cache()
     for name, fn, cnt in (("fp32_broadcast_fused", lambda b: rar.broadcast(b, 0), w5["bcast_count"]),
                           ("fp32_allgather_fused", lambda b: rar.allgather(b), w5["ag_shard"] * 8)):
         xf = inputs.filler(8, cnt)
@@ -335,6 +370,35 @@ def extra_legs(args):
     return out
 
 
+def counters_run(reps=3):
+    """Short launch sequence for hardware-counter passes: a plain copy of known
+    size (broadcast over 2 ranks of 256 MiB fp32: 256 MiB read, 256 MiB written)
+    to calibrate FETCH_SIZE / WRITE_SIZE, then the two timed kernels."""
+    import torch
+
+    import ring_all_reduce_scatter_amd as rar
+    from ring_all_reduce_scatter_amd import inputs
+
+    cal = [torch.full((64 << 20,), float(r + 1), device="cuda:0") for r in range(2)]
+    for _ in range(reps):
+        rar.broadcast(cal, 0)
+    del cal
+    w = inputs.WORKLOADS["ring_grad"]
+    bufs = [torch.from_numpy(x).to("cuda:0") for x in inputs.gradient_like(w["n"], w["count"])]
+    for _ in range(reps):
+        rar.ring_allreduce(bufs)
+    del bufs
+    wb = inputs.WORKLOADS["bfp8"]
+    bufs = [torch.from_numpy(x).to("cuda:0") for x in inputs.block_scaled(wb["n"], wb["count"])]
+    cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"])
+    ws = torch.empty(rar.compressed_workspace_bytes(wb["n"], wb["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    for _ in range(reps):
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+    torch.cuda.synchronize()
+    log("[bench] counters run done")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +408,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-bfp8", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time stepwise, staged and other collectives")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run the short launch sequence used for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the N simulated ranks share one MI355X's HBM, so --gpus "
@@ -359,6 +425,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rar.lib()
+    if args.counters:
+        counters_run()
+        return
 
     f = fp32_leg(args)
     line = {
