@@ -231,17 +231,31 @@ int rar_compressed_traffic(const void* workspace, int nranks, uint64_t* sent, ui
 size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t cap_bytes,
                        int* bucket_of);
 
-/* Workspace for rar_bucketed_allreduce (0 on bad args). */
+/* Workspace for rar_bucketed_allreduce(_ex) (0 on bad args).
+ * FUSED: the launch table, 8 * (2 + 5*nbuckets + (2 + nranks)*ntensors)
+ * bytes rounded up to 256.  STEPWISE: nranks flat buffers of the largest
+ * padded bucket. */
 size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
                                     size_t cap_bytes);
+size_t rar_bucketed_workspace_bytes_ex(const size_t* counts, size_t ntensors, int nranks, int dtype,
+                                       size_t cap_bytes, int algo);
 
 /* tensors: host array of nranks*ntensors device pointers, rank-major
- * (tensors[r*ntensors + t] is rank r's tensor t of counts[t] elements).
- * Each bucket is packed into a flat per-rank buffer in the workspace,
- * ring-allreduced (chunk rule on the bucket), and unpacked in place. */
+ * (tensors[r*ntensors + t] is rank r's tensor t of counts[t] elements; the N
+ * copies of a tensor must not overlap).  Buckets follow rar_bucket_plan; in a
+ * bucket the tensors are laid end to end, each starting on a 16-byte
+ * boundary with a zero gap after it, and the bucket is ring-allreduced with
+ * the chunk rule on that flat layout.
+ * FUSED (rar_bucketed_allreduce): one launch folds every bucket straight
+ * from and into the tensors (no packing; workspace holds the launch table).
+ * STEPWISE: each bucket is packed into flat per-rank buffers in the
+ * workspace, allreduced, and unpacked.  Both give the same bits. */
 int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors,
                            int nranks, int dtype, size_t cap_bytes, void* workspace,
                            size_t ws_bytes, void* stream);
+int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t ntensors,
+                              int nranks, int dtype, size_t cap_bytes, int algo, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
 

@@ -73,6 +73,9 @@ _SIGS = {
     "rar_bucketed_workspace_bytes": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size]),
     "rar_bucketed_allreduce": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_vp, _c_size,
                                         _c_vp]),
+    "rar_bucketed_workspace_bytes_ex": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size, _c_int]),
+    "rar_bucketed_allreduce_ex": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_int, _c_vp,
+                                           _c_size, _c_vp]),
     "rar_status_string": (ctypes.c_char_p, [_c_int]),
     "rar_version": (ctypes.c_char_p, []),
 }
@@ -274,11 +277,11 @@ def bucket_plan(counts, dtype: int, cap_bytes: int):
     return int(nb), list(out)[:len(counts)]
 
 
-def bucketed_workspace_bytes(counts, nranks: int, dtype: int, cap_bytes: int) -> int:
-    return lib().rar_bucketed_workspace_bytes(_sizes(counts), len(counts), nranks, dtype, cap_bytes)
+def bucketed_workspace_bytes(counts, nranks: int, dtype: int, cap_bytes: int, algo: int = ALGO_FUSED) -> int:
+    return lib().rar_bucketed_workspace_bytes_ex(_sizes(counts), len(counts), nranks, dtype, cap_bytes, algo)
 
 
-def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None):
+def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None, algo: int = ALGO_FUSED):
     """tensors[r][t]: rank r's gradient tensor t (device tensors, in place)."""
     n, nt = len(tensors), len(tensors[0])
     t0 = tensors[0][0]
@@ -290,8 +293,8 @@ def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None):
                 raise ValueError("tensor t must have the same size and dtype on every rank")
     ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() for x in flat])
     counts = [tensors[0][t].numel() for t in range(nt)]
-    rc = lib().rar_bucketed_allreduce(ptrs, _sizes(counts), nt, n, dtype_code(t0), cap_bytes,
-                                      workspace.data_ptr() if workspace is not None else None,
-                                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                      _stream(stream, t0))
-    _check(rc, "rar_bucketed_allreduce")
+    rc = lib().rar_bucketed_allreduce_ex(ptrs, _sizes(counts), nt, n, dtype_code(t0), cap_bytes, algo,
+                                         workspace.data_ptr() if workspace is not None else None,
+                                         workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                         _stream(stream, t0))
+    _check(rc, "rar_bucketed_allreduce_ex")

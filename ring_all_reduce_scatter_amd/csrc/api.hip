@@ -743,31 +743,74 @@ static size_t bucket_flat_bytes(const size_t* counts, size_t nt, int dtype, size
   return round_up(maxb, kAlign);
 }
 
-size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
-                                    size_t cap_bytes) {
+// Zero-copy plan: table words (see bucket_kernels.hip) and the launch grid.
+static void bucket_table(const size_t* counts, size_t nt, int n, int dtype, size_t cap, void* const* tensors,
+                         std::vector<uint64_t>& tab, uint64_t* grid, Traffic* tr) {
+  const size_t es = es_of(dtype);
+  std::vector<int> plan(nt ? nt : 1, 0);
+  const size_t nb = rar_bucket_plan(counts, nt, dtype, cap, plan.data());
+  const uint64_t tile = bucket_fold_tile_elems(dtype);
+  tab.assign(2 + 5 * nb + 2 * nt + (size_t)n * nt, 0);
+  tab[0] = nb;
+  uint64_t* start = &tab[1];
+  uint64_t* hdr = &tab[2 + nb];
+  uint64_t* ten = &tab[2 + 5 * nb];
+  uint64_t* ptr = &tab[2 + 5 * nb + 2 * nt];
+  uint64_t wg = 0;
+  size_t t = 0;
+  for (size_t b = 0; b < nb; ++b) {
+    const size_t t0 = t;
+    uint64_t total = 0;
+    while (t < nt && plan[t] == (int)b) {
+      ten[2 * t] = total;
+      ten[2 * t + 1] = counts[t];
+      total += padded_elems(counts[t], es);
+      ++t;
+    }
+    const uint64_t L = chunk_len_aligned(total, n, 128);
+    hdr[4 * b] = total;
+    hdr[4 * b + 1] = L;
+    hdr[4 * b + 2] = t0;
+    hdr[4 * b + 3] = t - t0;
+    start[b] = wg;
+    wg += (uint64_t)n * ((L + tile - 1) / tile);
+    if (tr) ring_pass_traffic(*tr, n, total, L, es, 0), ring_pass_traffic(*tr, n, total, L, es, 1);
+  }
+  start[nb] = wg;
+  if (tensors)
+    for (int r = 0; r < n; ++r)
+      for (size_t k = 0; k < nt; ++k) ptr[(size_t)r * nt + k] = (uint64_t)(uintptr_t)tensors[(size_t)r * nt + k];
+  *grid = wg;
+}
+
+size_t rar_bucketed_workspace_bytes_ex(const size_t* counts, size_t ntensors, int nranks, int dtype,
+                                       size_t cap_bytes, int algo) {
   if (nranks < 1 || nranks > RAR_MAX_RANKS || !dt_ok(dtype) || (ntensors && !counts)) return 0;
+  if (algo == RAR_ALGO_FUSED) {
+    std::vector<uint64_t> tab;
+    uint64_t grid = 0;
+    bucket_table(counts, ntensors, nranks, dtype, cap_bytes, nullptr, tab, &grid, nullptr);
+    return round_up(tab.size() * sizeof(uint64_t), kAlign);
+  }
+  if (algo != RAR_ALGO_STEPWISE) return 0;
   std::vector<int> plan;
   size_t nb = 0;
   const size_t per = bucket_flat_bytes(counts, ntensors, dtype, cap_bytes, plan, &nb);
   return std::max<size_t>((size_t)nranks * per, 16);
 }
 
-int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,
-                           int dtype, size_t cap_bytes, void* workspace, size_t ws_bytes, void* stream) {
-  if (nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
-  if (!dt_ok(dtype)) return RAR_EDTYPE;
-  if (ntensors && (!tensors || !counts)) return RAR_EINVAL;
+size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
+                                    size_t cap_bytes) {
+  return rar_bucketed_workspace_bytes_ex(counts, ntensors, nranks, dtype, cap_bytes, RAR_ALGO_FUSED);
+}
+
+// Pack each bucket into flat per-rank buffers, fused ring allreduce, unpack.
+static int bucketed_packed(void* const* tensors, const size_t* counts, size_t ntensors, int nranks, int dtype,
+                           size_t cap_bytes, void* workspace, hipStream_t st) {
   const size_t es = es_of(dtype);
-  for (size_t i = 0; i < (size_t)nranks * ntensors; ++i) {
-    if (!tensors[i]) return RAR_EOVERLAP;
-    if ((uintptr_t)tensors[i] & 15u) return RAR_EALIGN;
-  }
   std::vector<int> plan;
   size_t nb = 0;
   const size_t per = bucket_flat_bytes(counts, ntensors, dtype, cap_bytes, plan, &nb);
-  if (!workspace || ws_bytes < (size_t)nranks * per) return RAR_EWORKSPACE;
-  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
-  hipStream_t st = (hipStream_t)stream;
   Traffic total;
   total.reset(nranks);
   void* flat[RAR_MAX_RANKS];
@@ -781,7 +824,6 @@ int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt
       off.push_back(elems);
       elems += padded_elems(counts[t1++], es);
     }
-    // pack: every (rank, tensor) segment into the rank's flat bucket
     SegJobs jobs{};
     auto flush = [&]() -> int {
       if (!jobs.njobs) return RAR_OK;
@@ -803,7 +845,6 @@ int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt
       total.sent[r] += g_last.sent[r];
       total.recv[r] += g_last.recv[r];
     }
-    // unpack: the reduced bucket back into every rank's tensors
     for (int r = 0; r < nranks; ++r)
       for (size_t t = t0; t < t1; ++t) {
         jobs.src[jobs.njobs] = (const char*)flat[r] + off[t - t0] * es;
@@ -817,6 +858,45 @@ int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt
   }
   g_last = total;
   return RAR_OK;
+}
+
+int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,
+                              int dtype, size_t cap_bytes, int algo, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  if (nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
+  if (!dt_ok(dtype)) return RAR_EDTYPE;
+  if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_STEPWISE) return RAR_EINVAL;
+  if (ntensors && (!tensors || !counts)) return RAR_EINVAL;
+  const size_t es = es_of(dtype);
+  // tensor t of every rank: non-null, aligned, and no two copies overlap
+  for (size_t t = 0; t < ntensors; ++t) {
+    if (counts[t] == 0) continue;
+    std::vector<void*> copies((size_t)nranks);
+    for (int r = 0; r < nranks; ++r) copies[(size_t)r] = tensors[(size_t)r * ntensors + t];
+    const int rc = check_bufs(copies.data(), nranks, dtype, counts[t] * es);
+    if (rc) return rc;
+  }
+  const size_t need = rar_bucketed_workspace_bytes_ex(counts, ntensors, nranks, dtype, cap_bytes, algo);
+  if (!workspace || ws_bytes < need) return RAR_EWORKSPACE;
+  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == RAR_ALGO_STEPWISE) return bucketed_packed(tensors, counts, ntensors, nranks, dtype, cap_bytes, workspace, st);
+  std::vector<uint64_t> tab;
+  uint64_t grid = 0;
+  Traffic tr;
+  tr.reset(nranks);
+  bucket_table(counts, ntensors, nranks, dtype, cap_bytes, tensors, tab, &grid, &tr);
+  g_last = tr;
+  if (nranks == 1 || grid == 0) return RAR_OK;
+  int rc = hip_rc(launch_fill_u64((uint64_t*)workspace, tab.data(), (int)tab.size(), st));
+  if (rc) return rc;
+  return hip_rc(launch_bucket_fold((const uint64_t*)workspace, nranks, ntensors, grid, dtype, st));
+}
+
+int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors, int nranks, int dtype,
+                           size_t cap_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  return rar_bucketed_allreduce_ex(tensors, counts, ntensors, nranks, dtype, cap_bytes, RAR_ALGO_FUSED, workspace,
+                                   ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ misc

@@ -270,13 +270,14 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_kernel(RankPtrs bufs, 
   }
 }
 
+constexpr int kFillWords = 448;  // 3.5 KiB of kernel arguments per launch
+
 struct U64Vals {
-  uint64_t v[2 * kMaxRanks];
+  uint64_t v[kFillWords];
 };
 
 __global__ void fill_u64_kernel(uint64_t* dst, int n, U64Vals vals) {
-  const int i = threadIdx.x;
-  if (i < n) dst[i] = vals.v[i];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = vals.v[i];
 }
 
 uint32_t blocks_for(uint64_t maxlen) {
@@ -408,11 +409,15 @@ hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uin
 }
 
 hipError_t launch_fill_u64(uint64_t* dst, const uint64_t* host_vals, int nvals, hipStream_t stream) {
-  U64Vals vals{};
-  if (nvals > 2 * kMaxRanks) nvals = 2 * kMaxRanks;
-  for (int i = 0; i < nvals; ++i) vals.v[i] = host_vals[i];
-  hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(2 * kMaxRanks), 0, stream, dst, nvals, vals);
-  return hipGetLastError();
+  for (int base = 0; base < nvals; base += kFillWords) {
+    U64Vals vals{};
+    const int n = nvals - base < kFillWords ? nvals - base : kFillWords;
+    for (int i = 0; i < n; ++i) vals.v[i] = host_vals[base + i];
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(256), 0, stream, dst + base, n, vals);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace rar

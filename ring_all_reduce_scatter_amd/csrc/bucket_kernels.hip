@@ -60,3 +60,174 @@ hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream) {
 }
 
 }  // namespace rar
+
+// ---------------------------------------------------------------- zero-copy bucket fold
+// All buckets of a bucketed allreduce in one launch, reading and writing the
+// gradient tensors in place.  A bucket is the virtual concatenation of its
+// tensors, each starting on a 16-byte boundary; the chunk rule and the ring
+// order apply to that flat index space exactly as if the bucket had been
+// packed, so the results equal pack -> ring allreduce -> unpack.  Because
+// every 16-byte vector of the flat space lies inside one tensor (or in its
+// zero gap), a vector is loaded straight from the N ranks' copies of that
+// tensor.
+//
+// Device table (uint64 words, written by the host before the launch):
+//   [0]                       number of buckets nb
+//   [1, nb+2)                 first workgroup of each bucket (prefix sums)
+//   per bucket b at hdr+4b:   padded length, chunk length L, first tensor, tensors
+//   per tensor t at ten+2t:   flat offset inside its bucket, element count
+//   pointers at ptr + r*nt+t: rank r's copy of tensor t
+namespace rar {
+namespace {
+
+__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) { return *p; }
+
+// Largest i in [lo, hi) with key(i) <= x, where key is ascending.
+template <typename F>
+__device__ __forceinline__ uint64_t upper_index(uint64_t lo, uint64_t hi, uint64_t x, F key) {
+  while (hi - lo > 1) {
+    const uint64_t mid = (lo + hi) / 2;
+    if (key(mid) <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <int DT, int NR, int V>
+__global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* __restrict__ tab, int nranks,
+                                                                uint64_t ntensors) {
+  constexpr int E = Vec<DT>::E;
+  constexpr int ES = DtypeSize<DT>::value;
+  const int N = NR > 0 ? NR : nranks;
+  const uint64_t nb = ld_u64(tab);
+  const uint64_t* start = tab + 1;
+  const uint64_t* hdr = tab + 2 + nb;
+  const uint64_t* ten = hdr + 4 * nb;
+  const uint64_t* ptr = ten + 2 * ntensors;
+  // which bucket this workgroup belongs to (uniform)
+  const uint64_t b = upper_index(0, nb, blockIdx.x, [&](uint64_t i) { return ld_u64(start + i); });
+  const uint64_t local = blockIdx.x - ld_u64(start + b);
+  const uint64_t total = ld_u64(hdr + 4 * b), L = ld_u64(hdr + 4 * b + 1);
+  const uint64_t t0 = ld_u64(hdr + 4 * b + 2), nt = ld_u64(hdr + 4 * b + 3);
+  const int c = (int)(local % (uint64_t)N);
+  const uint64_t tile = local / (uint64_t)N;
+  const uint64_t lo = (uint64_t)c * L;
+  if (lo >= total) return;
+  const uint64_t hi = lo + L < total ? lo + L : total;
+  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
+  const uint64_t tile0 = lo + tile * kTile;
+  if (tile0 >= hi) return;
+  const uint64_t tile1 = tile0 + kTile < hi ? tile0 + kTile : hi;
+  const int first = c + 1 < N ? c + 1 : 0;
+  auto tensor_of = [&](uint64_t f) {  // index into the bucket's tensors
+    return upper_index(0, nt, f, [&](uint64_t i) { return ld_u64(ten + 2 * (t0 + i)); });
+  };
+  const uint64_t ja = tensor_of(tile0), jb = tensor_of(tile1 - 1);
+  auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
+
+  if (ja == jb) {
+    // The whole tile lies in one tensor: uniform pointers, vector loads.
+    const uint64_t t = t0 + ja;
+    const uint64_t off = ld_u64(ten + 2 * t), cnt = ld_u64(ten + 2 * t + 1);
+    if (tile1 <= off + cnt && tile0 + kTile == tile1) {
+      Vec<DT> acc[V];
+      if constexpr (NR > 0) {
+        u32x4 x[NR][V];
+        int r = first;
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+#pragma unroll
+          for (int v = 0; v < V; ++v) x[k][v] = ld16<true>(p + (elem(v) - off) * ES);
+          r = r + 1 == NR ? 0 : r + 1;
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          acc[v] = unpack16<DT>(x[0][v]);
+#pragma unroll
+          for (int k = 1; k < NR; ++k) {
+            const Vec<DT> y = unpack16<DT>(x[k][v]);
+#pragma unroll
+            for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
+          }
+        }
+      } else {
+        int r = first;
+        const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = unpack16<DT>(ld16<true>(p + (elem(v) - off) * ES));
+        for (int k = 1; k < N; ++k) {
+          r = r + 1 == N ? 0 : r + 1;
+          p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            const Vec<DT> y = unpack16<DT>(ld16<true>(p + (elem(v) - off) * ES));
+#pragma unroll
+            for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const u32x4 out = pack16<DT>(acc[v]);
+        for (int d = 0; d < N; ++d)
+          st16<true>((char*)ld_u64(ptr + (uint64_t)d * ntensors + t) + (elem(v) - off) * ES, out);
+      }
+      return;
+    }
+  }
+  // Tiles that cross a tensor boundary, reach into a zero gap, or are the
+  // ragged end of a chunk: element by element, each finding its tensor.
+  for (int v = 0; v < V; ++v) {
+    const uint64_t e = elem(v);
+    for (int i = 0; i < E; ++i) {
+      const uint64_t f = e + i;
+      if (f >= tile1) break;
+      const uint64_t t = t0 + tensor_of(f);
+      const uint64_t off = ld_u64(ten + 2 * t), cnt = ld_u64(ten + 2 * t + 1);
+      if (f - off >= cnt) continue;  // zero gap after the tensor: nothing stored
+      int r = first;
+      float acc = load_elem<DT>((const char*)ld_u64(ptr + (uint64_t)r * ntensors + t), f - off);
+      for (int k = 1; k < N; ++k) {
+        r = r + 1 == N ? 0 : r + 1;
+        acc = round_to<DT>(load_elem<DT>((const char*)ld_u64(ptr + (uint64_t)r * ntensors + t), f - off) + acc);
+      }
+      for (int d = 0; d < N; ++d) store_elem<DT>((char*)ld_u64(ptr + (uint64_t)d * ntensors + t), f - off, acc);
+    }
+  }
+}
+
+template <int DT, int NR>
+hipError_t bucket_fold_dispatch(const uint64_t* tab, int n, uint64_t ntensors, uint64_t grid, hipStream_t stream) {
+  constexpr int V = DT == DT_BF16 ? 1 : 2;
+  hipLaunchKernelGGL((bucket_fold_kernel<DT, NR, V>), dim3((unsigned)grid), dim3(kThreads),
+                     residency_lds(fold_wgs_per_cu(DT, n)), stream, tab, n, ntensors);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t bucket_fold_n(const uint64_t* tab, int n, uint64_t ntensors, uint64_t grid, hipStream_t stream) {
+  switch (n) {
+    case 8: return bucket_fold_dispatch<DT, 8>(tab, n, ntensors, grid, stream);
+    case 16: return bucket_fold_dispatch<DT, 16>(tab, n, ntensors, grid, stream);
+    default: return bucket_fold_dispatch<DT, 0>(tab, n, ntensors, grid, stream);
+  }
+}
+
+}  // namespace
+
+uint64_t bucket_fold_tile_elems(int dt) {
+  return (uint64_t)kThreads * (dt == DT_F32 ? 4 : 8) * (dt == DT_BF16 ? 1 : 2);
+}
+
+hipError_t launch_bucket_fold(const uint64_t* dev_table, int n, uint64_t ntensors, uint64_t grid, int dt,
+                              hipStream_t stream) {
+  if (grid == 0) return hipSuccess;
+  switch (dt) {
+    case DT_F32: return bucket_fold_n<DT_F32>(dev_table, n, ntensors, grid, stream);
+    case DT_F16: return bucket_fold_n<DT_F16>(dev_table, n, ntensors, grid, stream);
+    default: return bucket_fold_n<DT_BF16>(dev_table, n, ntensors, grid, stream);
+  }
+}
+
+}  // namespace rar

@@ -31,9 +31,12 @@ struct DtypeSize {
 };
 
 // ------------------------------------------------------------ conversions
-// binary16: the hardware conversion rounds to nearest even and keeps
-// subnormals.  bfloat16: widening is exact (the upper half of a binary32);
-// narrowing rounds to nearest even on the bit pattern, NaN stays quiet NaN.
+// binary16 and bfloat16: the gfx950 conversion instructions (v_cvt_f16_f32,
+// v_cvt_pk_bf16_f32) round to nearest even under the default mode and keep
+// subnormals; widening is exact (bfloat16 is the upper half of a binary32).
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float h16_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -43,10 +46,11 @@ __device__ __forceinline__ uint32_t f32_to_h16(float f) {
 }
 __device__ __forceinline__ float b16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ uint32_t f32_to_b16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two binary32 values to packed bfloat16 (lo in bits 15:0) in one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_b16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, b16x2));
 }
 
 template <int DT>
@@ -56,6 +60,13 @@ __device__ __forceinline__ float widen16(uint32_t h) {
 template <int DT>
 __device__ __forceinline__ uint32_t narrow16(float f) {
   return DT == DT_F16 ? f32_to_h16(f) : f32_to_b16(f);
+}
+
+// Two binary32 values rounded to a 16-bit type, packed (first in bits 15:0).
+template <int DT>
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+  if constexpr (DT == DT_BF16) return f32x2_to_b16x2(lo, hi);
+  else return narrow16<DT>(lo) | (narrow16<DT>(hi) << 16);
 }
 
 // Round a binary32 value to the dtype and return it widened again.
@@ -134,8 +145,7 @@ __device__ __forceinline__ Raw8<DT> pack8(const G8& g) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r.w[0][i] = narrow16<DT>(g.v[2 * i]) | (narrow16<DT>(g.v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) r.w[0][i] = pack_pair<DT>(g.v[2 * i], g.v[2 * i + 1]);
   }
   return r;
 }
@@ -174,7 +184,7 @@ __device__ __forceinline__ u32x4 pack16(const Vec<DT>& x) {
     for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(x.v[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = narrow16<DT>(x.v[2 * i]) | (narrow16<DT>(x.v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack_pair<DT>(x.v[2 * i], x.v[2 * i + 1]);
   }
   return w;
 }

@@ -19,6 +19,8 @@ namespace rar {
 // residency_lds(w) is just over 1/(w+1) of the CU's LDS, so w workgroups fit
 // and w+1 do not.  0 = no cap.
 size_t residency_lds(int wgs_per_cu);
+// Workgroups per CU for a fused fold of dtype dt over n ranks (0 = no cap).
+int fold_wgs_per_cu(int dt, int n);
 
 // -------------------------------------------------------------- ring (ring_kernels.hip)
 
@@ -110,7 +112,16 @@ struct SegJobs {
 };
 hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream);
 
-// Small utility kernels.
+// Elements per workgroup tile of the zero-copy bucket fold (per chunk).
+uint64_t bucket_fold_tile_elems(int dt);
+// All buckets in one launch, in place on the tensors, driven by a device
+// table (layout in bucket_kernels.hip); grid = total workgroups.
+hipError_t launch_bucket_fold(const uint64_t* dev_table, int n, uint64_t ntensors, uint64_t grid, int dt,
+                              hipStream_t stream);
+
+// Writes nvals host values into device memory, stream-ordered: the values
+// travel as kernel arguments (3.5 KiB per launch), so the host array may be
+// reused as soon as the call returns.
 hipError_t launch_fill_u64(uint64_t* dst, const uint64_t* host_vals, int nvals, hipStream_t stream);
 
 __host__ __device__ inline uint64_t bfp_exp_bytes(uint64_t count, int block) {

@@ -31,13 +31,6 @@ template <int DT>
 struct FoldVecs {
   static constexpr int value = DT == DT_BF16 ? 1 : 2;
 };
-// Workgroups per CU for the fold over n ranks: keeps n * vectors * waves
-// (the loads in flight per CU) at its N = 8 optimum; 0 = no cap.
-int fold_wgs_per_cu(int dt, int n) {
-  const int at8 = dt == DT_BF16 ? 2 : 1;
-  const int w = n > 0 ? at8 * 8 / n : at8;
-  return w < 1 ? 1 : (w >= 8 ? 0 : w);
-}
 constexpr int kStepVecs = 4;  // ... in rs_step
 constexpr int kCopyVecs = 4;  // ... in copy_jobs
 
@@ -255,6 +248,14 @@ hipError_t step_dispatch(const RankPtrs& bufs, int n, uint64_t count, uint64_t L
 
 }  // namespace
 
+// Workgroups per CU for the fold over n ranks: keeps n * vectors * waves
+// (the loads in flight per CU) at its N = 8 optimum; 0 = no cap.
+int fold_wgs_per_cu(int dt, int n) {
+  const int at8 = dt == DT_BF16 ? 2 : 1;
+  const int floor = dt == DT_BF16 ? 2 : 1;  // bf16 needs the waves to hide its rounding ALU
+  const int w = n > 0 ? at8 * 8 / n : at8;
+  return w < floor ? floor : (w >= 8 ? 0 : w);
+}
 size_t residency_lds(int wgs_per_cu) {
   if (wgs_per_cu <= 0) return 0;
   static std::atomic<uint64_t> cache[kMaxRanks];  // per device: LDS per CU << 32 | LDS per workgroup

@@ -82,6 +82,14 @@ def test_bucket_plan_matches_oracle(orc):
     assert rar.bucket_plan([10, 20, 5, 100, 3, 3], rar.BF16, 60) == (4, [0, 0, 1, 2, 3, 3])
 
 
+def test_bucketed_workspace_sizes():
+    counts = [10, 20, 5, 100, 3, 3]
+    # fused: table of 2 + 5*4 + (2 + 8)*6 words, rounded to 256 bytes
+    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == (2 + 20 + 60) * 8 // 256 * 256 + 256
+    # stepwise: 8 flat buffers of the largest padded bucket (100 bf16 -> 208 bytes -> 256)
+    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60, rar.ALGO_STEPWISE) == 8 * 256
+
+
 class _FakeTensor:
     """Stands in for a device tensor in argument-error tests (never launched)."""
 

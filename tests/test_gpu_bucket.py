@@ -13,26 +13,27 @@ from gpu_util import DT_NAMES, assert_bits_equal, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _run(tensors_host, dt, cap):
+def _run(tensors_host, dt, cap, algo=rar.ALGO_FUSED):
     n, nt = len(tensors_host), len(tensors_host[0])
     dev = [to_dev(tensors_host[r], dt) for r in range(n)]
     counts = [t.size for t in tensors_host[0]]
-    ws = torch.empty(rar.bucketed_workspace_bytes(counts, n, DT_NAMES[dt], cap), dtype=torch.uint8,
+    ws = torch.empty(rar.bucketed_workspace_bytes(counts, n, DT_NAMES[dt], cap, algo), dtype=torch.uint8,
                      device="cuda:0")
-    rar.bucketed_allreduce(dev, cap, ws)
+    rar.bucketed_allreduce(dev, cap, ws, algo=algo)
     sent, recv = rar.last_traffic(n)
     return [to_host(dev[r], dt) for r in range(n)], sent, recv
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32", "f16"])
-@pytest.mark.parametrize("n", [2, 4, 16])
-def test_bucketed_matches_oracle(dt, n):
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("algo", [rar.ALGO_FUSED, rar.ALGO_STEPWISE])
+def test_bucketed_matches_oracle(dt, n, algo):
     sizes = inputs.bucket_sizes(40, lo_exp=3, hi_exp=15, salt=n)
     th = inputs.bucket_tensors(n, sizes, dtype=dt, salt=n)
     ref = [[t.copy() for t in th[r]] for r in range(n)]
     cap = 64 << 10
     osent, orecv = oracle.bucketed_allreduce(ref, cap, dt=DT_NAMES[dt])
-    got, sent, recv = _run(th, dt, cap)
+    got, sent, recv = _run(th, dt, cap, algo)
     for r in range(n):
         for t in range(len(sizes)):
             assert_bits_equal(got[r][t], ref[r][t], f"rank {r} tensor {t}")
@@ -48,7 +49,7 @@ def test_buckets_workload_full_size_sampled():
     n, cap = w["n"], w["cap_bytes"]
     sizes = inputs.bucket_sizes(w["ntensors"])
     th = inputs.bucket_tensors(n, sizes)
-    got, _, _ = _run(th, "bf16", cap)
+    got, _, _ = _run(th, "bf16", cap)  # the zero-copy launch
     for r in range(1, n):
         for t in range(len(sizes)):
             assert np.array_equal(got[r][t], got[0][t]), (r, t)
@@ -60,3 +61,18 @@ def test_buckets_workload_full_size_sampled():
         oracle.bucketed_allreduce(sub, cap, dt=oracle.BF16)
         for k, t in enumerate(members):
             assert_bits_equal(got[0][t], sub[0][k], f"bucket {b} tensor {t}")
+
+
+def test_bucketed_large_tensors_both_schedules_agree():
+    """Tensors big enough for full vector tiles, with ragged sizes."""
+    n = 8
+    sizes = [70_001, 3, 250_000, 128, 99_999, 1 << 17]
+    th = inputs.bucket_tensors(n, sizes, dtype="f32", salt=11)
+    ref = [[t.copy() for t in th[r]] for r in range(n)]
+    cap = 1 << 20
+    oracle.bucketed_allreduce(ref, cap)
+    for algo in (rar.ALGO_FUSED, rar.ALGO_STEPWISE):
+        got, _, _ = _run(th, "f32", cap, algo)
+        for r in range(n):
+            for t in range(len(sizes)):
+                assert_bits_equal(got[r][t], ref[r][t], f"algo {algo} rank {r} tensor {t}")

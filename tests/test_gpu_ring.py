@@ -164,3 +164,40 @@ def test_ring_grad_workload_full_size():
     oracle.ring_allreduce(xs)
     for r in range(w["n"]):
         assert_bits_equal(got[r], xs[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_16bit_rounding_edge_pairs_match_oracle(dt):
+    """Pairs whose binary32 sums sit on rounding ties, in the subnormal range,
+    at the overflow boundary and on cancellations: with N=2 every element is
+    one local + received add, rounded to the 16-bit type."""
+    import torch
+    g = np.random.default_rng(21)
+    n = 1 << 16
+    if dt == "f16":
+        a = g.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16).view(np.float16)
+        b = g.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16).view(np.float16)
+        fin = np.isfinite(a) & np.isfinite(b)
+        a, b = a[fin].copy(), b[fin].copy()
+        tiny = (g.integers(0, 1024, size=4096).astype(np.uint16) | (g.integers(0, 2, 4096).astype(np.uint16) << 15))
+        a = np.concatenate([a, tiny.view(np.float16), np.full(64, 65504, np.float16)])
+        b = np.concatenate([b, tiny[::-1].copy().view(np.float16), np.full(64, 16, np.float16)])
+    else:
+        bits_a = g.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+        bits_b = g.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+        fa = (bits_a.astype(np.uint32) << 16).view(np.float32)
+        fb = (bits_b.astype(np.uint32) << 16).view(np.float32)
+        fin = np.isfinite(fa) & np.isfinite(fb)
+        a, b = bits_a[fin].copy(), bits_b[fin].copy()
+        # same-binade pairs whose sums land on bf16 ties, and bf16 subnormals
+        base = (g.integers(0x3f80, 0x4000, size=4096)).astype(np.uint16)
+        a = np.concatenate([a, base, (g.integers(0, 0x80, 4096)).astype(np.uint16), np.full(64, 0x7f7f, np.uint16)])
+        b = np.concatenate([b, (base ^ 1).astype(np.uint16), (g.integers(0, 0x80, 4096)).astype(np.uint16),
+                            np.full(64, 0x7f7f, np.uint16)])
+    ref = [a.copy(), b.copy()]
+    oracle.ring_allreduce(ref, dt=DT_NAMES[dt])
+    bufs = to_dev([a, b], dt)
+    rar.ring_allreduce(bufs)
+    got = to_host(bufs, dt)
+    for r in range(2):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
