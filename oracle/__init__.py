@@ -22,6 +22,8 @@ Parity status of each function (what pins it is in the tests under
                                     vs exact sum, sparse==uncompressed ring)
   bucket plan / bucketed allreduce  pinned (hand-worked plan, greedy rule
                                     properties, exact integer sums)
+  tree allreduce .................. pinned (exact integer sums, hand-written
+                                    balanced-tree expressions, byte counts)
 """
 import ctypes
 import os
@@ -79,6 +81,8 @@ def _load():
                                                   _c_size, _u64p, _u64p]),
         "orc_fpenv_ok": (ctypes.c_int, []),
         "orc_convert": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, ctypes.c_int, _c_size]),
+        "orc_tree_reduce_round": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int]),
+        "orc_tree_allreduce": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, _u64p, _u64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -188,6 +192,16 @@ def _collective(name, bufs, dt, *extra):
 def ring_allreduce(bufs, dt=None):
     """In place; returns (sent_bytes, recv_bytes) per rank."""
     return _collective("orc_ring_allreduce", bufs, dt)
+
+
+def tree_allreduce(bufs, dt=None):
+    """Binomial-tree reduce into rank 0, then binomial broadcast; in place."""
+    return _collective("orc_tree_allreduce", bufs, dt)
+
+
+def tree_reduce_round(bufs, span, dt=None):
+    dt = _dt_of(bufs[0], dt)
+    _check(lib().orc_tree_reduce_round(_ptrs(bufs), len(bufs), bufs[0].size, dt, span), "tree_reduce_round")
 
 
 def reduce_scatter(bufs, dt=None):

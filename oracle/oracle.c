@@ -262,6 +262,34 @@ int orc_broadcast(void* const* bufs, int n, size_t count, int dt, int root, uint
   return ORC_OK;
 }
 
+/* One reduce round of the tree allreduce ([P2] ring-vs-tree table: the
+ * tree reduces along a binary tree of depth log2 N).  Round with distance
+ * `span` (1, 2, 4, ...): every rank rel with rel % (2*span) == 0 and
+ * rel + span < N adds rank rel+span's buffer into its own (local (+)
+ * received).  Ranks are counted from rank 0. */
+static void tree_reduce_round(void* const* bufs, int n, size_t count, int dt, int span, uint64_t* sent,
+                              uint64_t* recv) {
+  size_t es = dtype_size(dt);
+  for (int rel = 0; rel + span < n; rel += 2 * span) {
+    for (size_t i = 0; i < count; ++i) accumulate(bufs[rel], i, dt, widen(bufs[rel + span], i, dt));
+    add_traffic(sent, recv, rel + span, rel, (uint64_t)count * es);
+  }
+}
+
+int orc_tree_reduce_round(void* const* bufs, int n, size_t count, int dt, int span) {
+  if (!check_bufs(bufs, n, dt) || span < 1 || span >= n || (span & (span - 1))) return ORC_EINVAL;
+  tree_reduce_round(bufs, n, count, dt, span, NULL, NULL);
+  return ORC_OK;
+}
+
+/* Tree allreduce: ceil(log2 N) reduce rounds into rank 0, then the
+ * binomial broadcast from rank 0 (2 ceil(log2 N) steps in all). */
+int orc_tree_allreduce(void* const* bufs, int n, size_t count, int dt, uint64_t* sent, uint64_t* recv) {
+  if (!check_bufs(bufs, n, dt)) return ORC_EINVAL;
+  for (int span = 1; span < n; span *= 2) tree_reduce_round(bufs, n, count, dt, span, sent, recv);
+  return orc_broadcast(bufs, n, count, dt, 0, sent, recv);
+}
+
 /* The naive allreduce the ring replaces ([P2] problem background): every
  * rank's tensor is gathered at a root and summed there.  Summed in binary64
  * in rank order; for integer-valued inputs every partial sum is exact, which
