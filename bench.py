@@ -354,6 +354,23 @@ def extra_legs(args):
                                      "frac_of_roofline_fold_only_bytes": round(2 * wk["n"] * S3 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del dev, ws
     torch.cuda.empty_cache()
+    # [P2] exercise: ring vs tree wall-clock on 4 ranks at 1 KB, 1 MB and 16 MB
+    rvt = {}
+    for nbytes in (1 << 10, 1 << 20, 16 << 20):
+        cnt = nbytes // 4
+        xf = inputs.gradient_like(4, cnt, salt=nbytes)
+        pristine = [torch.from_numpy(x).to("cuda:0") for x in xf]
+        sets = make_sets(pristine, 1 + steps)
+        row = {}
+        for nm, fn in (("ring_stepwise", lambda b: rar.ring_allreduce_ex(b, rar.ALGO_STEPWISE)),
+                       ("tree_stepwise", lambda b: rar.tree_allreduce_ex(b, rar.ALGO_STEPWISE)),
+                       ("ring_fused", lambda b: rar.ring_allreduce(b)),
+                       ("tree_fused", lambda b: rar.tree_allreduce(b))):
+            ms, k, _ = time_leg(fn, sets, 2, steps)
+            row[nm + "_us"] = round(ms * 1e3, 2)
+        rvt[f"{nbytes}B"] = row
+        del sets, pristine
+    out["ring_vs_tree_4ranks_fp32"] = rvt
     for name, fn, cnt in (("fp32_broadcast_fused", lambda b: rar.broadcast(b, 0), w5["bcast_count"]),
                           ("fp32_allgather_fused", lambda b: rar.allgather(b), w5["ag_shard"] * 8)):
         xf = inputs.filler(8, cnt)

@@ -122,6 +122,34 @@ int rar_broadcast_ex(void* const* bufs, int nranks, size_t count, int dtype, int
 int rar_rs_step(void* const* bufs, int nranks, size_t count, int dtype, int step, void* stream);
 int rar_ag_step(void* const* bufs, int nranks, size_t count, int dtype, int step, void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Tree allreduce and size-based selection ([P2] ring-vs-tree table and   */
+/* production patterns: the tree has depth log2 N and wins for small      */
+/* messages or high-latency links; the ring wins for large ones).         */
+/* ---------------------------------------------------------------------- */
+
+/* Binomial tree rooted at rank 0: in the reduce round with distance span
+ * (1, 2, 4, ...) rank rel (rel % 2span == 0, rel + span < N) adds rank
+ * rel+span's buffer into its own (local + received); then the binomial
+ * broadcast from rank 0.  Every rank ends with rank 0's sum, e.g. for N = 8
+ * ((x0+x1)+(x2+x3))+((x4+x5)+(x6+x7)).  FUSED runs in one launch for
+ * N in 2..8 and 16 (other N run the STEPWISE rounds); STEPWISE launches one
+ * pairwise-add per reduce round and one copy per broadcast round.
+ * Per-rank bytes: rank 0 receives and sends ceil(log2 N) * T. */
+int rar_tree_allreduce(void* const* bufs, int nranks, size_t count, int dtype, void* stream);
+int rar_tree_allreduce_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo,
+                          void* stream);
+
+enum { RAR_ALLREDUCE_RING = 0, RAR_ALLREDUCE_TREE = 1 };
+#define RAR_TREE_THRESHOLD_DEFAULT (1u << 20) /* 1 MiB per rank, the crossover [P2] quotes */
+
+/* Tree below threshold_bytes per rank (0 = RAR_TREE_THRESHOLD_DEFAULT),
+ * ring otherwise; *chosen (if not NULL) receives RAR_ALLREDUCE_RING or
+ * RAR_ALLREDUCE_TREE.  The two orders round differently, so results can
+ * differ in the last bits between the two sides of the threshold. */
+int rar_allreduce_auto(void* const* bufs, int nranks, size_t count, int dtype,
+                       size_t threshold_bytes, int* chosen, void* stream);
+
 /* Logical bytes each rank sent and received in the last collective issued
  * by the calling host thread (uncompressed calls; the counters of the
  * compressed allreduce are read with rar_compressed_traffic).  sent/recv:

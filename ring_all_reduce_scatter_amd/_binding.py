@@ -59,6 +59,10 @@ _SIGS = {
     "rar_rs_step": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
     "rar_ag_step": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
     "rar_last_traffic": (_c_int, [_u64p, _u64p, _c_int]),
+    "rar_tree_allreduce": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_vp]),
+    "rar_tree_allreduce_ex": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp]),
+    "rar_allreduce_auto": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_size, ctypes.POINTER(ctypes.c_int),
+                                    _c_vp]),
     "rar_bfp_bytes": (_c_size, [_c_size, _c_int, _c_int]),
     "rar_bfp_compress": (_c_int, [_c_vp, _c_int, _c_size, _c_int, _c_int, _c_vp, _c_vp]),
     "rar_bfp_decompress_accumulate": (_c_int, [_c_vp, _c_size, _c_int, _c_int, _c_vp, _c_int, _c_vp]),
@@ -192,6 +196,25 @@ def rs_step(bufs, step: int, stream=None):
 
 def ag_step(bufs, step: int, stream=None):
     _call_bufs("rar_ag_step", bufs, step, stream=stream)
+
+
+ALLREDUCE_RING, ALLREDUCE_TREE = 0, 1
+TREE_THRESHOLD_DEFAULT = 1 << 20
+
+
+def tree_allreduce(bufs, stream=None):
+    _call_bufs("rar_tree_allreduce", bufs, stream=stream)
+
+
+def tree_allreduce_ex(bufs, algo: int, stream=None):
+    _call_bufs("rar_tree_allreduce_ex", bufs, algo, stream=stream)
+
+
+def allreduce_auto(bufs, threshold_bytes: int = 0, stream=None) -> int:
+    """Tree below the threshold (bytes per rank), ring above; returns the choice."""
+    chosen = ctypes.c_int(-1)
+    _call_bufs("rar_allreduce_auto", bufs, threshold_bytes, ctypes.byref(chosen), stream=stream)
+    return chosen.value
 
 
 def last_traffic(nranks: int):

@@ -563,6 +563,68 @@ int rar_broadcast(void* const* bufs, int nranks, size_t count, int dtype, int ro
   return rar_broadcast_ex(bufs, nranks, count, dtype, root, RAR_ALGO_FUSED, stream);
 }
 
+// ------------------------------------------------------------------ tree allreduce
+
+static int tree_broadcast_rounds(const RankPtrs& p, int nranks, size_t bytes, hipStream_t st) {
+  for (int span = 1; span < nranks; span *= 2) {
+    CopyJobs jobs{};
+    jobs.ptrs = p;
+    int j = 0;
+    for (int rel = 0; rel < span && rel + span < nranks; ++rel) {
+      jobs.lo[j] = 0;
+      jobs.len[j] = bytes;
+      jobs.dstmask[j] = 1ull << (rel + span);
+      jobs.src[j] = (int8_t)rel;
+      ++j;
+    }
+    jobs.njobs = j;
+    int rc = hip_rc(launch_copy_jobs(jobs, st));
+    if (rc) return rc;
+  }
+  return RAR_OK;
+}
+
+int rar_tree_allreduce_ex(void* const* bufs, int nranks, size_t count, int dtype, int algo, void* stream) {
+  const size_t es = es_of(dtype);
+  int rc = check_bufs(bufs, nranks, dtype, count * es);
+  if (rc) return rc;
+  if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_STEPWISE) return RAR_EINVAL;
+  g_last.reset(nranks);
+  for (int span = 1; span < nranks; span *= 2)
+    for (int rel = 0; rel + span < nranks; rel += 2 * span) g_last.add(rel + span, rel, (uint64_t)count * es);
+  tree_traffic(g_last, nranks, 0, (uint64_t)count * es);
+  if (nranks == 1 || count == 0) return RAR_OK;
+  RankPtrs p = make_ptrs(bufs, nranks);
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == RAR_ALGO_FUSED && tree_fold_supported(nranks))
+    return hip_rc(launch_tree_fold(p, nranks, count, dtype, st));
+  for (int span = 1; span < nranks; span *= 2) {
+    PairJobs pairs{};
+    for (int rel = 0; rel + span < nranks; rel += 2 * span) {
+      pairs.dst[pairs.npairs] = (int8_t)rel;
+      pairs.src[pairs.npairs] = (int8_t)(rel + span);
+      ++pairs.npairs;
+    }
+    if ((rc = hip_rc(launch_pair_add(p, pairs, count, dtype, st)))) return rc;
+  }
+  return tree_broadcast_rounds(p, nranks, count * es, st);
+}
+
+int rar_tree_allreduce(void* const* bufs, int nranks, size_t count, int dtype, void* stream) {
+  return rar_tree_allreduce_ex(bufs, nranks, count, dtype, RAR_ALGO_FUSED, stream);
+}
+
+int rar_allreduce_auto(void* const* bufs, int nranks, size_t count, int dtype, size_t threshold_bytes,
+                       int* chosen, void* stream) {
+  if (!dt_ok(dtype)) return RAR_EDTYPE;
+  const size_t thr = threshold_bytes ? threshold_bytes : (size_t)RAR_TREE_THRESHOLD_DEFAULT;
+  const int tree = count * es_of(dtype) < thr;
+  const int rc = tree ? rar_tree_allreduce(bufs, nranks, count, dtype, stream)
+                      : rar_ring_allreduce(bufs, nranks, count, dtype, stream);
+  if (rc == RAR_OK && chosen) *chosen = tree ? RAR_ALLREDUCE_TREE : RAR_ALLREDUCE_RING;
+  return rc;
+}
+
 int rar_last_traffic(uint64_t* sent, uint64_t* recv, int nranks) {
   if (!sent || !recv || nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
   for (int r = 0; r < nranks; ++r) {

@@ -34,6 +34,18 @@ hipError_t launch_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_
 hipError_t launch_rs_step(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt, int s,
                           hipStream_t stream);
 
+// Tree allreduce: fused (all ranks in registers, binomial order) for the
+// rank counts tree_fold_supported() accepts; pairwise whole-buffer adds for
+// the stepwise rounds.
+struct PairJobs {
+  int8_t src[kMaxRanks];
+  int8_t dst[kMaxRanks];
+  int npairs;
+};
+bool tree_fold_supported(int n);
+hipError_t launch_tree_fold(const RankPtrs& bufs, int n, uint64_t count, int dt, hipStream_t stream);
+hipError_t launch_pair_add(const RankPtrs& bufs, const PairJobs& pairs, uint64_t count, int dt, hipStream_t stream);
+
 // Byte-range copies from one rank buffer to a set of rank buffers, at the
 // same offset in each.  Up to kMaxRanks jobs per launch.
 struct CopyJobs {

@@ -171,6 +171,96 @@ __global__ __launch_bounds__(kThreads) void rs_step_kernel(RankPtrs bufs, int N,
   }
 }
 
+// ---------------------------------------------------------------- tree allreduce
+// Binomial tree (page "从零实现集合通信", ring-vs-tree table: depth log2 N):
+// in the reduce round with distance span, rank rel (rel % 2span == 0,
+// rel + span < N) adds rank rel+span into its own copy; rank 0 ends with
+// the sum, which the binomial broadcast then gives to every rank.  The fused
+// kernel applies the same rounds to all N ranks' vectors in registers and
+// stores rank 0's result to every rank.
+template <int DT, int NR, int V>
+__global__ __launch_bounds__(kThreads) void tree_fold_kernel(RankPtrs bufs, uint64_t count) {
+  constexpr int E = Vec<DT>::E;
+  constexpr int ES = DtypeSize<DT>::value;
+  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
+  const uint64_t tile0 = (uint64_t)blockIdx.x * kTile;
+  if (tile0 >= count) return;
+  auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
+  if (tile0 + kTile <= count) {
+    Vec<DT> x[NR][V];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) x[r][v] = unpack16<DT>(ld16<true>(bufs.p[r] + elem(v) * ES));
+#pragma unroll
+    for (int span = 1; span < NR; span *= 2)
+#pragma unroll
+      for (int rel = 0; rel + span < NR; rel += 2 * span)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int i = 0; i < E; ++i) x[rel][v].v[i] = round_to<DT>(x[rel][v].v[i] + x[rel + span][v].v[i]);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const u32x4 out = pack16<DT>(x[0][v]);
+      for (int d = 0; d < NR; ++d) st16<true>(bufs.p[d] + elem(v) * ES, out);
+    }
+    return;
+  }
+  for (int v = 0; v < V; ++v) {
+    const uint64_t e = elem(v);
+    for (int i = 0; i < E && e + i < count; ++i) {
+      float x[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) x[r] = load_elem<DT>(bufs.p[r], e + i);
+#pragma unroll
+      for (int span = 1; span < NR; span *= 2)
+#pragma unroll
+        for (int rel = 0; rel + span < NR; rel += 2 * span) x[rel] = round_to<DT>(x[rel] + x[rel + span]);
+      for (int d = 0; d < NR; ++d) store_elem<DT>(bufs.p[d], e + i, x[0]);
+    }
+  }
+}
+
+// One stepwise reduce round: pair j adds rank src[j]'s whole buffer into rank dst[j].
+template <int DT, int V>
+__global__ __launch_bounds__(kThreads) void pair_add_kernel(RankPtrs bufs, PairJobs pairs, uint64_t count,
+                                                             uint32_t tiles) {
+  constexpr int E = Vec<DT>::E;
+  constexpr int ES = DtypeSize<DT>::value;
+  const int j = (int)(blockIdx.x % (uint32_t)pairs.npairs);
+  const uint64_t t = blockIdx.x / (uint32_t)pairs.npairs;
+  const char* src = bufs.p[pairs.src[j]];
+  char* dst = bufs.p[pairs.dst[j]];
+  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
+  const uint64_t tile0 = t * kTile;
+  if (tile0 >= count) return;
+  auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
+  if (tile0 + kTile <= count) {
+    u32x4 a[V], b[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      a[v] = ld16<false>(dst + elem(v) * ES);
+      b[v] = ld16<true>(src + elem(v) * ES);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      Vec<DT> x = unpack16<DT>(a[v]);
+      const Vec<DT> y = unpack16<DT>(b[v]);
+#pragma unroll
+      for (int i = 0; i < E; ++i) x.v[i] = round_to<DT>(x.v[i] + y.v[i]);
+      st16<false>(dst + elem(v) * ES, pack16<DT>(x));
+    }
+    return;
+  }
+  for (int v = 0; v < V; ++v) {
+    const uint64_t e = elem(v);
+    for (int i = 0; i < E && e + i < count; ++i)
+      store_elem<DT>(dst, e + i, round_to<DT>(load_elem<DT>(dst, e + i) + load_elem<DT>(src, e + i)));
+  }
+  (void)tiles;
+}
+
 // Copy jobs: job j copies bytes [lo, lo+len) of rank src[j] to the same range
 // of every rank in dstmask[j].  The 16-byte aligned middle is tiled over the
 // job's workgroups; the unaligned head and tail (2-byte units) are done by
@@ -246,6 +336,41 @@ hipError_t step_dispatch(const RankPtrs& bufs, int n, uint64_t count, uint64_t L
   return hipGetLastError();
 }
 
+template <int DT, int NR>
+hipError_t tree_dispatch_v(const RankPtrs& bufs, uint64_t count, hipStream_t stream) {
+  constexpr int V = DT == DT_BF16 ? 1 : 2;
+  const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * V;
+  const uint64_t tiles = (count + tile - 1) / tile;
+  hipLaunchKernelGGL((tree_fold_kernel<DT, NR, V>), dim3((unsigned)tiles), dim3(kThreads),
+                     residency_lds(fold_wgs_per_cu(DT, NR)), stream, bufs, count);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t tree_dispatch_n(const RankPtrs& bufs, int n, uint64_t count, hipStream_t stream) {
+  switch (n) {
+    case 2: return tree_dispatch_v<DT, 2>(bufs, count, stream);
+    case 3: return tree_dispatch_v<DT, 3>(bufs, count, stream);
+    case 4: return tree_dispatch_v<DT, 4>(bufs, count, stream);
+    case 5: return tree_dispatch_v<DT, 5>(bufs, count, stream);
+    case 6: return tree_dispatch_v<DT, 6>(bufs, count, stream);
+    case 7: return tree_dispatch_v<DT, 7>(bufs, count, stream);
+    case 8: return tree_dispatch_v<DT, 8>(bufs, count, stream);
+    case 16: return tree_dispatch_v<DT, 16>(bufs, count, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t pair_dispatch(const RankPtrs& bufs, const PairJobs& pairs, uint64_t count, hipStream_t stream) {
+  constexpr int V = 4;
+  const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * V;
+  const uint64_t tiles = (count + tile - 1) / tile;
+  hipLaunchKernelGGL((pair_add_kernel<DT, V>), dim3((unsigned)(tiles * (uint64_t)pairs.npairs)), dim3(kThreads), 0,
+                     stream, bufs, pairs, count, (uint32_t)tiles);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Workgroups per CU for the fold over n ranks: keeps n * vectors * waves
@@ -312,6 +437,26 @@ hipError_t launch_copy_jobs(const CopyJobs& jobs, hipStream_t stream) {
   const size_t lds = residency_lds(fanout >= 4 ? 3 : 6);
   hipLaunchKernelGGL(copy_jobs_kernel, grid, block, lds, stream, jobs, tiles);
   return hipGetLastError();
+}
+
+bool tree_fold_supported(int n) { return (n >= 2 && n <= 8) || n == 16; }
+
+hipError_t launch_tree_fold(const RankPtrs& bufs, int n, uint64_t count, int dt, hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  switch (dt) {
+    case DT_F32: return tree_dispatch_n<DT_F32>(bufs, n, count, stream);
+    case DT_F16: return tree_dispatch_n<DT_F16>(bufs, n, count, stream);
+    default: return tree_dispatch_n<DT_BF16>(bufs, n, count, stream);
+  }
+}
+
+hipError_t launch_pair_add(const RankPtrs& bufs, const PairJobs& pairs, uint64_t count, int dt, hipStream_t stream) {
+  if (count == 0 || pairs.npairs == 0) return hipSuccess;
+  switch (dt) {
+    case DT_F32: return pair_dispatch<DT_F32>(bufs, pairs, count, stream);
+    case DT_F16: return pair_dispatch<DT_F16>(bufs, pairs, count, stream);
+    default: return pair_dispatch<DT_BF16>(bufs, pairs, count, stream);
+  }
 }
 
 }  // namespace rar
