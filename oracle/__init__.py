@@ -22,6 +22,11 @@ Parity status of each function (what pins it is in the tests under
                                     vs exact sum, sparse==uncompressed ring)
   bucket plan / bucketed allreduce  pinned (hand-worked plan, greedy rule
                                     properties, exact integer sums)
+  stateful BFP ring (error feedback / delta)
+                                    pinned (first call = plain BFP ring; exact
+                                    conservation of value + residual; 1/T
+                                    convergence of the mean; delta coding
+                                    converging on constant inputs)
   tree allreduce .................. pinned (exact integer sums, hand-written
                                     balanced-tree expressions, byte counts)
 """
@@ -81,6 +86,9 @@ def _load():
                                                   _c_size, _u64p, _u64p]),
         "orc_fpenv_ok": (ctypes.c_int, []),
         "orc_convert": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, ctypes.c_int, _c_size]),
+        "orc_ring_allreduce_compressed_state": (ctypes.c_int, [
+            _c_vp, _c_vp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_size, ctypes.c_int,
+            _u64p, _u64p]),
         "orc_tree_reduce_round": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int]),
         "orc_tree_allreduce": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, _u64p, _u64p]),
     }
@@ -295,6 +303,23 @@ def ring_allreduce_compressed(bufs, method=COMP_BFP, block=128, mbits=8, theta=0
         bm.ctypes.data if bm is not None else None, sent, recv), "ring_allreduce_compressed")
     if with_blockmax:
         return list(sent), list(recv), bm
+    return list(sent), list(recv)
+
+
+FB_ERROR, FB_DELTA = 1, 2
+
+
+def ring_allreduce_compressed_state(bufs, state, feedback, block=128, mbits=8, unit=2097152, dt=None):
+    """BFP ring with per-rank binary32 state (error feedback or delta
+    encoding); bufs and state (float32 arrays, one per rank) in place."""
+    dt = _dt_of(bufs[0], dt)
+    n = len(bufs)
+    for st in state:
+        if st.dtype != np.float32 or st.size != bufs[0].size:
+            raise ValueError("state must be float32 arrays of the buffer length")
+    sent, recv = _traffic(n)
+    _check(lib().orc_ring_allreduce_compressed_state(_ptrs(bufs), _ptrs(state), n, bufs[0].size, dt, block, mbits,
+                                                     unit, feedback, sent, recv), "compressed_state")
     return list(sent), list(recv)
 
 

@@ -626,6 +626,92 @@ int orc_ring_allreduce_compressed(void* const* bufs, int n, size_t count, int dt
 }
 
 /* ------------------------------------------------------------------ */
+/* Stateful BFP ring ([P4] section 2.1 differential encoding, section 3.3 */
+/* 'diff' compression type, section 5 error feedback).  In the           */
+/* compressed ring every rank encodes each of its elements exactly once  */
+/* per allreduce (the N-1 chunks it sends in the reduce-scatter, its own */
+/* chunk in the allgather), so one binary32 state value per rank and     */
+/* element is well defined:                                              */
+/*   error feedback:  v = p + e;  send E(v);  e <- v - D(E(v))           */
+/*   delta:           v = p - ref; send E(v); p^ = ref + D(E(v));         */
+/*                    ref <- p^ (both ends track the reconstruction)     */
+/* where p is the sender's current value (its partial in the reduce-     */
+/* scatter, the finished sum in the allgather) and the receiver uses     */
+/* D(E(v)) (error feedback) or p^ (delta) in place of the message value. */
+/* ------------------------------------------------------------------ */
+
+enum { ORC_FB_ERROR = 1, ORC_FB_DELTA = 2 };
+
+/* Encode len elements of `src` (dtype dt) with the sender's state st[] and
+ * return in `val` the binary32 value the receiver takes for each element. */
+static void stateful_message(const void* src, int dt, float* st, size_t len, int block, int mbits, int feedback,
+                             float* v, uint8_t* msg, float* val) {
+  for (size_t i = 0; i < len; ++i) {
+    float p = widen(src, i, dt);
+    v[i] = feedback == ORC_FB_ERROR ? p + st[i] : p - st[i];
+  }
+  orc_bfp_encode(v, ORC_F32, len, block, mbits, msg, NULL);
+  size_t nb = (len + (size_t)block - 1) / (size_t)block;
+  size_t eb = (nb + 15) / 16 * 16;
+  for (size_t i = 0; i < len; ++i) {
+    float d = bfp_value(msg, eb, i, block, mbits);
+    if (feedback == ORC_FB_ERROR) {
+      st[i] = v[i] - d;
+      val[i] = d;
+    } else {
+      float rec = st[i] + d;
+      st[i] = rec;
+      val[i] = rec;
+    }
+  }
+}
+
+/* state[r]: rank r's binary32 state, count elements (zero before the first
+ * call).  unit must be a positive multiple of block. */
+int orc_ring_allreduce_compressed_state(void* const* bufs, float* const* state, int n, size_t count, int dt,
+                                        int block, int mbits, size_t unit, int feedback, uint64_t* sent,
+                                        uint64_t* recv) {
+  if (!check_bufs(bufs, n, dt) || !bfp_args_ok(block, mbits) || !state) return ORC_EINVAL;
+  if (feedback != ORC_FB_ERROR && feedback != ORC_FB_DELTA) return ORC_EINVAL;
+  if (unit == 0 || unit % (size_t)block) return ORC_EINVAL;
+  size_t es = dtype_size(dt);
+  size_t L = orc_comp_chunk_len(count, n, block);
+  float* v = (float*)malloc(sizeof(float) * unit);
+  float* val = (float*)malloc(sizeof(float) * unit);
+  uint8_t* msg = (uint8_t*)malloc(orc_bfp_bytes(unit, block, mbits));
+  for (int s = 1; s <= n - 1; ++s) {
+    for (int r = 0; r < n; ++r) {
+      int src = modn(r - 1, n), c = modn(r - s - 1, n);
+      size_t lo, hi;
+      chunk_range(count, L, c, &lo, &hi);
+      for (size_t u = lo; u < hi; u += unit) {
+        size_t len = hi - u < unit ? hi - u : unit;
+        stateful_message((const char*)bufs[src] + u * es, dt, state[src] + u, len, block, mbits, feedback, v, msg,
+                         val);
+        add_traffic(sent, recv, src, r, (uint64_t)orc_bfp_bytes(len, block, mbits));
+        for (size_t i = 0; i < len; ++i) accumulate(bufs[r], u + i, dt, val[i]);
+      }
+    }
+  }
+  for (int c = 0; c < n; ++c) {
+    size_t lo, hi;
+    chunk_range(count, L, c, &lo, &hi);
+    for (size_t u = lo; u < hi; u += unit) {
+      size_t len = hi - u < unit ? hi - u : unit;
+      stateful_message((const char*)bufs[c] + u * es, dt, state[c] + u, len, block, mbits, feedback, v, msg, val);
+      for (int s = 1; s <= n - 1; ++s)
+        add_traffic(sent, recv, modn(c + s - 1, n), modn(c + s, n), (uint64_t)orc_bfp_bytes(len, block, mbits));
+      for (int r = 0; r < n; ++r)
+        for (size_t i = 0; i < len; ++i) narrow_store(bufs[r], u + i, dt, val[i]);
+    }
+  }
+  free(msg);
+  free(val);
+  free(v);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* Gradient bucketing ([P2] production patterns: fuse small gradients   */
 /* into buckets of about 25 MB, one allreduce per bucket).  Greedy in   */
 /* tensor order; a tensor larger than the cap travels alone.            */

@@ -1,0 +1,97 @@
+"""Pins for the oracle's stateful BFP ring: error feedback and delta coding
+(CPU only).
+
+Page "CCCL通信压缩库：突破LLM训练通信墙的工程实践": section 2.1 (differential
+encoding sends the change from the previous round at fewer bits), section 3.3
+(the 'diff' compression type), section 5 (error feedback carries the
+precision lost this round into the next round).  Pinned by:
+  * with zero state the first call equals the plain BFP ring;
+  * error feedback conserves value exactly: for every element,
+    result + sum of new residuals == sum of inputs + sum of old residuals
+    (every rank encodes each element once; inputs chosen so that every
+    operation is exact in binary32);
+  * the mean of T error-feedback results on a constant gradient converges
+    to the exact sum like 1/T;
+  * delta coding on a constant gradient converges to the exact sum, and the
+    owner's reference equals the final value.
+"""
+import numpy as np
+import pytest
+
+from ring_all_reduce_scatter_amd import inputs
+
+
+def _zeros(n, count):
+    return [np.zeros(count, dtype=np.float32) for _ in range(n)]
+
+
+@pytest.mark.parametrize("feedback", [1, 2])
+@pytest.mark.parametrize("mbits", [8, 4])
+def test_first_call_equals_plain_bfp_ring(orc, feedback, mbits):
+    n, count = 4, 4 * 2048 + 300
+    xs = inputs.block_scaled(n, count, salt=feedback + mbits)
+    a = [x.copy() for x in xs]
+    b = [x.copy() for x in xs]
+    sa, ra = orc.ring_allreduce_compressed(a, mbits=mbits, unit=1024)
+    sb, rb = orc.ring_allreduce_compressed_state(b, _zeros(n, count), feedback, mbits=mbits, unit=1024)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint16), v.view(np.uint16))
+    assert sa == sb and ra == rb
+
+
+def _exact_inputs(n, count, seed):
+    g = np.random.default_rng(seed)
+    return [(g.integers(-2048, 2049, size=count) / 256.0).astype(np.float32) for _ in range(n)]
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("mbits", [4, 6])
+def test_error_feedback_conserves_value_exactly(orc, n, mbits):
+    count = n * 512 + 100
+    state = _zeros(n, count)
+    for it in range(3):
+        xs = _exact_inputs(n, count, 10 * n + it)
+        before = sum(s.astype(np.float64) for s in state)
+        bufs = [x.copy() for x in xs]
+        orc.ring_allreduce_compressed_state(bufs, state, orc.FB_ERROR, mbits=mbits, unit=256)
+        after = sum(s.astype(np.float64) for s in state)
+        lhs = bufs[0].astype(np.float64) + after
+        rhs = sum(x.astype(np.float64) for x in xs) + before
+        assert np.array_equal(lhs, rhs), it
+        for b in bufs[1:]:
+            assert np.array_equal(b, bufs[0])
+        if it == 0:
+            assert np.any(after != 0)  # the quantiser really lost something
+
+
+def test_error_feedback_mean_converges_like_one_over_t(orc):
+    n, count = 4, 4 * 1024
+    g = inputs.gradient_like(n, count, outlier_p=0.0, salt=5)
+    exact = sum(x.astype(np.float64) for x in g)
+    state = _zeros(n, count)
+    acc = np.zeros(count)
+    errs = {}
+    for t in range(1, 65):
+        bufs = [x.copy() for x in g]
+        orc.ring_allreduce_compressed_state(bufs, state, orc.FB_ERROR, mbits=4, unit=1024)
+        acc += bufs[0].astype(np.float64)
+        if t in (1, 64):
+            errs[t] = np.max(np.abs(acc / t - exact))
+    assert errs[64] < errs[1] / 16
+
+
+def test_delta_coding_converges_on_constant_input(orc):
+    n, count = 4, 4 * 1024
+    g = inputs.gradient_like(n, count, outlier_p=0.0, salt=6)
+    exact = sum(x.astype(np.float64) for x in g)
+    state = _zeros(n, count)
+    errs = []
+    L = orc.comp_chunk_len(count, n, 128)
+    for t in range(8):
+        bufs = [x.copy() for x in g]
+        orc.ring_allreduce_compressed_state(bufs, state, orc.FB_DELTA, mbits=4, unit=1024)
+        errs.append(np.max(np.abs(bufs[0].astype(np.float64) - exact)))
+        for c in range(n):  # the owner's reference is the value every rank stored
+            assert np.array_equal(state[c][c * L:(c + 1) * L], bufs[0][c * L:(c + 1) * L])
+    assert errs[-1] < errs[0] * 1e-3
+    assert all(b <= a for a, b in zip(errs, errs[1:]))
