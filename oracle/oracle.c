@@ -580,6 +580,8 @@ int orc_ring_allreduce_compressed(void* const* bufs, int n, size_t count, int dt
   if (!check_bufs(bufs, n, dt) || !bfp_args_ok(block, mbits)) return ORC_EINVAL;
   if (method != ORC_COMP_BFP && method != ORC_COMP_SPARSE_AUTO) return ORC_EINVAL;
   if (unit == 0 || unit % (size_t)block) return ORC_EINVAL;
+  /* One rank sends nothing, so nothing is compressed: the buffer stays as it is. */
+  if (n == 1) return ORC_OK;
   comp_t cf = {method, block, mbits, dt, theta};
   size_t es = dtype_size(dt);
   size_t L = orc_comp_chunk_len(count, n, block);
@@ -674,6 +676,7 @@ int orc_ring_allreduce_compressed_state(void* const* bufs, float* const* state, 
   if (!check_bufs(bufs, n, dt) || !bfp_args_ok(block, mbits) || !state) return ORC_EINVAL;
   if (feedback != ORC_FB_ERROR && feedback != ORC_FB_DELTA) return ORC_EINVAL;
   if (unit == 0 || unit % (size_t)block) return ORC_EINVAL;
+  if (n == 1) return ORC_OK; /* nothing travels: buffer and state stay as they are */
   size_t es = dtype_size(dt);
   size_t L = orc_comp_chunk_len(count, n, block);
   float* v = (float*)malloc(sizeof(float) * unit);

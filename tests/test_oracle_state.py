@@ -13,7 +13,8 @@ precision lost this round into the next round).  Pinned by:
   * the mean of T error-feedback results on a constant gradient converges
     to the exact sum like 1/T;
   * delta coding on a constant gradient converges to the exact sum, and the
-    owner's reference equals the final value.
+    owner's reference equals the final value;
+  * one rank sends nothing, so nothing is encoded: buffer and state stay.
 """
 import numpy as np
 import pytest
@@ -95,3 +96,16 @@ def test_delta_coding_converges_on_constant_input(orc):
             assert np.array_equal(state[c][c * L:(c + 1) * L], bufs[0][c * L:(c + 1) * L])
     assert errs[-1] < errs[0] * 1e-3
     assert all(b <= a for a, b in zip(errs, errs[1:]))
+
+
+@pytest.mark.parametrize("feedback", [1, 2])
+def test_single_rank_sends_nothing(orc, feedback):
+    x = inputs.block_scaled(1, 5000, salt=3)
+    st = [np.full(5000, 0.25, dtype=np.float32)]
+    b = [x[0].copy()]
+    sent, recv = orc.ring_allreduce_compressed_state(b, st, feedback, unit=1024)
+    assert np.array_equal(b[0].view(np.uint16), x[0].view(np.uint16))
+    assert np.all(st[0] == 0.25) and sent == [0] and recv == [0]
+    c = [x[0].copy()]
+    assert orc.ring_allreduce_compressed(c, unit=1024) == ([0], [0])
+    assert np.array_equal(c[0].view(np.uint16), x[0].view(np.uint16))
