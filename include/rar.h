@@ -243,6 +243,35 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
                                   const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
                                   void* stream);
 
+/* Stateful compression for the fused BFP ring ([P4] section 2.1, the
+ * differential encoding layer; section 5, error feedback as the remedy for
+ * the accuracy loss of lossy compression). */
+typedef enum rar_feedback {
+  RAR_FEEDBACK_ERROR = 1,  /* encode v = p + e; keep e = v - decode(msg) */
+  RAR_FEEDBACK_DELTA = 2   /* encode v = p - ref; ref += decode(msg); the
+                              receiver takes ref, the sender's reconstruction */
+} rar_feedback;
+
+/* rar_ring_allreduce_compressed with per-rank state.  state[r] holds count
+ * binary32 values owned by rank r (device memory, 16-byte aligned, zero
+ * before the first call, kept by the caller between calls; neither the state
+ * buffers nor the rank buffers may overlap).  Each rank encodes each element
+ * exactly once per call: in the reduce-scatter as the sender of its partial,
+ * in the allgather as the owner of its chunk, and that encode reads and
+ * rewrites the rank's state element.  With error feedback the receiver takes
+ * decode(msg); with delta coding it takes the sender's running
+ * reconstruction ref.  In every other respect (order, rounding, message
+ * bytes) the call is the fused BFP ring: with all-zero state and feedback
+ * ERROR its first result equals rar_ring_allreduce_compressed's.
+ * cfg must select RAR_COMP_BFP, RAR_SCHED_FUSED and include
+ * RAR_OP_ALLREDUCE (else RAR_ENOTSUP); the workspace is the one
+ * rar_compressed_workspace_bytes sizes for cfg, and receives the wire byte
+ * counters.  With nranks == 1 nothing travels and nothing is encoded:
+ * buffer and state are left as they are. */
+int rar_ring_allreduce_compressed_state(void* const* bufs, void* const* state, int nranks, size_t count,
+                                        int dtype, int feedback, const rar_compress_cfg* cfg,
+                                        void* workspace, size_t ws_bytes, void* stream);
+
 /* Wire bytes each rank sent and received in the last compressed allreduce
  * that used this workspace.  Synchronises `stream` first. */
 int rar_compressed_traffic(const void* workspace, int nranks, uint64_t* sent, uint64_t* recv,

@@ -11,5 +11,6 @@ from ._binding import (  # noqa: F401
     broadcast_ex, bucket_plan, bucketed_allreduce, bucketed_workspace_bytes, chunk_len, compress_cfg,
     compress_cfg_default, compressed_chunk_len, compressed_traffic, compressed_workspace_bytes, dtype_code,
     last_traffic, lib, reduce_scatter, reduce_scatter_ex, ring_allreduce, ring_allreduce_compressed,
-    ring_allreduce_ex, rs_step, status_string, version,
+    ring_allreduce_ex, rs_step, status_string, version, FEEDBACK_DELTA, FEEDBACK_ERROR,
+    ring_allreduce_compressed_state,
 )

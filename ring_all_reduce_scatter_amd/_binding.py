@@ -19,6 +19,7 @@ ALGO_FUSED, ALGO_STEPWISE = 0, 1
 COMP_NONE, COMP_BFP, COMP_SPARSE_AUTO = 0, 1, 2
 OP_ALLREDUCE, OP_ALLGATHER, OP_BROADCAST = 1, 2, 4
 SCHED_FUSED, SCHED_STAGED = 0, 1
+FEEDBACK_ERROR, FEEDBACK_DELTA = 1, 2
 MAX_RANKS = 64
 
 _c_vp = ctypes.c_void_p
@@ -72,6 +73,8 @@ _SIGS = {
     "rar_compressed_workspace_bytes": (_c_size, [_c_int, _c_size, _c_int, ctypes.POINTER(CompressCfg)]),
     "rar_ring_allreduce_compressed": (_c_int, [_c_vp, _c_int, _c_size, _c_int, ctypes.POINTER(CompressCfg),
                                                _c_vp, _c_size, _c_vp]),
+    "rar_ring_allreduce_compressed_state": (_c_int, [_c_vp, _c_vp, _c_int, _c_size, _c_int, _c_int,
+                                                     ctypes.POINTER(CompressCfg), _c_vp, _c_size, _c_vp]),
     "rar_compressed_traffic": (_c_int, [_c_vp, _c_int, _u64p, _u64p, _c_vp]),
     "rar_bucket_plan": (_c_size, [_c_vp, _c_size, _c_int, _c_size, _c_vp]),
     "rar_bucketed_workspace_bytes": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size]),
@@ -278,6 +281,23 @@ def ring_allreduce_compressed(bufs, cfg: CompressCfg, workspace, stream=None):
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream, bufs[0]))
     _check(rc, "rar_ring_allreduce_compressed")
+
+
+def ring_allreduce_compressed_state(bufs, state, feedback: int, cfg: CompressCfg, workspace, stream=None):
+    """state: one float32 tensor of bufs[0].numel() elements per rank, zero
+    before the first call and kept between calls."""
+    if len(state) != len(bufs):
+        raise ValueError("need one state tensor per rank")
+    for s_ in state:
+        if s_.numel() != bufs[0].numel() or s_.element_size() != 4 or not s_.is_contiguous():
+            raise ValueError("state tensors must be contiguous float32 of the rank buffers' length")
+    rc = lib().rar_ring_allreduce_compressed_state(
+        _rank_ptrs(bufs), (ctypes.c_void_p * len(state))(*[t.data_ptr() for t in state]), len(bufs),
+        bufs[0].numel(), dtype_code(bufs[0]), feedback, ctypes.byref(cfg),
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream, bufs[0]))
+    _check(rc, "rar_ring_allreduce_compressed_state")
 
 
 def compressed_traffic(workspace, nranks: int, stream=None):

@@ -84,6 +84,24 @@ int check_bufs(void* const* bufs, int n, int dt, size_t bytes) {
   return RAR_OK;
 }
 
+// bufs (n buffers of `bytes`) and state (n buffers of `sbytes`): every
+// pointer non-null and 16-byte aligned, no two of the 2n ranges overlapping.
+int check_state_bufs(void* const* bufs, void* const* state, int n, size_t bytes, size_t sbytes) {
+  if (!state) return RAR_EOVERLAP;
+  if (bytes == 0) return RAR_OK;
+  std::vector<std::pair<uintptr_t, size_t>> a;
+  for (int r = 0; r < n; ++r) {
+    if (!state[r]) return RAR_EOVERLAP;
+    if ((uintptr_t)state[r] & 15u) return RAR_EALIGN;
+    a.emplace_back((uintptr_t)bufs[r], bytes);
+    a.emplace_back((uintptr_t)state[r], sbytes);
+  }
+  std::sort(a.begin(), a.end());
+  for (size_t i = 0; i + 1 < a.size(); ++i)
+    if (a[i + 1].first - a[i].first < a[i].second) return RAR_EOVERLAP;
+  return RAR_OK;
+}
+
 RankPtrs make_ptrs(void* const* bufs, int n) {
   RankPtrs p{};
   for (int r = 0; r < n; ++r) p.p[r] = (char*)bufs[r];
@@ -744,6 +762,33 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
     } else {
       if ((rc = staged_bfp(pl, bufs, (char*)workspace, tr, st))) return rc;
     }
+  }
+  return write_traffic(tr, workspace, st);
+}
+
+int rar_ring_allreduce_compressed_state(void* const* bufs, void* const* state, int nranks, size_t count, int dtype,
+                                        int feedback, const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+  const size_t es = es_of(dtype);
+  int rc = check_bufs(bufs, nranks, dtype, count * es);
+  if (rc) return rc;
+  if (feedback != RAR_FEEDBACK_ERROR && feedback != RAR_FEEDBACK_DELTA) return RAR_EINVAL;
+  CompPlan pl{};
+  if ((rc = cfg_check(cfg, dtype, &pl))) return rc;
+  if (cfg->method != RAR_COMP_BFP || cfg->schedule != RAR_SCHED_FUSED || !(cfg->collective_mask & RAR_OP_ALLREDUCE))
+    return RAR_ENOTSUP;
+  if ((rc = check_state_bufs(bufs, state, nranks, count * es, count * sizeof(float)))) return rc;
+  plan_sizes(&pl, nranks, count, dtype);
+  if (!workspace || ws_bytes < workspace_need(pl)) return RAR_EWORKSPACE;
+  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  Traffic tr;
+  tr.reset(nranks);
+  if (nranks > 1 && count > 0) {
+    fused_bfp_traffic(pl, tr);
+    if ((rc = hip_rc(launch_bfp_ring_fold_state(make_ptrs(bufs, nranks), make_ptrs(state, nranks), nranks, count,
+                                                 pl.L, dtype, pl.block, pl.mbits, feedback, st))))
+      return rc;
   }
   return write_traffic(tr, workspace, st);
 }

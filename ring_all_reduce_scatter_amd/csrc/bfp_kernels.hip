@@ -276,6 +276,70 @@ struct U64Vals {
   uint64_t v[kFillWords];
 };
 
+// ---------------------------------------------------------------- stateful fused ring
+// Error feedback (FB = 1) or delta coding (FB = 2) on the fused compressed
+// ring ("CCCL..." page, section 2.1 differential layer, section 5 error
+// feedback).  Each rank encodes each of its elements once per allreduce, so
+// rank r keeps one binary32 state value per element (st.p[r]):
+//   error feedback: v = p + e, send E(v), e <- v - D(E(v)), receiver gets D
+//   delta:          v = p - ref, send E(v), ref <- ref + D(E(v)) = value the
+//                   receiver gets
+// The hop chain of a block is the one of bfp_ring_fold_kernel with v in place
+// of p at every encode, in binary32.
+template <int DT, int NR, int LPB, int FB>
+__global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs bufs, RankPtrs st, int nranks,
+                                                                        uint64_t count, uint64_t L, int lpb_rt,
+                                                                        int mbits) {
+  const int N = NR > 0 ? NR : nranks;
+  const int lpb = LPB > 0 ? LPB : lpb_rt;
+  const uint32_t c = blockIdx.x % (uint32_t)N;
+  const uint32_t t = blockIdx.x / (uint32_t)N;
+  const uint64_t lo = (uint64_t)c * L;
+  if (lo >= count) return;
+  const uint64_t hi = lo + L < count ? lo + L : count;
+  const uint64_t tile0 = lo + (uint64_t)t * kThreads * kGroupElems;
+  if (tile0 >= hi) return;
+  const uint64_t e = tile0 + (uint64_t)threadIdx.x * kGroupElems;
+  const int nv = e >= hi ? 0 : (hi - e >= 8 ? 8 : (int)(hi - e));
+  const float qmax = (float)((1 << (mbits - 1)) - 1);
+  // v from the sender's value and state; returns what the receiver takes and
+  // updates the sender's state
+  auto message = [&](const G8& p, int sender) -> G8 {
+    G8 s = load_part8<DT_F32>(st.p[sender], e, nv), v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v.v[i] = FB == 1 ? p.v[i] + s.v[i] : p.v[i] - s.v[i];
+    const uint32_t m = group_max_sel<LPB>(lane_absmax(v), lpb);
+    const G8 d = qdq8(v, bfp_scale(m, mbits), qmax);
+    G8 out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (FB == 1) {
+        s.v[i] = v.v[i] - d.v[i];
+        out.v[i] = d.v[i];
+      } else {
+        s.v[i] = s.v[i] + d.v[i];
+        out.v[i] = s.v[i];
+      }
+    }
+    if (nv == 8) store_raw8<DT_F32, false>(st.p[sender], e, pack8<DT_F32>(s));
+    else store_part8<DT_F32>(st.p[sender], e, nv, s);
+    return out;
+  };
+  const int first = (int)c + 1 < N ? (int)c + 1 : 0;
+  G8 p = load_group<DT>(bufs.p[first], e, nv);
+  int r = first;
+  for (int k = 2; k <= N; ++k) {
+    const int sender = r;
+    r = r + 1 == N ? 0 : r + 1;
+    const G8 x = load_group<DT>(bufs.p[r], e, nv);
+    const G8 d = message(p, sender);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p.v[i] = round_to<DT>(x.v[i] + d.v[i]);
+  }
+  const G8 y = message(p, (int)c);
+  for (int d = 0; d < N; ++d) store_group<DT>(bufs.p[d], e, nv, y);
+}
+
 __global__ void fill_u64_kernel(uint64_t* dst, int n, U64Vals vals) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = vals.v[i];
 }
@@ -337,6 +401,20 @@ void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, i
                       hipStream_t stream) {
   if (n == 8) fold_dispatch_lpb<DT, 8>(bufs, n, count, L, block, mbits, stream);
   else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, stream);
+}
+
+template <int DT, int FB>
+void fold_state_dispatch(const RankPtrs& bufs, const RankPtrs& st, int n, uint64_t count, uint64_t L, int block,
+                         int mbits, hipStream_t stream) {
+  const uint64_t tile = (uint64_t)kThreads * kGroupElems;
+  const uint64_t tiles = (L + tile - 1) / tile;
+  dim3 grid((unsigned)((uint64_t)n * tiles));
+  if (block == 128)
+    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, 0, 16, FB>), grid, dim3(kThreads), 0, stream, bufs, st, n,
+                       count, L, 16, mbits);
+  else
+    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, 0, 0, FB>), grid, dim3(kThreads), 0, stream, bufs, st, n,
+                       count, L, block / 8, mbits);
 }
 
 }  // namespace
@@ -405,6 +483,21 @@ hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uin
     case DT_F16: fold_dispatch_nr<DT_F16>(bufs, n, count, L, block, mbits, stream); break;
     default: fold_dispatch_nr<DT_BF16>(bufs, n, count, L, block, mbits, stream); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bfp_ring_fold_state(const RankPtrs& bufs, const RankPtrs& state, int n, uint64_t count, uint64_t L,
+                                      int dt, int block, int mbits, int feedback, hipStream_t stream) {
+  if (L == 0 || count == 0) return hipSuccess;
+#define RAR_FS(DTV)                                                                         \
+  if (feedback == 1) fold_state_dispatch<DTV, 1>(bufs, state, n, count, L, block, mbits, stream); \
+  else fold_state_dispatch<DTV, 2>(bufs, state, n, count, L, block, mbits, stream);
+  switch (dt) {
+    case DT_F32: RAR_FS(DT_F32) break;
+    case DT_F16: RAR_FS(DT_F16) break;
+    default: RAR_FS(DT_BF16) break;
+  }
+#undef RAR_FS
   return hipGetLastError();
 }
 

@@ -131,6 +131,11 @@ uint64_t bucket_fold_tile_elems(int dt);
 hipError_t launch_bucket_fold(const uint64_t* dev_table, int n, uint64_t ntensors, uint64_t grid, int dt,
                               hipStream_t stream);
 
+// Fused compressed ring with per-rank binary32 state (feedback 1 = error
+// feedback, 2 = delta coding); state.p[r] holds count floats.
+hipError_t launch_bfp_ring_fold_state(const RankPtrs& bufs, const RankPtrs& state, int n, uint64_t count, uint64_t L,
+                                      int dt, int block, int mbits, int feedback, hipStream_t stream);
+
 // Writes nvals host values into device memory, stream-ordered: the values
 // travel as kernel arguments (3.5 KiB per launch), so the host array may be
 // reused as soon as the call returns.

@@ -161,3 +161,29 @@ def test_traffic_of_noop_allreduce_follows_byte_table():
     base = 1 << 40
     rar.ring_allreduce(_fake([base, base + 65536, base + 131072], numel=0), stream=0)
     assert rar.last_traffic(3) == ([0, 0, 0], [0, 0, 0])
+
+
+def test_stateful_compressed_argument_errors():
+    """Checks of rar_ring_allreduce_compressed_state that end before any launch."""
+    base = 1 << 40
+    lib = rar.lib()
+    bufs = (ctypes.c_void_p * 2)(base, base + (1 << 20))
+    state = (ctypes.c_void_p * 2)(base + (2 << 20), base + (3 << 20))
+    ws = base + (8 << 20)
+    count = 4096
+
+    def call(st=state, fb=rar.FEEDBACK_ERROR, cfg=None, wsb=1 << 16):
+        cfg = cfg if cfg is not None else rar.compress_cfg()
+        return lib.rar_ring_allreduce_compressed_state(bufs, st, 2, count, rar.F16, fb, ctypes.byref(cfg), ws, wsb,
+                                                       None)
+
+    assert call(fb=0) == 1 and call(fb=3) == 1
+    assert call(cfg=rar.compress_cfg(schedule=rar.SCHED_STAGED)) == 6
+    assert call(cfg=rar.compress_cfg(method=rar.COMP_SPARSE_AUTO)) == 6
+    assert call(cfg=rar.compress_cfg(collective_mask=rar.OP_ALLGATHER)) == 6
+    assert call(cfg=rar.compress_cfg(mbits=9)) == 1
+    assert call(st=(ctypes.c_void_p * 2)(base + (2 << 20), base + 4096)) == 7  # state inside rank 0's buffer
+    assert call(st=(ctypes.c_void_p * 2)(base + (2 << 20), base + (2 << 20) + 8192)) == 7  # 16 KiB states overlap
+    assert call(st=(ctypes.c_void_p * 2)(base + (2 << 20), base + (3 << 20) + 4)) == 3
+    assert call(st=(ctypes.c_void_p * 2)(base + (2 << 20), None)) == 7
+    assert call(wsb=64) == 4

@@ -113,7 +113,7 @@ def _run_compressed(xs, dt, sched, block=128, mbits=8, unit_elems=4096, method=r
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("sched", ["fused", "staged"])
 @pytest.mark.parametrize("mbits", [8, 4])
 def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):

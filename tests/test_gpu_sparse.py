@@ -28,7 +28,7 @@ def _run_auto(xs, dt, mbits=4, unit_elems=4096, theta=0.5, block=128):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("mbits", [4, 8])
 def test_sparse_auto_matches_oracle(dt, n, mbits):
     count = n * 4096 * 3 + 2500  # several units and tiles per chunk, ragged last chunk
