@@ -319,7 +319,20 @@ def extra_legs(args):
     Sb = wb["count"] * 2
     out["bfp8_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
                                     "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del sets, pristine, ws
+    del ws
+    # the same fused ring with per-rank error-feedback state (state read and
+    # rewritten once per element per rank: 8 more bytes per element per rank)
+    cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"], schedule=rar.SCHED_FUSED)
+    ws = torch.empty(rar.compressed_workspace_bytes(wb["n"], wb["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    state = [torch.zeros(wb["count"], dtype=torch.float32, device="cuda:0") for _ in range(wb["n"])]
+    for nm, fb in (("bfp8_allreduce_fused_error_feedback", rar.FEEDBACK_ERROR),
+                   ("bfp8_allreduce_fused_delta", rar.FEEDBACK_DELTA)):
+        ms, k, _ = time_leg(lambda b: rar.ring_allreduce_compressed_state(b, state, fb, cfg, ws), sets, 2, steps)
+        moved = 2 * wb["n"] * Sb + 2 * wb["n"] * wb["count"] * 4
+        out[nm] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
+                   "frac_of_roofline": round(moved / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, pristine, ws, state
     torch.cuda.empty_cache()
     w5 = inputs.WORKLOADS["sparse_bfp4"]
     xsp = inputs.sparse_mix(w5["n"], w5["count"])

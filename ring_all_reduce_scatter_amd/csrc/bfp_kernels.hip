@@ -302,15 +302,24 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs 
   const uint64_t e = tile0 + (uint64_t)threadIdx.x * kGroupElems;
   const int nv = e >= hi ? 0 : (hi - e >= 8 ? 8 : (int)(hi - e));
   const float qmax = (float)((1 << (mbits - 1)) - 1);
-  // v from the sender's value and state; returns what the receiver takes and
-  // updates the sender's state
-  auto message = [&](const G8& p, int sender) -> G8 {
-    G8 s = load_part8<DT_F32>(st.p[sender], e, nv), v;
+  auto ld = [&](int rank) -> G8 {
+    return nv == 8 ? unpack8<DT>(load_raw8<DT, true>(bufs.p[rank], e)) : load_part8<DT>(bufs.p[rank], e, nv);
+  };
+  auto ld_state = [&](int rank) -> G8 {
+    return nv == 8 ? unpack8<DT_F32>(load_raw8<DT_F32, true>(st.p[rank], e)) : load_part8<DT_F32>(st.p[rank], e, nv);
+  };
+  auto st_state = [&](int rank, const G8& s) {
+    if (nv == 8) store_raw8<DT_F32, true>(st.p[rank], e, pack8<DT_F32>(s));
+    else store_part8<DT_F32>(st.p[rank], e, nv, s);
+  };
+  // Encode v = p +- s, update the sender's state s in place, return what the
+  // receiver takes.
+  auto message = [&](const G8& p, G8& s) -> G8 {
+    G8 v, out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v.v[i] = FB == 1 ? p.v[i] + s.v[i] : p.v[i] - s.v[i];
     const uint32_t m = group_max_sel<LPB>(lane_absmax(v), lpb);
     const G8 d = qdq8(v, bfp_scale(m, mbits), qmax);
-    G8 out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (FB == 1) {
@@ -321,23 +330,54 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs 
         out.v[i] = s.v[i];
       }
     }
-    if (nv == 8) store_raw8<DT_F32, false>(st.p[sender], e, pack8<DT_F32>(s));
-    else store_part8<DT_F32>(st.p[sender], e, nv, s);
     return out;
   };
+  // ring order of chunk c: ranks c+1, ..., c+N-1 send their partials in the
+  // reduce-scatter, c is the receiver of the last hop and the allgather owner
   const int first = (int)c + 1 < N ? (int)c + 1 : 0;
-  G8 p = load_group<DT>(bufs.p[first], e, nv);
-  int r = first;
-  for (int k = 2; k <= N; ++k) {
-    const int sender = r;
-    r = r + 1 == N ? 0 : r + 1;
-    const G8 x = load_group<DT>(bufs.p[r], e, nv);
-    const G8 d = message(p, sender);
+  if constexpr (NR > 0) {
+    // every load issued before the chain (the state writes cannot alias them)
+    // (16-bit inputs stay packed until their hop: half the registers)
+    Raw8<DT> x[NR];
+    G8 s[NR];
+    auto rank_of = [&](int j) { return first + j < NR ? first + j : first + j - NR; };
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p.v[i] = round_to<DT>(x.v[i] + d.v[i]);
+    for (int j = 0; j < NR; ++j) {
+      const int q = rank_of(j);
+      x[j] = nv == 8 ? load_raw8<DT, true>(bufs.p[q], e) : pack8<DT>(load_part8<DT>(bufs.p[q], e, nv));
+      s[j] = ld_state(q);
+    }
+    G8 p = unpack8<DT>(x[0]);
+#pragma unroll
+    for (int j = 1; j < NR; ++j) {
+      const G8 d = message(p, s[j - 1]);
+      st_state(rank_of(j - 1), s[j - 1]);
+      const G8 xj = unpack8<DT>(x[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p.v[i] = round_to<DT>(xj.v[i] + d.v[i]);
+    }
+    const G8 y = message(p, s[NR - 1]);
+    st_state(rank_of(NR - 1), s[NR - 1]);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) store_group<DT>(bufs.p[j], e, nv, y);
+  } else {
+    G8 p = ld(first);
+    int r = first;
+    for (int k = 2; k <= N; ++k) {
+      const int sender = r;
+      r = r + 1 == N ? 0 : r + 1;
+      const G8 x = ld(r);
+      G8 s = ld_state(sender);
+      const G8 d = message(p, s);
+      st_state(sender, s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p.v[i] = round_to<DT>(x.v[i] + d.v[i]);
+    }
+    G8 s = ld_state((int)c);
+    const G8 y = message(p, s);
+    st_state((int)c, s);
+    for (int d = 0; d < N; ++d) store_group<DT>(bufs.p[d], e, nv, y);
   }
-  const G8 y = message(p, (int)c);
-  for (int d = 0; d < N; ++d) store_group<DT>(bufs.p[d], e, nv, y);
 }
 
 __global__ void fill_u64_kernel(uint64_t* dst, int n, U64Vals vals) {
@@ -403,18 +443,33 @@ void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, i
   else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, stream);
 }
 
-template <int DT, int FB>
-void fold_state_dispatch(const RankPtrs& bufs, const RankPtrs& st, int n, uint64_t count, uint64_t L, int block,
-                         int mbits, hipStream_t stream) {
+// Workgroups per CU of the stateful fold.  Each lane holds N inputs and N
+// state groups in flight (N = 8, fp16: 384 bytes); two workgroups per CU
+// measured best on MI355X (2.47 ms vs 2.60 uncapped and 2.52 at three for
+// N = 8, 128M fp16 with 128M-float state per rank).
+int state_fold_wgs_per_cu() { return 2; }
+
+template <int DT, int NR, int FB>
+void fold_state_dispatch_nr(const RankPtrs& bufs, const RankPtrs& st, int n, uint64_t count, uint64_t L, int block,
+                            int mbits, hipStream_t stream) {
   const uint64_t tile = (uint64_t)kThreads * kGroupElems;
   const uint64_t tiles = (L + tile - 1) / tile;
   dim3 grid((unsigned)((uint64_t)n * tiles));
+  const size_t lds = residency_lds(state_fold_wgs_per_cu());
   if (block == 128)
-    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, 0, 16, FB>), grid, dim3(kThreads), 0, stream, bufs, st, n,
-                       count, L, 16, mbits);
+    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, NR, 16, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
+                       n, count, L, 16, mbits);
   else
-    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, 0, 0, FB>), grid, dim3(kThreads), 0, stream, bufs, st, n,
-                       count, L, block / 8, mbits);
+    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, NR, 0, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
+                       n, count, L, block / 8, mbits);
+}
+
+template <int DT, int FB>
+void fold_state_dispatch(const RankPtrs& bufs, const RankPtrs& st, int n, uint64_t count, uint64_t L, int block,
+                         int mbits, hipStream_t stream) {
+  if (n == 8) fold_state_dispatch_nr<DT, 8, FB>(bufs, st, n, count, L, block, mbits, stream);
+  else if (n == 4) fold_state_dispatch_nr<DT, 4, FB>(bufs, st, n, count, L, block, mbits, stream);
+  else fold_state_dispatch_nr<DT, 0, FB>(bufs, st, n, count, L, block, mbits, stream);
 }
 
 }  // namespace

@@ -82,8 +82,54 @@ def test_stateful_rejects_unsupported_configs():
         with pytest.raises(rar.RarError) as e:
             rar.ring_allreduce_compressed_state(bufs, st, rar.FEEDBACK_ERROR, cfg, ws)
         assert e.value.status == 6
-    with pytest.raises(rar.RarError) as e:
+    with pytest.raises(rar.RarError) as e:  # two ranks sharing one state buffer
+        rar.ring_allreduce_compressed_state(bufs, [st[0], st[0]], rar.FEEDBACK_ERROR, rar.compress_cfg(), ws)
+    assert e.value.status == 7
+    with pytest.raises(ValueError):  # state must be float32
         rar.ring_allreduce_compressed_state(bufs, [st[0], bufs[1]], rar.FEEDBACK_ERROR, rar.compress_cfg(), ws)
     with pytest.raises(rar.RarError) as e:
         rar.ring_allreduce_compressed_state(bufs, st, 0, rar.compress_cfg(), ws)
     assert e.value.status == 1
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fb", ["error", "delta"])
+def test_stateful_bfp8_workload_full_size_sampled(fb):
+    """N=8, T=128M fp16 per rank, 128-element blocks, 8-bit mantissas, with
+    128M-float state per rank: two calls of the launch the benchmark times.
+    Every block's chain depends only on its N inputs and N state blocks and
+    its chunk's ring order, so sampled blocks are re-run in a small ring where
+    each keeps its chunk index; result and every rank's state must match."""
+    w = inputs.WORKLOADS["bfp8"]
+    n, count, mbits = w["n"], w["count"], w["mbits"]
+    xs = inputs.block_scaled(n, count)
+    cfg = rar.compress_cfg(mbits=mbits, unit_bytes=w["unit_bytes"])
+    ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
+    st = [torch.zeros(count, dtype=torch.float32, device="cuda:0") for _ in range(n)]
+    bufs = None
+    for _ in range(2):
+        bufs = to_dev(xs, "f16")
+        rar.ring_allreduce_compressed_state(bufs, st, FB[fb][0], cfg, ws)
+    for r in range(1, n):
+        assert torch.equal(bufs[r].view(torch.int16), bufs[0].view(torch.int16)), f"rank {r} differs"
+    L = rar.compressed_chunk_len(count, n, 128)
+    K = 64
+    g = np.random.default_rng(7)
+    picks = []
+    for c in range(n):
+        nblk = (min((c + 1) * L, count) - c * L) // 128
+        picks.append(np.sort(g.choice(nblk, size=K, replace=False)) + c * L // 128)
+    elems = np.concatenate([np.arange(b * 128, (b + 1) * 128) for c in range(n) for b in picks[c]])
+    idx = torch.from_numpy(elems).to("cuda:0")
+    got = bufs[0][idx].cpu().numpy()
+    got_st = [s[idx].cpu().numpy() for s in st]
+    del bufs, st
+    mini_x = [x[elems].copy() for x in xs]
+    mini_st = [np.zeros(elems.size, dtype=np.float32) for _ in range(n)]
+    mini = None
+    for _ in range(2):
+        mini = [m.copy() for m in mini_x]
+        oracle.ring_allreduce_compressed_state(mini, mini_st, FB[fb][1], mbits=mbits, unit=K * 128)
+    assert_bits_equal(got, mini[0], "sampled blocks, result")
+    for r in range(n):
+        assert_bits_equal(got_st[r], mini_st[r], f"sampled blocks, rank {r} state")
