@@ -29,6 +29,13 @@ Parity status of each function (what pins it is in the tests under
                                     converging on constant inputs)
   tree allreduce .................. pinned (exact integer sums, hand-written
                                     balanced-tree expressions, byte counts)
+  hash64 / shared-state sync ...... pinned (published splitmix64 outputs,
+                                    sensitivity to every bit, position and
+                                    length; hand-worked majority cases)
+  fault-injected ring ............. pinned (no fault = plain ring; survivors'
+                                    result = a fresh ring over the survivors;
+                                    exact integer sums; hand-worked attempts
+                                    and byte counts; failed ranks restored)
 """
 import ctypes
 import os
@@ -91,6 +98,11 @@ def _load():
             _u64p, _u64p]),
         "orc_tree_reduce_round": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int]),
         "orc_tree_allreduce": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, _u64p, _u64p]),
+        "orc_mix64": (ctypes.c_uint64, [ctypes.c_uint64]),
+        "orc_hash64": (ctypes.c_uint64, [_c_vp, _c_size]),
+        "orc_shared_state_sync": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, _u64p, _u64p, _u64p]),
+        "orc_ring_allreduce_ft": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, _c_vp, _c_vp,
+                                                 ctypes.c_int, _c_vp, _c_vp, _c_vp, _u64p, _u64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -343,3 +355,53 @@ def bucketed_allreduce(tensors, cap_bytes, dt=None):
     _check(lib().orc_bucketed_allreduce(_ptrs(flat), counts.ctypes.data, nt, n, dt, cap_bytes, sent, recv),
            "bucketed_allreduce")
     return list(sent), list(recv)
+
+
+# ---------------------------------------------------------------- shared state and faults
+
+EABORT = 2
+
+
+def mix64(z):
+    return int(lib().orc_mix64(z & 0xFFFFFFFFFFFFFFFF))
+
+
+def hash64(a):
+    a = np.ascontiguousarray(a)
+    return int(lib().orc_hash64(a.ctypes.data, a.nbytes))
+
+
+def shared_state_sync(bufs):
+    """Majority-hash check over the rank buffers (numpy, same byte size);
+    diverged ranks receive the majority buffer in place.  Returns
+    (resent, hashes, sent, recv)."""
+    n = len(bufs)
+    nbytes = bufs[0].nbytes
+    if any(b.nbytes != nbytes for b in bufs):
+        raise ValueError("rank buffers must have one byte size")
+    hashes = (ctypes.c_uint64 * n)()
+    sent, recv = _traffic(n)
+    resent = lib().orc_shared_state_sync(_ptrs(bufs), n, nbytes, hashes, sent, recv)
+    if resent < 0:
+        raise ValueError("oracle shared_state_sync rejected its arguments")
+    return resent, list(hashes), list(sent), list(recv)
+
+
+def ring_allreduce_ft(bufs, faults=(), dt=None):
+    """Ring allreduce with injected faults [(rank, step), ...] (see
+    orc_ring_allreduce_ft).  Returns a dict with status, attempts,
+    dead_attempt, dead_step, survivors, sent, recv."""
+    dt = _dt_of(bufs[0], dt)
+    n = len(bufs)
+    fr = np.ascontiguousarray(np.array([f[0] for f in faults] or [0], dtype=np.int32))
+    fs = np.ascontiguousarray(np.array([f[1] for f in faults] or [1], dtype=np.int32))
+    da = np.zeros(n, dtype=np.int32)
+    ds = np.zeros(n, dtype=np.int32)
+    att = np.zeros(1, dtype=np.int32)
+    sent, recv = _traffic(n)
+    rc = lib().orc_ring_allreduce_ft(_ptrs(bufs), n, bufs[0].size, dt, fr.ctypes.data, fs.ctypes.data, len(faults),
+                                     att.ctypes.data, da.ctypes.data, ds.ctypes.data, sent, recv)
+    if rc not in (0, EABORT):
+        raise ValueError(f"oracle ring_allreduce_ft rejected its arguments (status {rc})")
+    return {"status": rc, "attempts": int(att[0]), "dead_attempt": da.tolist(), "dead_step": ds.tolist(),
+            "survivors": [r for r in range(n) if da[r] == 0], "sent": list(sent), "recv": list(recv)}

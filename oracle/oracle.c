@@ -800,3 +800,155 @@ int orc_fpenv_ok(void) {
   return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------ */
+/* Shared-state hash and fault injection on the simulated ring.         */
+/* [P1] "Prime Intellect 发布 PCCL 分布式训练通信库", section "PCCL 模型"   */
+/* (the PCCL model): peers keep a shared state that is checked by hash  */
+/* and re-sent to a peer whose hash differs from the majority; a        */
+/* collective interrupted by a failing peer is retried on the remaining */
+/* peers.                                                               */
+/* ------------------------------------------------------------------ */
+
+/* Output function of the splitmix64 generator (Steele, Lea and Flood,
+ * "Fast splittable pseudorandom number generators", OOPSLA 2014; the
+ * constants of Vigna's public-domain splitmix64). */
+static uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+#define ORC_GOLDEN 0x9E3779B97F4A7C15ull
+
+uint64_t orc_mix64(uint64_t z) { return mix64(z); }
+
+/* 64-bit hash of nbytes bytes (a reading: the pages name a hash of the
+ * shared state, not which one).  The bytes are read as little-endian 64-bit
+ * words w_0 .. w_{W-1}, the last one zero-padded;
+ *   h = sum over i of mix64(w_i + (i+1) * GOLDEN)   (mod 2^64)
+ *   H = mix64(h xor nbytes). */
+uint64_t orc_hash64(const void* buf, size_t nbytes) {
+  const uint8_t* b = (const uint8_t*)buf;
+  uint64_t h = 0;
+  size_t words = (nbytes + 7) / 8;
+  for (size_t i = 0; i < words; ++i) {
+    uint64_t w = 0;
+    for (int k = 0; k < 8; ++k) {
+      size_t j = i * 8 + (size_t)k;
+      if (j < nbytes) w |= (uint64_t)b[j] << (8 * k);
+    }
+    h += mix64(w + (uint64_t)(i + 1) * ORC_GOLDEN);
+  }
+  return mix64(h ^ (uint64_t)nbytes);
+}
+
+/* Shared-state check: hash every rank's buffer; the majority hash is the one
+ * held by the most ranks (a tie goes to the hash of the lowest rank among
+ * the tied ones); the lowest rank holding it sends its buffer to every rank
+ * whose hash differs.  Returns the number of ranks re-sent, -1 on bad args. */
+int orc_shared_state_sync(void* const* bufs, int n, size_t nbytes, uint64_t* hashes, uint64_t* sent,
+                          uint64_t* recv) {
+  if (n < 1 || n > ORC_MAXN || !bufs) return -1;
+  uint64_t h[ORC_MAXN];
+  for (int r = 0; r < n; ++r) {
+    h[r] = orc_hash64(bufs[r], nbytes);
+    if (hashes) hashes[r] = h[r];
+  }
+  int src = 0, best = 0;
+  for (int r = 0; r < n; ++r) {
+    int votes = 0;
+    for (int q = 0; q < n; ++q) votes += h[q] == h[r];
+    if (votes > best) {
+      best = votes;
+      src = r;
+    }
+  }
+  int resent = 0;
+  for (int r = 0; r < n; ++r) {
+    if (h[r] == h[src]) continue;
+    memcpy(bufs[r], bufs[src], nbytes);
+    add_traffic(sent, recv, src, r, (uint64_t)nbytes);
+    ++resent;
+  }
+  return resent;
+}
+
+enum { ORC_EABORT = 2 };
+
+/* Ring allreduce with injected faults.  Fault i says: rank fault_rank[i]
+ * stops before step fault_step[i] (steps counted 1 .. 2(M-1) within one
+ * pass over M members: reduce-scatter steps first, then allgather steps).
+ * Before each step the members are checked; a fault fires the first time a
+ * pass reaches its step while its rank is still a member.  A pass that
+ * meets a fired fault is abandoned: every rank's buffer is restored from the
+ * snapshot taken on entry, the failed ranks leave the ring, and a new pass
+ * starts over the survivors (ascending rank order, the ring closing over the
+ * gaps, chunk length from the survivor count).  Bytes of abandoned steps
+ * count in the traffic.  Out: attempts = passes started; dead_attempt[r] /
+ * dead_step[r] = pass and step at which rank r was found failed (0 = never).
+ * Returns ORC_OK when a pass completed, ORC_EABORT when no rank is left
+ * (buffers restored). */
+int orc_ring_allreduce_ft(void* const* bufs, int n, size_t count, int dt, const int* fault_rank,
+                          const int* fault_step, int nfaults, int* attempts, int* dead_attempt, int* dead_step,
+                          uint64_t* sent, uint64_t* recv) {
+  if (!check_bufs(bufs, n, dt) || nfaults < 0 || (nfaults && (!fault_rank || !fault_step))) return ORC_EINVAL;
+  for (int i = 0; i < nfaults; ++i)
+    if (fault_rank[i] < 0 || fault_rank[i] >= n || fault_step[i] < 1) return ORC_EINVAL;
+  size_t bytes = count * dtype_size(dt);
+  void* snap[ORC_MAXN];
+  for (int r = 0; r < n; ++r) {
+    snap[r] = malloc(bytes + 1);
+    memcpy(snap[r], bufs[r], bytes);
+  }
+  int alive[ORC_MAXN], fired[256];
+  for (int r = 0; r < n; ++r) {
+    alive[r] = 1;
+    dead_attempt[r] = dead_step[r] = 0;
+  }
+  for (int i = 0; i < nfaults && i < 256; ++i) fired[i] = 0;
+  int attempt = 0, rc = ORC_OK;
+  for (;;) {
+    ++attempt;
+    int members[ORC_MAXN], m = 0;
+    void* sub[ORC_MAXN];
+    for (int r = 0; r < n; ++r)
+      if (alive[r]) {
+        members[m] = r;
+        sub[m++] = bufs[r];
+      }
+    if (m == 0) {
+      rc = ORC_EABORT;
+      break;
+    }
+    size_t L = orc_chunk_len(count, m, 128);
+    int aborted = 0;
+    for (int g = 1; g <= 2 * (m - 1) && !aborted; ++g) {
+      for (int i = 0; i < nfaults; ++i) {
+        if (fired[i] || fault_step[i] != g) continue;
+        fired[i] = 1;
+        int k = fault_rank[i];
+        if (!alive[k]) continue;
+        alive[k] = 0;
+        dead_attempt[k] = attempt;
+        dead_step[k] = g;
+        aborted = 1;
+      }
+      if (aborted) break;
+      uint64_t ps[ORC_MAXN] = {0}, pr[ORC_MAXN] = {0};
+      if (g <= m - 1) rs_step_L(sub, m, count, dt, g, L, ps, pr);
+      else ag_step_L(sub, m, count, dt, g - (m - 1), L, ps, pr);
+      for (int j = 0; j < m; ++j) {
+        if (sent) sent[members[j]] += ps[j];
+        if (recv) recv[members[j]] += pr[j];
+      }
+    }
+    if (!aborted) break;
+    for (int r = 0; r < n; ++r) memcpy(bufs[r], snap[r], bytes);
+  }
+  if (rc == ORC_EABORT)
+    for (int r = 0; r < n; ++r) memcpy(bufs[r], snap[r], bytes);
+  *attempts = attempt;
+  for (int r = 0; r < n; ++r) free(snap[r]);
+  return rc;
+}

@@ -1,0 +1,176 @@
+"""Pins for the oracle's shared-state hash, majority re-send and
+fault-injected ring allreduce (CPU only).
+
+Page "Prime Intellect 发布 PCCL 分布式训练通信库", section "PCCL 模型": the
+shared state is synchronised by hash (a peer whose hash leaves the majority
+gets the state again), and a collective interrupted by a failing peer is
+retried on the peers that remain.  Pinned by:
+  * the mixing function reproduces published splitmix64 outputs (seed 0);
+  * the hash changes with any single bit, with word order and with length;
+  * majority re-send on hand-worked cases (ties to the lowest rank);
+  * no fault: the ring allreduce itself, bit for bit and byte for byte;
+  * after faults: the survivors hold a fresh ring allreduce over the
+    survivors' inputs, failed ranks hold their inputs, integer inputs give
+    the exact survivor sum, attempts and byte counts as worked out by hand.
+"""
+import numpy as np
+import pytest
+
+from ring_all_reduce_scatter_amd import inputs
+
+GOLDEN = 0x9E3779B97F4A7C15
+M64 = (1 << 64) - 1
+
+
+def test_mix64_reproduces_published_splitmix64_outputs(orc):
+    # splitmix64 seeded with 0: the state advances by GOLDEN before each output
+    assert orc.mix64(GOLDEN) == 0xE220A8397B1DCDAF
+    assert orc.mix64(2 * GOLDEN & M64) == 0x6E789E6AA1B965F4
+    assert orc.mix64(3 * GOLDEN & M64) == 0x06C45D188009454F
+    assert orc.mix64(0) == 0
+
+
+def test_hash_of_small_buffers_by_hand(orc):
+    assert orc.hash64(np.zeros(0, dtype=np.uint8)) == orc.mix64(0)
+    # one zero word: h = mix64(0 + 1*GOLDEN), then mixed with the length 8
+    assert orc.hash64(np.zeros(8, dtype=np.uint8)) == orc.mix64(0xE220A8397B1DCDAF ^ 8)
+    # three bytes 1,2,3 -> one word 0x030201 zero-padded
+    h = orc.mix64((0x030201 + GOLDEN) & M64)
+    assert orc.hash64(np.array([1, 2, 3], dtype=np.uint8)) == orc.mix64(h ^ 3)
+
+
+def test_hash_sees_every_bit_position_and_length(orc):
+    g = np.random.default_rng(4)
+    x = g.integers(0, 256, size=4099, dtype=np.uint8)
+    h0 = orc.hash64(x)
+    assert orc.hash64(x.copy()) == h0
+    for pos in g.choice(x.size, size=300, replace=False):
+        y = x.copy()
+        y[pos] ^= np.uint8(1 << int(g.integers(0, 8)))
+        assert orc.hash64(y) != h0, pos
+    w = x[:4096].view(np.uint64).copy()
+    w[[3, 77]] = w[[77, 3]]
+    assert orc.hash64(w) != orc.hash64(x[:4096])  # word order matters
+    assert orc.hash64(np.concatenate([x, [0]]).astype(np.uint8)) != h0  # trailing zero byte
+    f = np.array([0.0], dtype=np.float32)
+    assert orc.hash64(f) != orc.hash64(-f)  # +0 and -0 differ as bytes
+
+
+def test_shared_state_sync_majority(orc):
+    base = inputs.filler(1, 1000, salt=2)[0]
+    bufs = [base.copy() for _ in range(5)]
+    bufs[1][7] += 1.0
+    bufs[4][999] = -bufs[4][999]
+    resent, hashes, sent, recv = orc.shared_state_sync(bufs)
+    assert resent == 2
+    assert len(set(orc.hash64(b) for b in bufs)) == 1
+    assert np.array_equal(bufs[1], base) and np.array_equal(bufs[4], base)
+    assert sent == [8000, 0, 0, 0, 0] and recv == [0, 4000, 0, 0, 4000]
+    assert hashes[0] == hashes[2] == hashes[3] != hashes[1]
+    # 2 against 2 against 1: the tie goes to the lowest rank's hash
+    a, b, c = (inputs.filler(1, 64, salt=s)[0] for s in (10, 11, 12))
+    bufs = [b.copy(), a.copy(), b.copy(), a.copy(), c.copy()]
+    resent, _, sent, _ = orc.shared_state_sync(bufs)
+    assert resent == 3 and all(np.array_equal(x, b) for x in bufs) and sent[0] == 3 * 256
+    # all equal: nothing moves
+    assert orc.shared_state_sync([a.copy(), a.copy()])[0] == 0
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+def test_ft_without_faults_is_the_ring(orc, dt, n):
+    xs = inputs.gradient_like(n, 3000, dtype=dt, salt=n)
+    a = [x.copy() for x in xs]
+    b = [x.copy() for x in xs]
+    sa, ra = orc.ring_allreduce(a)
+    rep = orc.ring_allreduce_ft(b, [])
+    assert rep["status"] == 0 and rep["attempts"] == 1 and rep["survivors"] == list(range(n))
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    assert rep["sent"] == sa and rep["recv"] == ra
+
+
+@pytest.mark.parametrize("faults", [[(2, 1)], [(0, 5)], [(7, 14)], [(3, 9), (5, 2)], [(1, 1), (6, 1)],
+                                    [(4, 3), (4, 1), (2, 20)]])
+def test_ft_survivors_hold_a_fresh_ring_over_survivors(orc, faults):
+    n, count = 8, 5000
+    xs = inputs.gradient_like(n, count, salt=len(faults))
+    bufs = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(bufs, faults)
+    surv = rep["survivors"]
+    ref = [xs[r].copy() for r in surv]
+    orc.ring_allreduce(ref)
+    for j, r in enumerate(surv):
+        assert np.array_equal(bufs[r].view(np.uint32), ref[j].view(np.uint32)), r
+    for r in range(n):
+        if r not in surv:
+            assert np.array_equal(bufs[r].view(np.uint32), xs[r].view(np.uint32)), f"failed rank {r} restored"
+    assert len(set(orc.hash64(bufs[r]) for r in surv)) == 1
+
+
+def test_ft_integer_inputs_exact_over_survivors(orc):
+    n, count = 6, 4099
+    xs = inputs.integers(n, count)
+    bufs = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(bufs, [(4, 3)])
+    assert rep["survivors"] == [0, 1, 2, 3, 5]
+    exact = sum(xs[r].astype(np.float64) for r in rep["survivors"])
+    for r in rep["survivors"]:
+        assert np.array_equal(bufs[r].astype(np.float64), exact)
+
+
+def test_ft_attempts_and_bytes_by_hand(orc):
+    """N = 4, T = 512 fp32 (L = 128, 512 bytes per chunk, every chunk full).
+    Faults: rank 2 before step 4 (the first allgather step), rank 0 before
+    step 2.  Pass 1 over {0,1,2,3}: step 1 runs, rank 0 fails before step 2.
+    Pass 2 over {1,2,3} (L = 256, chunks 1024, 1024, 0 bytes): steps 1..3
+    run, rank 2 fails before step 4.  Pass 3 over {1,3} (L = 256, chunks of
+    1024 bytes): steps 1 and 2 complete."""
+    xs = inputs.gradient_like(4, 512, salt=9)
+    bufs = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(bufs, [(2, 4), (0, 2)])
+    assert rep["status"] == 0 and rep["attempts"] == 3
+    assert rep["dead_attempt"] == [1, 0, 2, 0] and rep["dead_step"] == [2, 0, 4, 0]
+    assert rep["survivors"] == [1, 3]
+    # pass 1 step 1: every rank sends one 512-byte chunk
+    sent = [512] * 4
+    # pass 2 over members (1,2,3): member j sends chunk (j - s) mod 3 at RS step s and
+    # (j - s + 1) mod 3 at AG step s; chunk bytes (1024, 1024, 0)
+    cb = [1024, 1024, 0]
+    for s in (1, 2):
+        for j, r in enumerate((1, 2, 3)):
+            sent[r] += cb[(j - s) % 3]
+    for j, r in enumerate((1, 2, 3)):  # AG step 1 (global step 3)
+        sent[r] += cb[(j - 1 + 1) % 3]
+    # pass 3 over (1,3): one RS step and one AG step of 1024 bytes each
+    sent[1] += 2048
+    sent[3] += 2048
+    assert rep["sent"] == sent
+    assert sum(rep["recv"]) == sum(sent)
+
+
+def test_ft_all_ranks_fail(orc):
+    xs = inputs.gradient_like(3, 1000, salt=1)
+    bufs = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(bufs, [(0, 1), (1, 1), (2, 1)])
+    assert rep["status"] == orc.EABORT and rep["survivors"] == []
+    for b, x in zip(bufs, xs):
+        assert np.array_equal(b, x)
+
+
+def test_ft_faults_after_the_last_step_never_fire(orc):
+    xs = inputs.gradient_like(4, 1000, salt=3)
+    a = [x.copy() for x in xs]
+    orc.ring_allreduce(a)
+    b = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(b, [(1, 7), (3, 100)])  # 4 ranks: steps 1..6
+    assert rep["attempts"] == 1 and rep["survivors"] == [0, 1, 2, 3]
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_ft_rejects_bad_faults(orc):
+    xs = inputs.gradient_like(2, 10, salt=3)
+    for f in ([(2, 1)], [(-1, 1)], [(0, 0)]):
+        with pytest.raises(ValueError):
+            orc.ring_allreduce_ft([x.copy() for x in xs], f)
