@@ -64,7 +64,8 @@ typedef enum rar_status {
   RAR_EWORKSPACE = 4, /* workspace missing or smaller than required */
   RAR_EHIP = 5,       /* the HIP runtime reported an error (launch, event, stream) */
   RAR_ENOTSUP = 6,    /* valid request that this library does not implement */
-  RAR_EOVERLAP = 7    /* two rank buffers overlap, or a buffer is NULL */
+  RAR_EOVERLAP = 7,   /* two rank buffers overlap, or a buffer is NULL */
+  RAR_EABORT = 8      /* fault-tolerant ring: every member failed */
 } rar_status;
 
 typedef enum rar_dtype { RAR_F32 = 0, RAR_F16 = 1, RAR_BF16 = 2 } rar_dtype;
@@ -276,6 +277,76 @@ int rar_ring_allreduce_compressed_state(void* const* bufs, void* const* state, i
  * that used this workspace.  Synchronises `stream` first. */
 int rar_compressed_traffic(const void* workspace, int nranks, uint64_t* sent, uint64_t* recv,
                            void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Shared state and fault tolerance ([P1] "Prime Intellect 发布 PCCL 分布式  */
+/* 训练通信库", section "PCCL 模型": peers check a shared state by hash and  */
+/* re-send it to peers off the majority; a collective interrupted by a    */
+/* failing peer is retried on the peers that remain).                     */
+/* ---------------------------------------------------------------------- */
+
+/* Device workspace the hash calls need: 64 accumulators. */
+#define RAR_HASH_WORKSPACE_BYTES 512
+
+/* hashes[r] = 64-bit hash of the first nbytes bytes of bufs[r].  The bytes
+ * are read as little-endian 64-bit words w_0 .. w_{W-1} (the last one
+ * zero-padded); h = sum_i mix64(w_i + (i+1) * 0x9E3779B97F4A7C15) mod 2^64
+ * and the hash is mix64(h xor nbytes), mix64 being the splitmix64 output
+ * function.  Not cryptographic: it detects divergence, not tampering.
+ * Buffers: 16-byte aligned, may overlap (they are only read).  workspace:
+ * RAR_HASH_WORKSPACE_BYTES of device memory, 16-byte aligned.  Synchronises
+ * `stream` to return the hashes. */
+int rar_rank_hashes(void* const* bufs, int nranks, size_t nbytes, void* workspace, size_t ws_bytes,
+                    uint64_t* hashes, void* stream);
+
+/* Shared-state check and re-send.  The majority hash is the one held by the
+ * most ranks (a tie goes to the hash of the lowest rank among the tied
+ * ones); the lowest rank holding it sends its nbytes bytes to every rank
+ * whose hash differs.  *resent = number of ranks overwritten; hashes (may be
+ * NULL) receives the hashes before the re-send.  rar_last_traffic reports
+ * nbytes per re-sent rank.  Buffers must not overlap.  Synchronises
+ * `stream` once (the source is chosen on the host), then enqueues the
+ * copies on it. */
+int rar_shared_state_sync(void* const* bufs, int nranks, size_t nbytes, void* workspace, size_t ws_bytes,
+                          int* resent, uint64_t* hashes, void* stream);
+
+/* A failure injected from the host: `rank` stops before step `step` of a
+ * pass (steps 1 .. 2(M-1) of a pass over M members, reduce-scatter steps
+ * first). */
+typedef struct rar_fault {
+  int rank;
+  int step;
+} rar_fault;
+
+typedef struct rar_ft_report {
+  int attempts;                     /* passes started (1 when no fault fired) */
+  int nsurvivors;                   /* members of the pass that completed */
+  int survivors[RAR_MAX_RANKS];     /* their ranks, ascending */
+  int dead_attempt[RAR_MAX_RANKS];  /* pass in which rank r was found failed, 0 = never */
+  int dead_step[RAR_MAX_RANKS];     /* step before which it was found failed */
+  uint64_t hash[RAR_MAX_RANKS];     /* rar_rank_hashes of every rank's final buffer */
+} rar_ft_report;
+
+/* Device workspace of rar_ring_allreduce_ft: one snapshot of every rank's
+ * buffer plus the hash accumulators. */
+size_t rar_ft_workspace_bytes(int nranks, size_t count, int dtype);
+
+/* Ring allreduce that survives failing members.  The ring runs step by step
+ * from the host (the stepwise schedule).  Before each step the host checks
+ * the members against the fault list: a fault fires the first time a pass
+ * reaches its step while its rank is still a member.  A pass that meets a
+ * fired fault is abandoned: every rank's buffer is restored from the
+ * snapshot taken on entry, the failed ranks leave the ring, and a new pass
+ * runs over the survivors (ascending rank order, the ring closing over the
+ * gaps, chunk length rar_chunk_len(count, M)).  On return the survivors
+ * hold the ring allreduce of their inputs, failed ranks hold their inputs,
+ * and report->hash lets the caller confirm the survivors agree.
+ * rar_last_traffic counts every step that ran, abandoned ones included.
+ * Returns RAR_OK when a pass completed, RAR_EABORT when every rank failed
+ * (all buffers restored).  Faults: 0 <= rank < nranks, step >= 1, at most
+ * 256.  Synchronises `stream` (for the hashes). */
+int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype, const rar_fault* faults,
+                          int nfaults, void* workspace, size_t ws_bytes, rar_ft_report* report, void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* Gradient bucketing ([P2] production patterns: fuse small gradients     */

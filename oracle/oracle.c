@@ -917,7 +917,8 @@ int orc_ring_allreduce_ft(void* const* bufs, int n, size_t count, int dt, const 
         members[m] = r;
         sub[m++] = bufs[r];
       }
-    if (m == 0) {
+    if (m == 0) { /* no pass can start */
+      --attempt;
       rc = ORC_EABORT;
       break;
     }

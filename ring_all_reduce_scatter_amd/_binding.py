@@ -21,11 +21,25 @@ OP_ALLREDUCE, OP_ALLGATHER, OP_BROADCAST = 1, 2, 4
 SCHED_FUSED, SCHED_STAGED = 0, 1
 FEEDBACK_ERROR, FEEDBACK_DELTA = 1, 2
 MAX_RANKS = 64
+HASH_WORKSPACE_BYTES = 512
+EABORT = 8
 
 _c_vp = ctypes.c_void_p
 _c_size = ctypes.c_size_t
 _c_int = ctypes.c_int
 _u64p = ctypes.POINTER(ctypes.c_uint64)
+
+
+class Fault(ctypes.Structure):
+    """Mirror of rar_fault: `rank` stops before `step` of a pass."""
+    _fields_ = [("rank", ctypes.c_int), ("step", ctypes.c_int)]
+
+
+class FtReport(ctypes.Structure):
+    """Mirror of rar_ft_report."""
+    _fields_ = [("attempts", ctypes.c_int), ("nsurvivors", ctypes.c_int),
+                ("survivors", ctypes.c_int * 64), ("dead_attempt", ctypes.c_int * 64),
+                ("dead_step", ctypes.c_int * 64), ("hash", ctypes.c_uint64 * 64)]
 
 
 class CompressCfg(ctypes.Structure):
@@ -76,6 +90,12 @@ _SIGS = {
     "rar_ring_allreduce_compressed_state": (_c_int, [_c_vp, _c_vp, _c_int, _c_size, _c_int, _c_int,
                                                      ctypes.POINTER(CompressCfg), _c_vp, _c_size, _c_vp]),
     "rar_compressed_traffic": (_c_int, [_c_vp, _c_int, _u64p, _u64p, _c_vp]),
+    "rar_rank_hashes": (_c_int, [_c_vp, _c_int, _c_size, _c_vp, _c_size, _u64p, _c_vp]),
+    "rar_shared_state_sync": (_c_int, [_c_vp, _c_int, _c_size, _c_vp, _c_size, ctypes.POINTER(ctypes.c_int),
+                                       _u64p, _c_vp]),
+    "rar_ft_workspace_bytes": (_c_size, [_c_int, _c_size, _c_int]),
+    "rar_ring_allreduce_ft": (_c_int, [_c_vp, _c_int, _c_size, _c_int, ctypes.POINTER(Fault), _c_int, _c_vp,
+                                       _c_size, ctypes.POINTER(FtReport), _c_vp]),
     "rar_bucket_plan": (_c_size, [_c_vp, _c_size, _c_int, _c_size, _c_vp]),
     "rar_bucketed_workspace_bytes": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size]),
     "rar_bucketed_allreduce": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_vp, _c_size,
@@ -306,6 +326,57 @@ def compressed_traffic(workspace, nranks: int, stream=None):
     _check(lib().rar_compressed_traffic(workspace.data_ptr(), nranks, sent, recv, _stream(stream, workspace)),
            "rar_compressed_traffic")
     return list(sent), list(recv)
+
+
+# ------------------------------------------------------------------ shared state, faults
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _ws(workspace):
+    return (workspace.data_ptr(), _nbytes(workspace)) if workspace is not None else (None, 0)
+
+
+def rank_hashes(bufs, workspace, nbytes=None, stream=None):
+    """64-bit hash of each rank buffer's first nbytes bytes (default: all)."""
+    nb = _nbytes(bufs[0]) if nbytes is None else nbytes
+    out = (ctypes.c_uint64 * len(bufs))()
+    ptrs = (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+    _check(lib().rar_rank_hashes(ptrs, len(bufs), nb, *_ws(workspace), out, _stream(stream, bufs[0])),
+           "rar_rank_hashes")
+    return list(out)
+
+
+def shared_state_sync(bufs, workspace, stream=None):
+    """Majority-hash check; diverged ranks receive the majority buffer.
+    Returns (resent, hashes before the re-send)."""
+    resent = ctypes.c_int(0)
+    out = (ctypes.c_uint64 * len(bufs))()
+    _check(lib().rar_shared_state_sync(_rank_ptrs(bufs), len(bufs), _nbytes(bufs[0]), *_ws(workspace),
+                                       ctypes.byref(resent), out, _stream(stream, bufs[0])),
+           "rar_shared_state_sync")
+    return resent.value, list(out)
+
+
+def ft_workspace_bytes(nranks: int, count: int, dtype: int) -> int:
+    return lib().rar_ft_workspace_bytes(nranks, count, dtype)
+
+
+def ring_allreduce_ft(bufs, faults, workspace, stream=None):
+    """Ring allreduce with injected faults [(rank, step), ...].  Returns a
+    dict: status (0 or EABORT), attempts, survivors, dead_attempt, dead_step,
+    hash (per rank)."""
+    n = len(bufs)
+    arr = (Fault * max(1, len(faults)))(*[Fault(int(r), int(s)) for r, s in faults])
+    rep = FtReport()
+    rc = lib().rar_ring_allreduce_ft(_rank_ptrs(bufs), n, bufs[0].numel(), dtype_code(bufs[0]), arr, len(faults),
+                                     *_ws(workspace), ctypes.byref(rep), _stream(stream, bufs[0]))
+    if rc not in (0, EABORT):
+        _check(rc, "rar_ring_allreduce_ft")
+    return {"status": rc, "attempts": rep.attempts, "survivors": list(rep.survivors)[:rep.nsurvivors],
+            "dead_attempt": list(rep.dead_attempt)[:n], "dead_step": list(rep.dead_step)[:n],
+            "hash": list(rep.hash)[:n]}
 
 
 # ------------------------------------------------------------------ bucketing

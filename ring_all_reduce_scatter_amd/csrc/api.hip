@@ -805,6 +805,146 @@ int rar_compressed_traffic(const void* workspace, int nranks, uint64_t* sent, ui
   return RAR_OK;
 }
 
+// ------------------------------------------------------------------ shared state, faults
+
+int rar_rank_hashes(void* const* bufs, int nranks, size_t nbytes, void* workspace, size_t ws_bytes,
+                    uint64_t* hashes, void* stream) {
+  if (nranks < 1 || nranks > RAR_MAX_RANKS || !bufs || !hashes) return RAR_EINVAL;
+  if (!workspace || ws_bytes < RAR_HASH_WORKSPACE_BYTES) return RAR_EWORKSPACE;
+  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  for (int r = 0; r < nranks && nbytes; ++r) {
+    if (!bufs[r]) return RAR_EOVERLAP;
+    if ((uintptr_t)bufs[r] & 15u) return RAR_EALIGN;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  uint64_t acc[RAR_MAX_RANKS] = {};
+  if (nbytes) {
+    if (hip_rc(launch_rank_hash(make_ptrs(bufs, nranks), nranks, nbytes, (uint64_t*)workspace, st))) return RAR_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return RAR_EHIP;
+    if (hipMemcpy(acc, workspace, sizeof(uint64_t) * (size_t)nranks, hipMemcpyDeviceToHost) != hipSuccess)
+      return RAR_EHIP;
+  }
+  for (int r = 0; r < nranks; ++r) hashes[r] = hash_mix64(acc[r] ^ (uint64_t)nbytes);
+  return RAR_OK;
+}
+
+int rar_shared_state_sync(void* const* bufs, int nranks, size_t nbytes, void* workspace, size_t ws_bytes,
+                          int* resent, uint64_t* hashes, void* stream) {
+  if (!resent) return RAR_EINVAL;
+  int rc = check_bufs(bufs, nranks, RAR_F32, nbytes);  // byte buffers: the element type plays no part
+  if (rc) return rc;
+  uint64_t h[RAR_MAX_RANKS];
+  if ((rc = rar_rank_hashes(bufs, nranks, nbytes, workspace, ws_bytes, h, stream))) return rc;
+  if (hashes)
+    for (int r = 0; r < nranks; ++r) hashes[r] = h[r];
+  int src = 0, best = 0;
+  for (int r = 0; r < nranks; ++r) {
+    int votes = 0;
+    for (int q = 0; q < nranks; ++q) votes += h[q] == h[r];
+    if (votes > best) {
+      best = votes;
+      src = r;
+    }
+  }
+  Traffic tr;
+  tr.reset(nranks);
+  int moved = 0;
+  for (int r = 0; r < nranks; ++r) {
+    if (h[r] == h[src]) continue;
+    if (hipMemcpyAsync(bufs[r], bufs[src], nbytes, hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess)
+      return RAR_EHIP;
+    tr.add(src, r, (uint64_t)nbytes);
+    ++moved;
+  }
+  g_last = tr;
+  *resent = moved;
+  return RAR_OK;
+}
+
+size_t rar_ft_workspace_bytes(int nranks, size_t count, int dtype) {
+  if (nranks < 1 || nranks > RAR_MAX_RANKS || !dt_ok(dtype)) return 0;
+  return RAR_HASH_WORKSPACE_BYTES + (size_t)nranks * round_up(count * es_of(dtype), kAlign);
+}
+
+int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype, const rar_fault* faults,
+                          int nfaults, void* workspace, size_t ws_bytes, rar_ft_report* report, void* stream) {
+  const size_t es = es_of(dtype);
+  int rc = check_bufs(bufs, nranks, dtype, count * es);
+  if (rc) return rc;
+  if (!report || nfaults < 0 || nfaults > 256 || (nfaults && !faults)) return RAR_EINVAL;
+  for (int i = 0; i < nfaults; ++i)
+    if (faults[i].rank < 0 || faults[i].rank >= nranks || faults[i].step < 1) return RAR_EINVAL;
+  if (!workspace || ws_bytes < rar_ft_workspace_bytes(nranks, count, dtype)) return RAR_EWORKSPACE;
+  if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t bytes = count * es, slot = round_up(bytes, kAlign);
+  char* snap = (char*)workspace + RAR_HASH_WORKSPACE_BYTES;
+  auto copy_all = [&](bool to_snapshot) -> int {
+    for (int r = 0; r < nranks && bytes; ++r) {
+      void* dst = to_snapshot ? (void*)(snap + (size_t)r * slot) : bufs[r];
+      const void* src = to_snapshot ? (const void*)bufs[r] : (const void*)(snap + (size_t)r * slot);
+      if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) return RAR_EHIP;
+    }
+    return RAR_OK;
+  };
+  if ((rc = copy_all(true))) return rc;
+  bool alive[RAR_MAX_RANKS];
+  std::vector<char> fired((size_t)nfaults, 0);
+  std::memset(report, 0, sizeof *report);
+  for (int r = 0; r < nranks; ++r) alive[r] = true;
+  Traffic tr;
+  tr.reset(nranks);
+  int attempt = 0, m = 0, members[RAR_MAX_RANKS];
+  for (;;) {
+    ++attempt;
+    m = 0;
+    RankPtrs sub{};
+    for (int r = 0; r < nranks; ++r)
+      if (alive[r]) {
+        sub.p[m] = (char*)bufs[r];
+        members[m++] = r;
+      }
+    if (m == 0) {  // no pass can start
+      --attempt;
+      break;
+    }
+    const size_t L = chunk_len_aligned(count, m, 128);
+    bool aborted = false;
+    for (int g = 1; g <= 2 * (m - 1); ++g) {
+      // liveness check of the members before step g
+      for (int i = 0; i < nfaults; ++i) {
+        if (fired[(size_t)i] || faults[i].step != g) continue;
+        fired[(size_t)i] = 1;
+        const int k = faults[i].rank;
+        if (!alive[k]) continue;
+        alive[k] = false;
+        report->dead_attempt[k] = attempt;
+        report->dead_step[k] = g;
+        aborted = true;
+      }
+      if (aborted) break;
+      const bool rs = g <= m - 1;
+      const int s = rs ? g : g - (m - 1);
+      for (int j = 0; j < m; ++j) {  // member j sends chunk (j-s) (RS) or (j-s+1) (AG) to member j+1
+        size_t lo, hi;
+        chunk_range(count, L, modn(rs ? j - s : j - s + 1, m), &lo, &hi);
+        tr.add(members[j], members[(j + 1) % m], (uint64_t)(hi - lo) * es);
+      }
+      if (count == 0) continue;
+      if ((rc = rs ? run_rs_step(sub, m, count, L, dtype, s, st) : run_ag_step(sub, m, count, L, es, s, st)))
+        return rc;
+    }
+    if (!aborted) break;
+    if ((rc = copy_all(false))) return rc;
+  }
+  g_last = tr;
+  report->attempts = attempt;
+  report->nsurvivors = m;
+  for (int j = 0; j < m; ++j) report->survivors[j] = members[j];
+  if ((rc = rar_rank_hashes(bufs, nranks, bytes, workspace, ws_bytes, report->hash, stream))) return rc;
+  return m == 0 ? RAR_EABORT : RAR_OK;
+}
+
 // ------------------------------------------------------------------ bucketing
 
 size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t cap_bytes, int* bucket_of) {
@@ -1018,6 +1158,7 @@ const char* rar_status_string(int status) {
     case RAR_EHIP: return "HIP runtime error";
     case RAR_ENOTSUP: return "not supported";
     case RAR_EOVERLAP: return "rank buffers overlap or are NULL";
+    case RAR_EABORT: return "ring aborted: every member failed";
     default: return "unknown status";
   }
 }

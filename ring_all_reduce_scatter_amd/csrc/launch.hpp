@@ -141,6 +141,21 @@ hipError_t launch_bfp_ring_fold_state(const RankPtrs& bufs, const RankPtrs& stat
 // reused as soon as the call returns.
 hipError_t launch_fill_u64(uint64_t* dst, const uint64_t* host_vals, int nvals, hipStream_t stream);
 
+// -------------------------------------------------------------- hash (hash_kernels.hip)
+
+// acc[y] = sum over the 64-bit words of bufs.p[y] (y < n) of the hash's
+// per-word terms (accumulators cleared first, stream-ordered).  The caller
+// finishes each rank's hash as mix64(acc[y] xor nbytes).
+hipError_t launch_rank_hash(const RankPtrs& bufs, int n, uint64_t nbytes, uint64_t* acc, hipStream_t stream);
+
+// Output function of the splitmix64 generator (Steele, Lea and Flood,
+// "Fast splittable pseudorandom number generators", OOPSLA 2014).
+__host__ __device__ inline uint64_t hash_mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 __host__ __device__ inline uint64_t bfp_exp_bytes(uint64_t count, int block) {
   uint64_t nb = (count + (uint64_t)block - 1) / (uint64_t)block;
   return (nb + 15) / 16 * 16;

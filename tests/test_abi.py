@@ -187,3 +187,61 @@ def test_stateful_compressed_argument_errors():
     assert call(st=(ctypes.c_void_p * 2)(base + (2 << 20), base + (3 << 20) + 4)) == 3
     assert call(st=(ctypes.c_void_p * 2)(base + (2 << 20), None)) == 7
     assert call(wsb=64) == 4
+
+
+def test_ft_workspace_and_argument_errors():
+    assert rar.ft_workspace_bytes(4, 1000, rar.F32) == 512 + 4 * 4096
+    assert rar.ft_workspace_bytes(0, 10, rar.F32) == 0
+    base = 1 << 40
+    lib = rar.lib()
+    ptrs = (ctypes.c_void_p * 2)(base, base + (1 << 20))
+    rep = rar.FtReport()
+    faults = (rar.Fault * 1)(rar.Fault(2, 1))
+    ws = base + (8 << 20)
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 1 << 20, ctypes.byref(rep), None) == 1
+    faults[0] = rar.Fault(1, 0)
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 1 << 20, ctypes.byref(rep), None) == 1
+    faults[0] = rar.Fault(1, 1)
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 64, ctypes.byref(rep), None) == 4
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 1 << 20, None, None) == 1
+    hs = (ctypes.c_uint64 * 2)()
+    assert lib.rar_rank_hashes(ptrs, 2, 64, ws, 100, hs, None) == 4
+    assert lib.rar_rank_hashes(ptrs, 2, 64, ws + 8, 512, hs, None) == 3
+
+
+def test_hash_of_empty_buffers_needs_no_device(orc):
+    base = 1 << 40
+    lib = rar.lib()
+    ptrs = (ctypes.c_void_p * 3)(base, base, base)
+    hs = (ctypes.c_uint64 * 3)()
+    assert lib.rar_rank_hashes(ptrs, 3, 0, base, 512, hs, None) == 0
+    assert list(hs) == [orc.hash64(np.zeros(0, np.uint8))] * 3
+
+
+def _fault_plans(n, seed):
+    g = np.random.default_rng(seed)
+    plans = [[], [(0, 1)], [(n - 1, max(1, 2 * (n - 1)))], [(r, 1) for r in range(n)]]
+    for _ in range(20):
+        k = int(g.integers(1, 5))
+        plans.append([(int(g.integers(0, n)), int(g.integers(1, 2 * n))) for _ in range(k)])
+    return plans
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 16])
+def test_ft_scheduler_matches_oracle_on_empty_buffers(orc, n):
+    """count = 0 runs the fault scheduler on the host alone (no copies, no
+    launches): attempts, failed ranks, steps and survivors match the oracle's."""
+    base = 1 << 40
+    lib = rar.lib()
+    ptrs = (ctypes.c_void_p * n)(*[base + i * 4096 for i in range(n)])
+    for plan in _fault_plans(n, n):
+        arr = (rar.Fault * max(1, len(plan)))(*[rar.Fault(r, s) for r, s in plan])
+        rep = rar.FtReport()
+        rc = lib.rar_ring_allreduce_ft(ptrs, n, 0, rar.F32, arr, len(plan), base, 512, ctypes.byref(rep), None)
+        ref = orc.ring_allreduce_ft([np.zeros(0, np.float32) for _ in range(n)], plan)
+        assert rc == (rar.EABORT if ref["status"] == orc.EABORT else 0), plan
+        assert rep.attempts == ref["attempts"], plan
+        assert list(rep.survivors)[:rep.nsurvivors] == ref["survivors"], plan
+        assert list(rep.dead_attempt)[:n] == ref["dead_attempt"], plan
+        assert list(rep.dead_step)[:n] == ref["dead_step"], plan
+        assert rar.last_traffic(n) == ([0] * n, [0] * n)

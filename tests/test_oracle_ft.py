@@ -153,7 +153,7 @@ def test_ft_all_ranks_fail(orc):
     xs = inputs.gradient_like(3, 1000, salt=1)
     bufs = [x.copy() for x in xs]
     rep = orc.ring_allreduce_ft(bufs, [(0, 1), (1, 1), (2, 1)])
-    assert rep["status"] == orc.EABORT and rep["survivors"] == []
+    assert rep["status"] == orc.EABORT and rep["survivors"] == [] and rep["attempts"] == 1
     for b, x in zip(bufs, xs):
         assert np.array_equal(b, x)
 
