@@ -46,6 +46,41 @@ def host_info():
     return {"cpu_model": model, "host_threads": os.cpu_count()}
 
 
+_CSRC = "ring_all_reduce_scatter_amd/csrc/"
+MIB = 1 << 20
+# Kernels whose HBM traffic the counter passes measure: the name fragment
+# that picks their dispatches in a rocprofv3 counter CSV, the algorithmic
+# bytes of one launch in the counters run, and the sources that define them
+# (the committed figures are used only while these are unchanged).
+COUNTER_KERNELS = {
+    "ring_fold_f32_n8": {
+        "match": "::ring_fold_kernel<0, 8,", "workload": "N=8 x 64M fp32",
+        "algorithmic": 2 * 8 * 256 * MIB, "sources": [_CSRC + "ring_kernels.hip", _CSRC + "common.hpp"]},
+    "bfp_ring_fold_f16_n8": {
+        "match": "::bfp_ring_fold_kernel<1, 8, 16,", "workload": "N=8 x 128M fp16, BFP-8",
+        "algorithmic": 2 * 8 * 256 * MIB,
+        "sources": [_CSRC + "bfp_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp"]},
+    "bfp_ring_fold_state_f16_n8": {
+        "match": "::bfp_ring_fold_state_kernel<1, 8, 16, 1>",
+        "workload": "N=8 x 128M fp16, BFP-8, error feedback (128M fp32 state per rank)",
+        "algorithmic": 2 * 8 * 256 * MIB + 2 * 8 * 512 * MIB,
+        "sources": [_CSRC + "bfp_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp"]},
+    "rank_hash_f32_n8": {
+        "match": "::rank_hash_kernel", "workload": "N=8 x 256 MiB",
+        "algorithmic": 8 * 256 * MIB, "sources": [_CSRC + "hash_kernels.hip", _CSRC + "common.hpp"]},
+}
+# calibration copy of the counters run: 256 MiB read and 256 MiB written
+CALIBRATION = {"match": "copy_jobs_kernel", "bytes": 256 * MIB}
+PMC_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv "
+    "-d $R/gpurun_out/pmc_fetch -o pmc -- python -u $R/bench.py --counters",
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv "
+    "-d $R/gpurun_out/pmc_write -o pmc -- python -u $R/bench.py --counters",
+    "python bench.py --ingest-counters gpurun_out/pmc_fetch/pmc_counter_collection.csv "
+    "gpurun_out/pmc_write/pmc_counter_collection.csv",
+]
+
+
 def source_sha(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -133,8 +168,7 @@ def fp32_leg(args):
     torch.cuda.empty_cache()
     alg_bytes = 2 * n * S  # every rank's input read once and output written once
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    sources = ["ring_all_reduce_scatter_amd/csrc/ring_kernels.hip", "ring_all_reduce_scatter_amd/csrc/common.hpp",
-               "ring_all_reduce_scatter_amd/csrc/launch.hpp"]
+    sources = COUNTER_KERNELS["ring_fold_f32_n8"]["sources"]
     res = {
         "n": n, "count": count, "S": S, "ms": ms, "kern_ms": kern_ms, "kern_min_ms": kern_min,
         "busbw": busbw(S, n, ms),
@@ -222,8 +256,7 @@ def bfp8_leg(args):
     torch.cuda.empty_cache()
     alg_bytes = 2 * n * S
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    sources = ["ring_all_reduce_scatter_amd/csrc/bfp_kernels.hip", "ring_all_reduce_scatter_amd/csrc/bfp_device.hpp",
-               "ring_all_reduce_scatter_amd/csrc/common.hpp", "ring_all_reduce_scatter_amd/csrc/launch.hpp"]
+    sources = COUNTER_KERNELS["bfp_ring_fold_f16_n8"]["sources"]
     res = {
         "metric": "BFP-8 compressed all-reduce effective bus GB/s (2T(N-1)/N fp16 bytes per rank)",
         "value": round(busbw(S, n, ms), 2), "unit": "GB/s", "ms_per_step": round(ms, 4),
@@ -306,6 +339,20 @@ def extra_legs(args):
     out["fp32_reduce_scatter_fused"] = {"ms": round(ms, 4),
                                         "busbw_GBs": round(S * (n - 1) / n / (ms * 1e-3) / 1e9, 1),
                                         "frac_of_roofline": round((n * S + S) / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # shared-state hash of every rank's buffer (reads N*S bytes; one host sync)
+    hws = torch.empty(rar.HASH_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    ms, k, _ = time_leg(lambda b: rar.rank_hashes(b, hws), sets, 2, steps)
+    out["rank_hashes_fp32_8x256MiB"] = {
+        "ms": round(ms, 4), "read_GBs": round(n * S / (k * 1e-3) / 1e9, 1),
+        "frac_of_roofline": round(n * S / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": counter_traffic("rank_hash_f32_n8", COUNTER_KERNELS["rank_hash_f32_n8"]["sources"])}
+    # fault-tolerant ring: no fault, and rank 3 failing before step 5 (snapshot,
+    # 4 abandoned steps, restore, a 7-rank stepwise pass, hashes)
+    fws = torch.empty(rar.ft_workspace_bytes(n, count, rar.F32), dtype=torch.uint8, device="cuda:0")
+    for nm, plan in (("ft_ring_fp32_no_fault", []), ("ft_ring_fp32_rank3_fails_before_step5", [(3, 5)])):
+        ms, k, _ = time_leg(lambda b: rar.ring_allreduce_ft(b, plan, fws), sets, 1, min(steps, 4))
+        out[nm] = {"ms": round(ms, 4), "attempts": rar.ring_allreduce_ft(sets[0], plan, fws)["attempts"]}
+    del fws, hws
     del sets, pristine
     torch.cuda.empty_cache()
     wb = inputs.WORKLOADS["bfp8"]
@@ -331,7 +378,11 @@ def extra_legs(args):
         ms, k, _ = time_leg(lambda b: rar.ring_allreduce_compressed_state(b, state, fb, cfg, ws), sets, 2, steps)
         moved = 2 * wb["n"] * Sb + 2 * wb["n"] * wb["count"] * 4
         out[nm] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
-                   "frac_of_roofline": round(moved / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                   "frac_of_roofline": round(moved / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "algorithmic_bytes": moved}
+    ck = COUNTER_KERNELS["bfp_ring_fold_state_f16_n8"]
+    out["bfp8_allreduce_fused_error_feedback"]["traffic"] = counter_traffic("bfp_ring_fold_state_f16_n8",
+                                                                            ck["sources"])
     del sets, pristine, ws, state
     torch.cuda.empty_cache()
     w5 = inputs.WORKLOADS["sparse_bfp4"]
@@ -425,8 +476,64 @@ def counters_run(reps=3):
                      device="cuda:0")
     for _ in range(reps):
         rar.ring_allreduce_compressed(bufs, cfg, ws)
+    state = [torch.zeros(wb["count"], dtype=torch.float32, device="cuda:0") for _ in range(wb["n"])]
+    for _ in range(reps):
+        rar.ring_allreduce_compressed_state(bufs, state, rar.FEEDBACK_ERROR, cfg, ws)
+    del state, bufs
+    w = inputs.WORKLOADS["ring_grad"]
+    bufs = [torch.from_numpy(x).to("cuda:0") for x in inputs.gradient_like(w["n"], w["count"])]
+    hws = torch.empty(rar.HASH_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    for _ in range(reps):
+        rar.rank_hashes(bufs, hws)
     torch.cuda.synchronize()
     log("[bench] counters run done")
+
+
+def _counter_values(path, counter, match):
+    import csv
+    vals = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and match in row["Kernel_Name"]:
+                vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def ingest_counters(fetch_csv, write_csv):
+    """Turn two rocprofv3 counter passes over `bench.py --counters` (FETCH_SIZE
+    and WRITE_SIZE, KiB per dispatch) into profiles/counters.json: each
+    counter is scaled by what it reads for the calibration copy of known size,
+    and the median over a kernel's dispatches is kept."""
+    import statistics
+    cal_bytes_kib = CALIBRATION["bytes"] / 1024
+    cf = statistics.median(_counter_values(fetch_csv, "FETCH_SIZE", CALIBRATION["match"]))
+    cw = statistics.median(_counter_values(write_csv, "WRITE_SIZE", CALIBRATION["match"]))
+    out = {"_calibration": {
+        "kernel": "copy_jobs_kernel (broadcast over 2 ranks, 256 MiB fp32: 262144 KiB read and written)",
+        "fetch_kib_measured": cf, "write_kib_measured": cw,
+        "fetch_scale": round(cal_bytes_kib / cf, 5), "write_scale": round(cal_bytes_kib / cw, 5),
+        "commands": PMC_COMMANDS}}
+    rows = []
+    for key, k in COUNTER_KERNELS.items():
+        fv = _counter_values(fetch_csv, "FETCH_SIZE", k["match"])
+        wv = _counter_values(write_csv, "WRITE_SIZE", k["match"])
+        if not fv or not wv:
+            continue
+        fk, wk = statistics.median(fv), statistics.median(wv)
+        hbm = int(round((fk * cal_bytes_kib / cf + wk * cal_bytes_kib / cw) * 1024))
+        out[key] = {"kernel_match": k["match"], "workload": k["workload"], "fetch_kib": fk, "write_kib": wk,
+                    "dispatches": len(fv), "hbm_bytes_per_launch": hbm,
+                    "algorithmic_bytes_per_launch": k["algorithmic"], "source_sha": source_sha(k["sources"]),
+                    "sources": k["sources"]}
+        rows.append(f"| `{k['match']}` ({k['workload']}) | {fk:.1f} | {wk:.1f} | {hbm:,} | {k['algorithmic']:,} | "
+                    f"{hbm / k['algorithmic']:.4f} |")
+    with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(f"calibration: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB for {cal_bytes_kib:.0f} KiB moved")
+    print("| kernel (workload) | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per launch | algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|")
+    print("\n".join(rows))
 
 
 def main():
@@ -440,7 +547,12 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time stepwise, staged and other collectives")
     ap.add_argument("--counters", action="store_true",
                     help="only run the short launch sequence used for rocprofv3 --pmc passes")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="(no GPU) write profiles/counters.json from two rocprofv3 --pmc passes over --counters")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the N simulated ranks share one MI355X's HBM, so --gpus "
               f"{args.gpus} is not supported", file=sys.stderr)
