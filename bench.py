@@ -141,6 +141,40 @@ def time_leg(run, sets, warmup, steps):
     return (t1 - t0) * 1e3 / steps, sum(ev) / len(ev), min(ev)
 
 
+def time_graph_leg(run, sets, steps):
+    """Like time_leg, but each set's call is captured once in a HIP graph and
+    the timed steps replay the graphs (one per set, so inputs stay fresh)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(sets[0])  # library streams and events exist before any capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for b in sets[1:]:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(b)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    graphs[0].replay()  # first replay uploads the graph
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        graphs[1 + i % (len(graphs) - 1) if len(graphs) > 1 else 0].replay()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    del graphs
+    return (t1 - t0) * 1e3 / steps, sum(ev) / len(ev), min(ev)
+
+
 def busbw(bytes_per_rank, n, ms):
     return 2.0 * bytes_per_rank * (n - 1) / n / (ms * 1e-3) / 1e9
 
@@ -366,6 +400,10 @@ def extra_legs(args):
     Sb = wb["count"] * 2
     out["bfp8_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
                                     "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms, k, _ = time_graph_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, steps)
+    out["bfp8_allreduce_staged_graph_replay"] = {
+        "ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
+        "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del ws
     # the same fused ring with per-rank error-feedback state (state read and
     # rewritten once per element per rank: 8 more bytes per element per rank)
