@@ -373,13 +373,21 @@ hipError_t pair_dispatch(const RankPtrs& bufs, const PairJobs& pairs, uint64_t c
 
 }  // namespace
 
-// Workgroups per CU for the fold over n ranks: keeps n * vectors * waves
-// (the loads in flight per CU) at its N = 8 optimum; 0 = no cap.
+// Workgroups per CU for the fold over n ranks, measured on MI355X (fused
+// allreduce, 2 GiB per launch).  fp32/fp16: N = 2 -> 3 (6.28 TB/s against
+// 5.84 uncapped), N = 4 -> 1 (5.77 against 4.94 at 2), N = 8 and 16 -> 1;
+// bf16 needs more waves to hide its rounding ALU: N = 2 -> 4, N = 4 -> 2
+// (6.35), N = 8 and 16 -> 2.  Rank counts without a specialised kernel
+// (runtime loop, loads not hoisted) -> 2 (N = 5: 5.11 against 4.57 at 1).
 int fold_wgs_per_cu(int dt, int n) {
-  const int at8 = dt == DT_BF16 ? 2 : 1;
-  const int floor = dt == DT_BF16 ? 2 : 1;  // bf16 needs the waves to hide its rounding ALU
-  const int w = n > 0 ? at8 * 8 / n : at8;
-  return w < floor ? floor : (w >= 8 ? 0 : w);
+  const bool b16 = dt == DT_BF16;
+  switch (n) {
+    case 2: return b16 ? 4 : 3;
+    case 4: return b16 ? 2 : 1;
+    case 8:
+    case 16: return b16 ? 2 : 1;
+    default: return 2;
+  }
 }
 size_t residency_lds(int wgs_per_cu) {
   if (wgs_per_cu <= 0) return 0;
