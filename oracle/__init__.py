@@ -12,7 +12,8 @@ Parity status of each function (what pins it is in the tests under
 ``tests/test_oracle_*.py``):
   f16/bf16 conversions ............ pinned (numpy / torch RNE conversions)
   ring RS / AG / allreduce ........ pinned (brute-force exact sums, closed-form
-                                    fold order, post-conditions, byte table)
+                                    fold order, post-conditions, byte table,
+                                    torch.distributed gloo within float32 eps)
   allgather / broadcast ........... pinned (copies, byte table)
   BFP encode / decode ............. pinned (brute-force optimal rounding,
                                     exponent via frexp, exact round trips,
