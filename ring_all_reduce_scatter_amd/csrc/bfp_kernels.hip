@@ -286,6 +286,15 @@ struct U64Vals {
 //                   receiver gets
 // The hop chain of a block is the one of bfp_ring_fold_kernel with v in place
 // of p at every encode, in binary32.
+// Orders LDS writes and reads among the lanes of one wavefront: each
+// wavefront only exchanges data inside its own 512-element slice of the tile,
+// so no workgroup barrier is needed.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int DT, int NR, int LPB, int FB>
 __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs bufs, RankPtrs st, int nranks,
                                                                         uint64_t count, uint64_t L, int lpb_rt,
@@ -336,30 +345,89 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs 
   // reduce-scatter, c is the receiver of the last hop and the allgather owner
   const int first = (int)c + 1 < N ? (int)c + 1 : 0;
   if constexpr (NR > 0) {
-    // every load issued before the chain (the state writes cannot alias them)
-    // (16-bit inputs stay packed until their hop: half the registers)
+    // Every load is issued before the chain (16-bit inputs stay packed until
+    // their hop: half the registers).  The state goes through LDS: a
+    // wavefront moves it with 16-byte lanes over 1 KiB of contiguous memory
+    // per instruction (lane l: floats 4l..4l+3 and 256+4l..), and LDS hands
+    // each lane its 8 consecutive floats.  Loading 8 consecutive floats per
+    // lane straight from memory splits every instruction into 16-byte pieces
+    // 32 bytes apart, which MI355X's HBM serves measurably slower.
+    extern __shared__ __align__(16) float lds_state[];  // [NR][tile of 2048 floats]
+    constexpr int kTileElems = kThreads * kGroupElems;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t w0 = (threadIdx.x & ~63u) * kGroupElems;  // wavefront's first element in the tile
+    const uint32_t qa = w0 + 4 * lane, qb = qa + 256;            // the lane's two quads in the tile
+    auto quad_n = [&](uint32_t q) { const uint64_t g = tile0 + q; return g >= hi ? 0 : (hi - g >= 4 ? 4 : (int)(hi - g)); };
+    const int na = quad_n(qa), nb = quad_n(qb);
+    auto gload_quad = [&](const char* base, uint32_t q, int nq) -> u32x4 {
+      if (nq == 4) return ld16<true>(base + (tile0 + q) * 4);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      for (int i = 0; i < nq; ++i) v[i] = ((const uint32_t*)base)[tile0 + q + i];
+      return v;
+    };
+    auto gstore_quad = [&](char* base, uint32_t q, int nq, const u32x4& v) {
+      if (nq == 4) st16<true>(base + (tile0 + q) * 4, v);
+      else
+        for (int i = 0; i < nq; ++i) ((uint32_t*)base)[tile0 + q + i] = v[i];
+    };
     Raw8<DT> x[NR];
+    u32x4 sa[NR], sb[NR];
     G8 s[NR];
     auto rank_of = [&](int j) { return first + j < NR ? first + j : first + j - NR; };
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int q = rank_of(j);
       x[j] = nv == 8 ? load_raw8<DT, true>(bufs.p[q], e) : pack8<DT>(load_part8<DT>(bufs.p[q], e, nv));
-      s[j] = ld_state(q);
+      sa[j] = gload_quad(st.p[q], qa, na);
+      sb[j] = gload_quad(st.p[q], qb, nb);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      *(u32x4*)&lds_state[j * kTileElems + qa] = sa[j];
+      *(u32x4*)&lds_state[j * kTileElems + qb] = sb[j];
+    }
+    wave_lds_sync();
+    const uint32_t mine = threadIdx.x * kGroupElems;  // the lane's 8 consecutive elements
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const u32x4 lo4 = *(const u32x4*)&lds_state[j * kTileElems + mine];
+      const u32x4 hi4 = *(const u32x4*)&lds_state[j * kTileElems + mine + 4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[j].v[i] = __uint_as_float(lo4[i]);
+        s[j].v[4 + i] = __uint_as_float(hi4[i]);
+      }
     }
     G8 p = unpack8<DT>(x[0]);
 #pragma unroll
     for (int j = 1; j < NR; ++j) {
       const G8 d = message(p, s[j - 1]);
-      st_state(rank_of(j - 1), s[j - 1]);
       const G8 xj = unpack8<DT>(x[j]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) p.v[i] = round_to<DT>(xj.v[i] + d.v[i]);
     }
     const G8 y = message(p, s[NR - 1]);
-    st_state(rank_of(NR - 1), s[NR - 1]);
 #pragma unroll
     for (int j = 0; j < NR; ++j) store_group<DT>(bufs.p[j], e, nv, y);
+    wave_lds_sync();  // every lane of the wavefront has read its state from LDS
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      u32x4 lo4, hi4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo4[i] = __float_as_uint(s[j].v[i]);
+        hi4[i] = __float_as_uint(s[j].v[4 + i]);
+      }
+      *(u32x4*)&lds_state[j * kTileElems + mine] = lo4;
+      *(u32x4*)&lds_state[j * kTileElems + mine + 4] = hi4;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int q = rank_of(j);
+      gstore_quad(st.p[q], qa, na, *(const u32x4*)&lds_state[j * kTileElems + qa]);
+      gstore_quad(st.p[q], qb, nb, *(const u32x4*)&lds_state[j * kTileElems + qb]);
+    }
   } else {
     G8 p = ld(first);
     int r = first;
@@ -455,7 +523,11 @@ void fold_state_dispatch_nr(const RankPtrs& bufs, const RankPtrs& st, int n, uin
   const uint64_t tile = (uint64_t)kThreads * kGroupElems;
   const uint64_t tiles = (L + tile - 1) / tile;
   dim3 grid((unsigned)((uint64_t)n * tiles));
-  const size_t lds = residency_lds(state_fold_wgs_per_cu());
+  // NR > 0 stages the tile's state through LDS (NR * 8 KiB), which also
+  // bounds the workgroups per CU
+  size_t lds = residency_lds(state_fold_wgs_per_cu());
+  if (NR > 0 && lds < (size_t)NR * kThreads * kGroupElems * sizeof(float))
+    lds = (size_t)NR * kThreads * kGroupElems * sizeof(float);
   if (block == 128)
     hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, NR, 16, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
                        n, count, L, 16, mbits);
