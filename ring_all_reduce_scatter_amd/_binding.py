@@ -395,20 +395,38 @@ def bucketed_workspace_bytes(counts, nranks: int, dtype: int, cap_bytes: int, al
     return lib().rar_bucketed_workspace_bytes_ex(_sizes(counts), len(counts), nranks, dtype, cap_bytes, algo)
 
 
+class BucketedAllreduce:
+    """A bucketed allreduce over fixed gradient tensors, marshalled once.
+
+    tensors[r][t] is rank r's tensor t (device tensors, updated in place on
+    every call).  Validating and collecting N x T device pointers costs
+    milliseconds of Python for a model's worth of tensors, so, as a training
+    loop reuses its gradient tensors every step, the pointer table is built
+    here once and each call only launches.  The tensors and the workspace must
+    stay alive and keep their storage while this object is used."""
+
+    def __init__(self, tensors, cap_bytes: int, workspace, algo: int = ALGO_FUSED):
+        n, nt = len(tensors), len(tensors[0])
+        t0 = tensors[0][0]
+        counts = [x.numel() for x in tensors[0]]
+        flat = [x for row in tensors for x in row]
+        if any(len(row) != nt for row in tensors) or any([x.numel() for x in row] != counts for row in tensors):
+            raise ValueError("tensor t must have the same size on every rank")
+        if any(x.dtype != t0.dtype for x in flat) or not all(x.is_contiguous() for x in flat):
+            raise ValueError("tensors must share one dtype and be contiguous")
+        self._keep = (tensors, workspace)
+        self._ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() for x in flat])
+        self._counts = _sizes(counts)
+        self._args = (nt, n, dtype_code(t0), cap_bytes, algo,
+                      workspace.data_ptr() if workspace is not None else None,
+                      workspace.numel() * workspace.element_size() if workspace is not None else 0)
+        self._t0 = t0
+
+    def __call__(self, stream=None):
+        rc = lib().rar_bucketed_allreduce_ex(self._ptrs, self._counts, *self._args, _stream(stream, self._t0))
+        _check(rc, "rar_bucketed_allreduce_ex")
+
+
 def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None, algo: int = ALGO_FUSED):
     """tensors[r][t]: rank r's gradient tensor t (device tensors, in place)."""
-    n, nt = len(tensors), len(tensors[0])
-    t0 = tensors[0][0]
-    flat = [tensors[r][t] for r in range(n) for t in range(nt)]
-    for r in range(n):
-        for t in range(nt):
-            x = tensors[r][t]
-            if x.dtype != t0.dtype or x.numel() != tensors[0][t].numel() or not x.is_contiguous():
-                raise ValueError("tensor t must have the same size and dtype on every rank")
-    ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() for x in flat])
-    counts = [tensors[0][t].numel() for t in range(nt)]
-    rc = lib().rar_bucketed_allreduce_ex(ptrs, _sizes(counts), nt, n, dtype_code(t0), cap_bytes, algo,
-                                         workspace.data_ptr() if workspace is not None else None,
-                                         workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                         _stream(stream, t0))
-    _check(rc, "rar_bucketed_allreduce_ex")
+    BucketedAllreduce(tensors, cap_bytes, workspace, algo)(stream)

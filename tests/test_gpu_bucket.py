@@ -76,3 +76,26 @@ def test_bucketed_large_tensors_both_schedules_agree():
         for r in range(n):
             for t in range(len(sizes)):
                 assert_bits_equal(got[r][t], ref[r][t], f"algo {algo} rank {r} tensor {t}")
+
+
+def test_prepared_bucketed_allreduce_repeats():
+    """BucketedAllreduce marshals the pointer table once; two calls on restored
+    inputs give the one-shot call's bits both times."""
+    n = 4
+    sizes = inputs.bucket_sizes(30, lo_exp=3, hi_exp=14, salt=9)
+    th = inputs.bucket_tensors(n, sizes, dtype="bf16", salt=9)
+    cap = 32 << 10
+    want, _, _ = _run(th, "bf16", cap)
+    dev = [to_dev(th[r], "bf16") for r in range(n)]
+    pristine = [to_dev(th[r], "bf16") for r in range(n)]
+    ws = torch.empty(rar.bucketed_workspace_bytes(sizes, n, rar.BF16, cap), dtype=torch.uint8, device="cuda:0")
+    step = rar.BucketedAllreduce(dev, cap, ws)
+    for call in range(2):
+        for r in range(n):
+            for t, p in zip(dev[r], pristine[r]):
+                t.copy_(p)
+        step()
+        for r in range(n):
+            got = to_host(dev[r], "bf16")
+            for t in range(len(sizes)):
+                assert_bits_equal(got[t], want[r][t], f"call {call} rank {r} tensor {t}")
