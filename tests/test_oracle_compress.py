@@ -424,3 +424,37 @@ def test_compressed_ring_closed_form_chain(orc, n, mbits):
         final = orc.bfp_decode(orc.bfp_encode(p, mbits=mbits), L, mbits=mbits, out_dtype=np.float16)
         for b in bufs:
             assert np.array_equal(b[sl].view(np.uint16), final.view(np.uint16))
+
+
+def _all_finite_f16(seed):
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = codes.view(np.float16)
+    x = x[np.isfinite(x)].copy()
+    np.random.default_rng(seed).shuffle(x)
+    return x
+
+
+@pytest.mark.parametrize("mbits", [8, 4, 2])
+def test_bfp_encode_exhaustive_f16(orc, mbits):
+    """Every finite binary16 value (63,488 of them, shuffled into 496 blocks
+    of 128) against a vectorised brute force: each q is the integer in
+    [-qmax, qmax] nearest to x / step, ties to even, with step the block's
+    2^(e+2-m); all arithmetic exact in binary64."""
+    x = _all_finite_f16(mbits)
+    msg = orc.bfp_encode(x, block=128, mbits=mbits)
+    E, q = parse_bfp(msg, x.size, 128, mbits)
+    xb = x.astype(np.float64).reshape(-1, 128)
+    mx = np.max(np.abs(xb), axis=1)
+    e = np.floor(np.log2(np.where(mx > 0, mx, 1.0))).astype(int)
+    assert np.all(E == np.where(mx > 0, e + 127, 0))  # fp16 values are binary32-normal or zero
+    step = np.exp2((e + 2 - mbits).astype(np.float64))[:, None]
+    qmax = (1 << (mbits - 1)) - 1
+    cand = np.arange(-qmax, qmax + 1, dtype=np.float64)
+    # distance of each element to each candidate grid point; exact (all dyadic rationals in range)
+    d = np.abs(xb[:, :, None] - cand[None, None, :] * step[:, :, None])
+    best = d.min(axis=2, keepdims=True)
+    tie = d == best
+    even = (cand.astype(int) % 2 == 0)[None, None, :]
+    pick = np.where(tie.sum(axis=2) > 1, np.argmax(tie & even, axis=2), np.argmax(tie, axis=2))
+    want = cand[pick].astype(int).reshape(-1)
+    assert np.array_equal(q, want)
