@@ -481,12 +481,14 @@ struct BfpFoldGroups {
   static constexpr int value = 1;
 };
 
-// Workgroups per CU of the fused compressed fold.  The packed binary16 hop
-// needs about half the VALU of the binary32 formulation, so four workgroups
-// per CU (16 waves) hide its latency while keeping HBM requests moderate
-// (MI355X, N = 8: 5.55 TB/s uncapped, 6.06 TB/s at four).  The binary32
-// formulation (fp32 and bf16 buffers) stays uncapped.
-int bfp_fold_wgs_per_cu(int dt) { return dt == DT_F16 ? 4 : 0; }
+// Workgroups per CU of the fused compressed fold, measured on MI355X at
+// N = 8, 2 GiB per launch.  The packed binary16 hop needs about half the VALU
+// of the binary32 formulation, so four workgroups per CU (16 waves) hide its
+// latency while keeping HBM requests moderate (5.55 TB/s uncapped, 6.06 at
+// four).  fp32 buffers move twice the bytes per element and do best at two
+// (5.38 TB/s against 4.82 uncapped); bf16 runs the binary32 hop on 2-byte
+// elements, ALU-heavy, and needs six (5.82 against 5.67 uncapped, 3.83 at two).
+int bfp_fold_wgs_per_cu(int dt) { return dt == DT_F16 ? 4 : (dt == DT_F32 ? 2 : 6); }
 
 template <int DT, int NR>
 void fold_dispatch_lpb(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
