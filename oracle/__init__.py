@@ -102,8 +102,9 @@ def _load():
         "orc_mix64": (ctypes.c_uint64, [ctypes.c_uint64]),
         "orc_hash64": (ctypes.c_uint64, [_c_vp, _c_size]),
         "orc_shared_state_sync": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, _u64p, _u64p, _u64p]),
-        "orc_ring_allreduce_ft": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, _c_vp, _c_vp,
-                                                 ctypes.c_int, _c_vp, _c_vp, _c_vp, _u64p, _u64p]),
+        "orc_ring_allreduce_ft": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_size, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                                 ctypes.c_int, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                                 _u64p, _u64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -388,21 +389,28 @@ def shared_state_sync(bufs):
     return resent, list(hashes), list(sent), list(recv)
 
 
-def ring_allreduce_ft(bufs, faults=(), dt=None):
-    """Ring allreduce with injected faults [(rank, step), ...] (see
-    orc_ring_allreduce_ft).  Returns a dict with status, attempts,
-    dead_attempt, dead_step, survivors, sent, recv."""
+def ring_allreduce_ft(bufs, faults=(), deadline_ms=0, dt=None):
+    """Ring allreduce with injected faults [(rank, step) or (rank, step,
+    stall_ms), ...] and a receive deadline (see orc_ring_allreduce_ft).
+    Returns a dict with status, attempts, dead_attempt, dead_step,
+    dead_reason, waited_ms, survivors, sent, recv."""
     dt = _dt_of(bufs[0], dt)
     n = len(bufs)
-    fr = np.ascontiguousarray(np.array([f[0] for f in faults] or [0], dtype=np.int32))
-    fs = np.ascontiguousarray(np.array([f[1] for f in faults] or [1], dtype=np.int32))
+    fs_ = [tuple(f) + (0,) * (3 - len(f)) for f in faults]
+    fr = np.ascontiguousarray(np.array([f[0] for f in fs_] or [0], dtype=np.int32))
+    fs = np.ascontiguousarray(np.array([f[1] for f in fs_] or [1], dtype=np.int32))
+    fw = np.ascontiguousarray(np.array([f[2] for f in fs_] or [0], dtype=np.int32))
     da = np.zeros(n, dtype=np.int32)
     ds = np.zeros(n, dtype=np.int32)
+    dr = np.zeros(n, dtype=np.int32)
     att = np.zeros(1, dtype=np.int32)
+    waited = np.zeros(1, dtype=np.int64)
     sent, recv = _traffic(n)
-    rc = lib().orc_ring_allreduce_ft(_ptrs(bufs), n, bufs[0].size, dt, fr.ctypes.data, fs.ctypes.data, len(faults),
-                                     att.ctypes.data, da.ctypes.data, ds.ctypes.data, sent, recv)
+    rc = lib().orc_ring_allreduce_ft(_ptrs(bufs), n, bufs[0].size, dt, fr.ctypes.data, fs.ctypes.data, fw.ctypes.data,
+                                     len(fs_), deadline_ms, att.ctypes.data, da.ctypes.data, ds.ctypes.data,
+                                     dr.ctypes.data, waited.ctypes.data, sent, recv)
     if rc not in (0, EABORT):
         raise ValueError(f"oracle ring_allreduce_ft rejected its arguments (status {rc})")
     return {"status": rc, "attempts": int(att[0]), "dead_attempt": da.tolist(), "dead_step": ds.tolist(),
+            "dead_reason": dr.tolist(), "waited_ms": int(waited[0]),
             "survivors": [r for r in range(n) if da[r] == 0], "sent": list(sent), "recv": list(recv)}

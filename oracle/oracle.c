@@ -877,24 +877,34 @@ int orc_shared_state_sync(void* const* bufs, int n, size_t nbytes, uint64_t* has
 enum { ORC_EABORT = 2 };
 
 /* Ring allreduce with injected faults.  Fault i says: rank fault_rank[i]
- * stops before step fault_step[i] (steps counted 1 .. 2(M-1) within one
+ * fails before step fault_step[i] (steps counted 1 .. 2(M-1) within one
  * pass over M members: reduce-scatter steps first, then allgather steps).
- * Before each step the members are checked; a fault fires the first time a
- * pass reaches its step while its rank is still a member.  A pass that
- * meets a fired fault is abandoned: every rank's buffer is restored from the
- * snapshot taken on entry, the failed ranks leave the ring, and a new pass
- * starts over the survivors (ascending rank order, the ring closing over the
- * gaps, chunk length from the survivor count).  Bytes of abandoned steps
- * count in the traffic.  Out: attempts = passes started; dead_attempt[r] /
- * dead_step[r] = pass and step at which rank r was found failed (0 = never).
- * Returns ORC_OK when a pass completed, ORC_EABORT when no rank is left
- * (buffers restored). */
+ * fault_stall[i] = 0: the rank is gone, and the check before the step finds
+ * it at once.  fault_stall[i] = s > 0: the rank stops answering for s ms;
+ * with a receive deadline D > 0 ([P2] exercise: a stuck rank raises a
+ * deadline error instead of hanging) it is declared failed after D ms when
+ * s > D, and the step goes ahead after s ms when s <= D; with D <= 0 every
+ * stall is waited out.  The members are checked together before a step, so
+ * the wait before a step is the largest wait any of its faults causes.
+ * A fault fires the first time a pass reaches its step while its rank is
+ * still a member.  A pass that meets a failed member is abandoned: every
+ * rank's buffer is restored from the snapshot taken on entry, the failed
+ * ranks leave the ring, and a new pass starts over the survivors (ascending
+ * rank order, the ring closing over the gaps, chunk length from the survivor
+ * count).  Bytes of abandoned steps count in the traffic.  Out: attempts =
+ * passes started; dead_attempt[r] / dead_step[r] = pass and step at which
+ * rank r was found failed (0 = never); dead_reason[r] = 0 alive, 1 gone,
+ * 2 deadline; *waited_ms = total wait.  Returns ORC_OK when a pass
+ * completed, ORC_EABORT when no rank is left (buffers restored). */
 int orc_ring_allreduce_ft(void* const* bufs, int n, size_t count, int dt, const int* fault_rank,
-                          const int* fault_step, int nfaults, int* attempts, int* dead_attempt, int* dead_step,
-                          uint64_t* sent, uint64_t* recv) {
-  if (!check_bufs(bufs, n, dt) || nfaults < 0 || (nfaults && (!fault_rank || !fault_step))) return ORC_EINVAL;
+                          const int* fault_step, const int* fault_stall, int nfaults, int deadline_ms, int* attempts,
+                          int* dead_attempt, int* dead_step, int* dead_reason, long long* waited_ms, uint64_t* sent,
+                          uint64_t* recv) {
+  if (!check_bufs(bufs, n, dt) || nfaults < 0 || nfaults > 256 ||
+      (nfaults && (!fault_rank || !fault_step || !fault_stall)))
+    return ORC_EINVAL;
   for (int i = 0; i < nfaults; ++i)
-    if (fault_rank[i] < 0 || fault_rank[i] >= n || fault_step[i] < 1) return ORC_EINVAL;
+    if (fault_rank[i] < 0 || fault_rank[i] >= n || fault_step[i] < 1 || fault_stall[i] < 0) return ORC_EINVAL;
   size_t bytes = count * dtype_size(dt);
   void* snap[ORC_MAXN];
   for (int r = 0; r < n; ++r) {
@@ -904,9 +914,10 @@ int orc_ring_allreduce_ft(void* const* bufs, int n, size_t count, int dt, const 
   int alive[ORC_MAXN], fired[256];
   for (int r = 0; r < n; ++r) {
     alive[r] = 1;
-    dead_attempt[r] = dead_step[r] = 0;
+    dead_attempt[r] = dead_step[r] = dead_reason[r] = 0;
   }
-  for (int i = 0; i < nfaults && i < 256; ++i) fired[i] = 0;
+  for (int i = 0; i < nfaults; ++i) fired[i] = 0;
+  long long waited = 0;
   int attempt = 0, rc = ORC_OK;
   for (;;) {
     ++attempt;
@@ -925,16 +936,25 @@ int orc_ring_allreduce_ft(void* const* bufs, int n, size_t count, int dt, const 
     size_t L = orc_chunk_len(count, m, 128);
     int aborted = 0;
     for (int g = 1; g <= 2 * (m - 1) && !aborted; ++g) {
+      long long wait = 0;
       for (int i = 0; i < nfaults; ++i) {
         if (fired[i] || fault_step[i] != g) continue;
         fired[i] = 1;
         int k = fault_rank[i];
         if (!alive[k]) continue;
+        int s = fault_stall[i];
+        if (s > 0 && (deadline_ms <= 0 || s <= deadline_ms)) { /* answers again in time */
+          if (s > wait) wait = s;
+          continue;
+        }
+        if (s > 0 && deadline_ms > wait) wait = deadline_ms;
         alive[k] = 0;
         dead_attempt[k] = attempt;
         dead_step[k] = g;
+        dead_reason[k] = s > 0 ? 2 : 1;
         aborted = 1;
       }
+      waited += wait;
       if (aborted) break;
       uint64_t ps[ORC_MAXN] = {0}, pr[ORC_MAXN] = {0};
       if (g <= m - 1) rs_step_L(sub, m, count, dt, g, L, ps, pr);
@@ -950,6 +970,7 @@ int orc_ring_allreduce_ft(void* const* bufs, int n, size_t count, int dt, const 
   if (rc == ORC_EABORT)
     for (int r = 0; r < n; ++r) memcpy(bufs[r], snap[r], bytes);
   *attempts = attempt;
+  *waited_ms = waited;
   for (int r = 0; r < n; ++r) free(snap[r]);
   return rc;
 }

@@ -174,3 +174,37 @@ def test_ft_rejects_bad_faults(orc):
     for f in ([(2, 1)], [(-1, 1)], [(0, 0)]):
         with pytest.raises(ValueError):
             orc.ring_allreduce_ft([x.copy() for x in xs], f)
+
+
+def test_ft_stall_within_deadline_keeps_the_rank(orc):
+    """A rank that stops answering for less than the deadline delays the step
+    and stays: the result is the plain ring, the wait is the stall."""
+    xs = inputs.gradient_like(4, 3000, salt=5)
+    a = [x.copy() for x in xs]
+    sa, _ = orc.ring_allreduce(a)
+    b = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(b, [(2, 3, 40)], deadline_ms=50)
+    assert rep["attempts"] == 1 and rep["survivors"] == [0, 1, 2, 3] and rep["waited_ms"] == 40
+    assert rep["dead_reason"] == [0, 0, 0, 0] and rep["sent"] == sa
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_ft_stall_past_deadline_is_a_failure(orc):
+    """Past the deadline the rank is declared failed after exactly the
+    deadline: same outcome as a crash at that step, with reason 2."""
+    xs = inputs.gradient_like(4, 3000, salt=6)
+    b = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(b, [(1, 2, 500), (3, 2, 20)], deadline_ms=50)
+    assert rep["survivors"] == [0, 2, 3] and rep["dead_reason"] == [0, 2, 0, 0]
+    assert rep["dead_attempt"] == [0, 1, 0, 0] and rep["dead_step"] == [0, 2, 0, 0]
+    assert rep["waited_ms"] == 50  # the two stalls at step 2 are waited for together
+    c = [x.copy() for x in xs]
+    crash = orc.ring_allreduce_ft(c, [(1, 2)], deadline_ms=50)
+    assert crash["dead_reason"] == [0, 1, 0, 0] and crash["waited_ms"] == 0
+    for u, v in zip(b, c):
+        assert np.array_equal(u, v)
+    # no deadline: every stall is waited out
+    d = [x.copy() for x in xs]
+    rep = orc.ring_allreduce_ft(d, [(1, 2, 500)], deadline_ms=0)
+    assert rep["survivors"] == [0, 1, 2, 3] and rep["waited_ms"] == 500
