@@ -310,20 +310,27 @@ int rar_rank_hashes(void* const* bufs, int nranks, size_t nbytes, void* workspac
 int rar_shared_state_sync(void* const* bufs, int nranks, size_t nbytes, void* workspace, size_t ws_bytes,
                           int* resent, uint64_t* hashes, void* stream);
 
-/* A failure injected from the host: `rank` stops before step `step` of a
- * pass (steps 1 .. 2(M-1) of a pass over M members, reduce-scatter steps
- * first). */
+/* A failure injected from the host before step `step` of a pass (steps
+ * 1 .. 2(M-1) of a pass over M members, reduce-scatter steps first).
+ * stall_ms = 0: `rank` is gone, and the check before the step finds it at
+ * once.  stall_ms > 0: `rank` stops answering for that long; see the
+ * deadline of rar_ring_allreduce_ft. */
 typedef struct rar_fault {
   int rank;
   int step;
+  int stall_ms;
 } rar_fault;
 
+enum { RAR_FT_ALIVE = 0, RAR_FT_GONE = 1, RAR_FT_DEADLINE = 2 };
+
 typedef struct rar_ft_report {
-  int attempts;                     /* passes started (1 when no fault fired) */
+  int attempts;                     /* passes started (1 when no member failed) */
   int nsurvivors;                   /* members of the pass that completed */
   int survivors[RAR_MAX_RANKS];     /* their ranks, ascending */
   int dead_attempt[RAR_MAX_RANKS];  /* pass in which rank r was found failed, 0 = never */
   int dead_step[RAR_MAX_RANKS];     /* step before which it was found failed */
+  int dead_reason[RAR_MAX_RANKS];   /* RAR_FT_ALIVE / _GONE / _DEADLINE */
+  long long waited_ms;              /* time the scheduler spent waiting on stalled members */
   uint64_t hash[RAR_MAX_RANKS];     /* rar_rank_hashes of every rank's final buffer */
 } rar_ft_report;
 
@@ -331,22 +338,30 @@ typedef struct rar_ft_report {
  * buffer plus the hash accumulators. */
 size_t rar_ft_workspace_bytes(int nranks, size_t count, int dtype);
 
-/* Ring allreduce that survives failing members.  The ring runs step by step
- * from the host (the stepwise schedule).  Before each step the host checks
- * the members against the fault list: a fault fires the first time a pass
- * reaches its step while its rank is still a member.  A pass that meets a
- * fired fault is abandoned: every rank's buffer is restored from the
- * snapshot taken on entry, the failed ranks leave the ring, and a new pass
- * runs over the survivors (ascending rank order, the ring closing over the
- * gaps, chunk length rar_chunk_len(count, M)).  On return the survivors
+/* Ring allreduce that survives failing members ([P1] retry on the
+ * remaining peers; [P2] exercise: a receive deadline turns a stuck rank
+ * into an error instead of a hang).  The ring runs step by step from the
+ * host (the stepwise schedule).  Before each step the host checks the
+ * members against the fault list: a fault fires the first time a pass
+ * reaches its step while its rank is still a member.  A gone member is
+ * found at once.  A stalled member is waited for: with deadline_ms > 0 it is
+ * declared failed after deadline_ms if its stall is longer, otherwise the
+ * step goes ahead once it answers; deadline_ms <= 0 waits out every stall.
+ * Members are checked together, so the wait before a step is the largest
+ * one its faults cause (the host thread sleeps that long).  A pass that
+ * meets a failed member is abandoned: every rank's buffer is restored from
+ * the snapshot taken on entry, the failed ranks leave the ring, and a new
+ * pass runs over the survivors (ascending rank order, the ring closing over
+ * the gaps, chunk length rar_chunk_len(count, M)).  On return the survivors
  * hold the ring allreduce of their inputs, failed ranks hold their inputs,
  * and report->hash lets the caller confirm the survivors agree.
  * rar_last_traffic counts every step that ran, abandoned ones included.
  * Returns RAR_OK when a pass completed, RAR_EABORT when every rank failed
- * (all buffers restored).  Faults: 0 <= rank < nranks, step >= 1, at most
- * 256.  Synchronises `stream` (for the hashes). */
+ * (all buffers restored).  Faults: 0 <= rank < nranks, step >= 1,
+ * stall_ms >= 0, at most 256.  Synchronises `stream` (for the hashes). */
 int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype, const rar_fault* faults,
-                          int nfaults, void* workspace, size_t ws_bytes, rar_ft_report* report, void* stream);
+                          int nfaults, int deadline_ms, void* workspace, size_t ws_bytes, rar_ft_report* report,
+                          void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* Gradient bucketing ([P2] production patterns: fuse small gradients     */

@@ -31,15 +31,17 @@ _u64p = ctypes.POINTER(ctypes.c_uint64)
 
 
 class Fault(ctypes.Structure):
-    """Mirror of rar_fault: `rank` stops before `step` of a pass."""
-    _fields_ = [("rank", ctypes.c_int), ("step", ctypes.c_int)]
+    """Mirror of rar_fault: before `step` of a pass `rank` is gone
+    (stall_ms = 0) or stops answering for stall_ms."""
+    _fields_ = [("rank", ctypes.c_int), ("step", ctypes.c_int), ("stall_ms", ctypes.c_int)]
 
 
 class FtReport(ctypes.Structure):
     """Mirror of rar_ft_report."""
     _fields_ = [("attempts", ctypes.c_int), ("nsurvivors", ctypes.c_int),
                 ("survivors", ctypes.c_int * 64), ("dead_attempt", ctypes.c_int * 64),
-                ("dead_step", ctypes.c_int * 64), ("hash", ctypes.c_uint64 * 64)]
+                ("dead_step", ctypes.c_int * 64), ("dead_reason", ctypes.c_int * 64),
+                ("waited_ms", ctypes.c_longlong), ("hash", ctypes.c_uint64 * 64)]
 
 
 class CompressCfg(ctypes.Structure):
@@ -94,8 +96,8 @@ _SIGS = {
     "rar_shared_state_sync": (_c_int, [_c_vp, _c_int, _c_size, _c_vp, _c_size, ctypes.POINTER(ctypes.c_int),
                                        _u64p, _c_vp]),
     "rar_ft_workspace_bytes": (_c_size, [_c_int, _c_size, _c_int]),
-    "rar_ring_allreduce_ft": (_c_int, [_c_vp, _c_int, _c_size, _c_int, ctypes.POINTER(Fault), _c_int, _c_vp,
-                                       _c_size, ctypes.POINTER(FtReport), _c_vp]),
+    "rar_ring_allreduce_ft": (_c_int, [_c_vp, _c_int, _c_size, _c_int, ctypes.POINTER(Fault), _c_int, _c_int,
+                                       _c_vp, _c_size, ctypes.POINTER(FtReport), _c_vp]),
     "rar_bucket_plan": (_c_size, [_c_vp, _c_size, _c_int, _c_size, _c_vp]),
     "rar_bucketed_workspace_bytes": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size]),
     "rar_bucketed_allreduce": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_vp, _c_size,
@@ -363,20 +365,22 @@ def ft_workspace_bytes(nranks: int, count: int, dtype: int) -> int:
     return lib().rar_ft_workspace_bytes(nranks, count, dtype)
 
 
-def ring_allreduce_ft(bufs, faults, workspace, stream=None):
-    """Ring allreduce with injected faults [(rank, step), ...].  Returns a
-    dict: status (0 or EABORT), attempts, survivors, dead_attempt, dead_step,
-    hash (per rank)."""
+def ring_allreduce_ft(bufs, faults, workspace, deadline_ms: int = 0, stream=None):
+    """Ring allreduce with injected faults [(rank, step) or (rank, step,
+    stall_ms), ...] and a receive deadline.  Returns a dict: status (0 or
+    EABORT), attempts, survivors, dead_attempt, dead_step, dead_reason,
+    waited_ms, hash (per rank)."""
     n = len(bufs)
-    arr = (Fault * max(1, len(faults)))(*[Fault(int(r), int(s)) for r, s in faults])
+    fl = [tuple(f) + (0,) * (3 - len(f)) for f in faults]
+    arr = (Fault * max(1, len(fl)))(*[Fault(int(r), int(s), int(w)) for r, s, w in fl])
     rep = FtReport()
-    rc = lib().rar_ring_allreduce_ft(_rank_ptrs(bufs), n, bufs[0].numel(), dtype_code(bufs[0]), arr, len(faults),
-                                     *_ws(workspace), ctypes.byref(rep), _stream(stream, bufs[0]))
+    rc = lib().rar_ring_allreduce_ft(_rank_ptrs(bufs), n, bufs[0].numel(), dtype_code(bufs[0]), arr, len(fl),
+                                     deadline_ms, *_ws(workspace), ctypes.byref(rep), _stream(stream, bufs[0]))
     if rc not in (0, EABORT):
         _check(rc, "rar_ring_allreduce_ft")
     return {"status": rc, "attempts": rep.attempts, "survivors": list(rep.survivors)[:rep.nsurvivors],
             "dead_attempt": list(rep.dead_attempt)[:n], "dead_step": list(rep.dead_step)[:n],
-            "hash": list(rep.hash)[:n]}
+            "dead_reason": list(rep.dead_reason)[:n], "waited_ms": rep.waited_ms, "hash": list(rep.hash)[:n]}
 
 
 # ------------------------------------------------------------------ bucketing

@@ -13,8 +13,10 @@
 // stream, and after an event the receiver's decompress + reduce of unit u
 // runs on a second stream while unit u+1 is being compressed.
 #include <algorithm>
+#include <chrono>
 #include <cstring>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include "launch.hpp"
@@ -867,13 +869,15 @@ size_t rar_ft_workspace_bytes(int nranks, size_t count, int dtype) {
 }
 
 int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype, const rar_fault* faults,
-                          int nfaults, void* workspace, size_t ws_bytes, rar_ft_report* report, void* stream) {
+                          int nfaults, int deadline_ms, void* workspace, size_t ws_bytes, rar_ft_report* report,
+                          void* stream) {
   const size_t es = es_of(dtype);
   int rc = check_bufs(bufs, nranks, dtype, count * es);
   if (rc) return rc;
   if (!report || nfaults < 0 || nfaults > 256 || (nfaults && !faults)) return RAR_EINVAL;
   for (int i = 0; i < nfaults; ++i)
-    if (faults[i].rank < 0 || faults[i].rank >= nranks || faults[i].step < 1) return RAR_EINVAL;
+    if (faults[i].rank < 0 || faults[i].rank >= nranks || faults[i].step < 1 || faults[i].stall_ms < 0)
+      return RAR_EINVAL;
   if (!workspace || ws_bytes < rar_ft_workspace_bytes(nranks, count, dtype)) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
   hipStream_t st = (hipStream_t)stream;
@@ -912,15 +916,26 @@ int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype
     bool aborted = false;
     for (int g = 1; g <= 2 * (m - 1); ++g) {
       // liveness check of the members before step g
+      long long wait = 0;
       for (int i = 0; i < nfaults; ++i) {
         if (fired[(size_t)i] || faults[i].step != g) continue;
         fired[(size_t)i] = 1;
-        const int k = faults[i].rank;
+        const int k = faults[i].rank, stall = faults[i].stall_ms;
         if (!alive[k]) continue;
+        if (stall > 0 && (deadline_ms <= 0 || stall <= deadline_ms)) {  // answers again in time
+          wait = std::max<long long>(wait, stall);
+          continue;
+        }
+        if (stall > 0) wait = std::max<long long>(wait, deadline_ms);
         alive[k] = false;
         report->dead_attempt[k] = attempt;
         report->dead_step[k] = g;
+        report->dead_reason[k] = stall > 0 ? RAR_FT_DEADLINE : RAR_FT_GONE;
         aborted = true;
+      }
+      if (wait > 0) {
+        std::this_thread::sleep_for(std::chrono::milliseconds(wait));
+        report->waited_ms += wait;
       }
       if (aborted) break;
       const bool rs = g <= m - 1;

@@ -198,12 +198,14 @@ def test_ft_workspace_and_argument_errors():
     rep = rar.FtReport()
     faults = (rar.Fault * 1)(rar.Fault(2, 1))
     ws = base + (8 << 20)
-    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 1 << 20, ctypes.byref(rep), None) == 1
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, 0, ws, 1 << 20, ctypes.byref(rep), None) == 1
     faults[0] = rar.Fault(1, 0)
-    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 1 << 20, ctypes.byref(rep), None) == 1
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, 0, ws, 1 << 20, ctypes.byref(rep), None) == 1
+    faults[0] = rar.Fault(1, 1, -5)
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, 0, ws, 1 << 20, ctypes.byref(rep), None) == 1
     faults[0] = rar.Fault(1, 1)
-    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 64, ctypes.byref(rep), None) == 4
-    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, ws, 1 << 20, None, None) == 1
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, 0, ws, 64, ctypes.byref(rep), None) == 4
+    assert lib.rar_ring_allreduce_ft(ptrs, 2, 256, rar.F32, faults, 1, 0, ws, 1 << 20, None, None) == 1
     hs = (ctypes.c_uint64 * 2)()
     assert lib.rar_rank_hashes(ptrs, 2, 64, ws, 100, hs, None) == 4
     assert lib.rar_rank_hashes(ptrs, 2, 64, ws + 8, 512, hs, None) == 3
@@ -219,11 +221,14 @@ def test_hash_of_empty_buffers_needs_no_device(orc):
 
 
 def _fault_plans(n, seed):
+    """(rank, step, stall_ms) plans; stalls of 1-4 ms against a 2 ms deadline."""
     g = np.random.default_rng(seed)
-    plans = [[], [(0, 1)], [(n - 1, max(1, 2 * (n - 1)))], [(r, 1) for r in range(n)]]
+    plans = [[], [(0, 1, 0)], [(n - 1, max(1, 2 * (n - 1)), 0)], [(r, 1, 0) for r in range(n)],
+             [(0, 1, 1), (n - 1, 1, 3)]]
     for _ in range(20):
         k = int(g.integers(1, 5))
-        plans.append([(int(g.integers(0, n)), int(g.integers(1, 2 * n))) for _ in range(k)])
+        plans.append([(int(g.integers(0, n)), int(g.integers(1, 2 * n)), int(g.choice([0, 0, 1, 3])))
+                      for _ in range(k)])
     return plans
 
 
@@ -234,11 +239,16 @@ def test_ft_scheduler_matches_oracle_on_empty_buffers(orc, n):
     base = 1 << 40
     lib = rar.lib()
     ptrs = (ctypes.c_void_p * n)(*[base + i * 4096 for i in range(n)])
+    import time
     for plan in _fault_plans(n, n):
-        arr = (rar.Fault * max(1, len(plan)))(*[rar.Fault(r, s) for r, s in plan])
+        arr = (rar.Fault * max(1, len(plan)))(*[rar.Fault(r, s, w) for r, s, w in plan])
         rep = rar.FtReport()
-        rc = lib.rar_ring_allreduce_ft(ptrs, n, 0, rar.F32, arr, len(plan), base, 512, ctypes.byref(rep), None)
-        ref = orc.ring_allreduce_ft([np.zeros(0, np.float32) for _ in range(n)], plan)
+        t = time.perf_counter()
+        rc = lib.rar_ring_allreduce_ft(ptrs, n, 0, rar.F32, arr, len(plan), 2, base, 512, ctypes.byref(rep), None)
+        took_ms = (time.perf_counter() - t) * 1e3
+        ref = orc.ring_allreduce_ft([np.zeros(0, np.float32) for _ in range(n)], plan, deadline_ms=2)
+        assert list(rep.dead_reason)[:n] == ref["dead_reason"], plan
+        assert rep.waited_ms == ref["waited_ms"] and took_ms >= rep.waited_ms * 0.99, plan
         assert rc == (rar.EABORT if ref["status"] == orc.EABORT else 0), plan
         assert rep.attempts == ref["attempts"], plan
         assert list(rep.survivors)[:rep.nsurvivors] == ref["survivors"], plan

@@ -58,7 +58,8 @@ def test_shared_state_sync_matches_oracle(n):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
 
 
-PLANS = [[], [(2, 1)], [(0, 5)], [(4, 3), (1, 1)], [(3, 9), (5, 2), (6, 6)], [(7, 14)], [(1, 1), (6, 1)]]
+PLANS = [[], [(2, 1)], [(0, 5)], [(4, 3), (1, 1)], [(3, 9), (5, 2), (6, 6)], [(7, 14)], [(1, 1), (6, 1)],
+         [(2, 4, 5), (6, 4, 30)], [(0, 2, 3)]]  # (rank, step, stall ms) against a 20 ms deadline
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
@@ -68,12 +69,12 @@ def test_ft_ring_matches_oracle(dt, plan, count):
     n = 8
     xs = inputs.gradient_like(n, count, dtype=dt, salt=count + len(plan))
     ref = [x.copy() for x in xs]
-    orep = oracle.ring_allreduce_ft(ref, plan, dt=DT_NAMES[dt])
+    orep = oracle.ring_allreduce_ft(ref, plan, deadline_ms=20, dt=DT_NAMES[dt])
     bufs = to_dev(xs, dt)
     ws = _ws(rar.ft_workspace_bytes(n, count, DT_NAMES[dt]))
-    rep = rar.ring_allreduce_ft(bufs, plan, ws)
+    rep = rar.ring_allreduce_ft(bufs, plan, ws, deadline_ms=20)
     assert rep["status"] == orep["status"] == 0
-    for key in ("attempts", "survivors", "dead_attempt", "dead_step"):
+    for key in ("attempts", "survivors", "dead_attempt", "dead_step", "dead_reason", "waited_ms"):
         assert rep[key] == orep[key], key
     assert rar.last_traffic(n) == (orep["sent"], orep["recv"])
     got = to_host(bufs, dt)
