@@ -405,6 +405,20 @@ def extra_legs(args):
         "ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
         "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del ws
+    # forwarding schedule: materialised messages, one decode+add+encode kernel per hop.
+    # Its own traffic per element: hop 0 encode 2 + 1.008, N-1 forwarding hops
+    # 1.008 + 2 + 1.008, allgather fan-out 1.008 + 2N (fp16, m = 8).
+    cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"], schedule=rar.SCHED_FORWARD)
+    ws = torch.empty(rar.compressed_workspace_bytes(wb["n"], wb["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    ms, k, _ = time_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, 2, steps)
+    mb = 1.0 + 1.0 / 128
+    own = wb["count"] * ((2 + mb) + (wb["n"] - 1) * (2 * mb + 2) + (mb + 2 * wb["n"]))
+    out["bfp8_allreduce_forward"] = {
+        "ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
+        "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "own_bytes": int(own), "frac_of_roofline_own_bytes": round(own / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del ws
     # the same fused ring with per-rank error-feedback state (state read and
     # rewritten once per element per rank: 8 more bytes per element per rank)
     cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"], schedule=rar.SCHED_FUSED)

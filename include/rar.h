@@ -204,9 +204,13 @@ typedef enum rar_comp {
 enum { RAR_OP_ALLREDUCE = 1u, RAR_OP_ALLGATHER = 2u, RAR_OP_BROADCAST = 4u };
 
 typedef enum rar_sched {
-  RAR_SCHED_FUSED = 0,  /* one launch, per-block hop chain in registers (BFP only) */
-  RAR_SCHED_STAGED = 1  /* messages materialised per pipeline unit; encode and
-                           decode on two streams ordered by events */
+  RAR_SCHED_FUSED = 0,   /* one launch, per-block hop chain in registers (BFP only) */
+  RAR_SCHED_STAGED = 1,  /* messages materialised per pipeline unit; encode and
+                            decode on two streams ordered by events */
+  RAR_SCHED_FORWARD = 2  /* messages materialised per unit (BFP only); hop by
+                            hop, every receiver decodes, adds its own copy and
+                            encodes its next message in one kernel, without
+                            writing the partial sum back; one launch per hop */
 } rar_sched;
 
 typedef struct rar_compress_cfg {

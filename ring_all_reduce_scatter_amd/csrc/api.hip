@@ -213,7 +213,8 @@ int cfg_check(const rar_compress_cfg* cfg, int dt, CompPlan* pl) {
   if (cfg->method < RAR_COMP_NONE || cfg->method > RAR_COMP_SPARSE_AUTO) return RAR_EINVAL;
   if (cfg->mbits < 2 || cfg->mbits > 8) return RAR_EINVAL;
   if (cfg->block < 16 || cfg->block > 512 || (cfg->block & (cfg->block - 1))) return RAR_EINVAL;
-  if (cfg->schedule != RAR_SCHED_FUSED && cfg->schedule != RAR_SCHED_STAGED) return RAR_EINVAL;
+  if (cfg->schedule != RAR_SCHED_FUSED && cfg->schedule != RAR_SCHED_STAGED && cfg->schedule != RAR_SCHED_FORWARD)
+    return RAR_EINVAL;
   const size_t es = es_of(dt);
   if (cfg->unit_bytes == 0 || cfg->unit_bytes % es) return RAR_EINVAL;
   const size_t U = cfg->unit_bytes / es;
@@ -249,6 +250,7 @@ size_t tiles_per_slot(const CompPlan& pl) { return 2 * (size_t)comp_tiles_per_un
 
 size_t workspace_need(const CompPlan& pl) {
   if (pl.method == RAR_COMP_NONE || pl.sched == RAR_SCHED_FUSED) return kTrafficBytes;
+  if (pl.sched == RAR_SCHED_FORWARD) return slots_offset() + 2 * (size_t)pl.n * pl.upc * pl.slot;
   size_t need = tiles_offset(pl);
   if (pl.method == RAR_COMP_SPARSE_AUTO) need += (size_t)pl.n * pl.upc * tiles_per_slot(pl) * sizeof(uint32_t);
   return need;
@@ -430,6 +432,69 @@ int staged_sparse(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t s
   if (hipEventRecord(ctx->join, D) != hipSuccess || hipStreamWaitEvent(E, ctx->join, 0) != hipSuccess)
     return RAR_EHIP;
   return RAR_OK;
+}
+
+// Forwarding BFP ring: message slots [parity][rank][unit] in the workspace.
+// Hop 0: every rank q encodes its own chunk (q-1) mod N, the one it sends at
+// reduce-scatter step 1.  Hop s = 1..N-1: receiver r decodes rank r-1's
+// message of chunk (r-s-1) mod N, adds its own copy and encodes the sum as
+// its next message (at s = N-1 r owns the chunk and the message is the
+// allgather's).  Then every rank stores the owners' messages decoded.
+int forward_bfp(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t st) {
+  const int n = pl.n;
+  char* slots = ws + slots_offset();
+  auto slot = [&](int parity, int rank, size_t u) {
+    return (uint8_t*)(slots + (((size_t)parity * n + rank) * pl.upc + u) * pl.slot);
+  };
+  int rc;
+  FwdJobs jobs{};
+  auto flush = [&]() -> int {
+    if (jobs.njobs == 0) return RAR_OK;
+    const int r = hip_rc(launch_bfp_forward(jobs, pl.dt, pl.block, pl.mbits, st));
+    jobs.njobs = 0;
+    return r;
+  };
+  for (int s = 0; s <= n - 1; ++s) {
+    for (int r = 0; r < n; ++r) {
+      const int c = modn(r - s - 1, n);
+      size_t lo, hi;
+      chunk_range(pl.count, pl.L, c, &lo, &hi);
+      for (size_t u = 0; u < pl.upc; ++u) {
+        const size_t ulo = lo + u * pl.U;
+        if (ulo >= hi) break;
+        const int j = jobs.njobs++;
+        jobs.in[j] = s == 0 ? nullptr : slot((s - 1) & 1, modn(r - 1, n), u);
+        jobs.local[j] = (const char*)bufs[r] + ulo * pl.es;
+        jobs.out[j] = slot(s & 1, r, u);
+        jobs.len[j] = std::min(pl.U, hi - ulo);
+        if (jobs.njobs == kMaxRanks && (rc = flush())) return rc;
+      }
+    }
+    if ((rc = flush())) return rc;  // hop s+1 reads what hop s wrote: stream order separates them
+  }
+  RankPtrs fan = make_ptrs(bufs, n);
+  BfpJobs ag{};
+  uint64_t off[kMaxRanks] = {};
+  auto flush_ag = [&]() -> int {
+    if (ag.njobs == 0) return RAR_OK;
+    const int r = hip_rc(launch_bfp_decode_fanout(ag, fan, n, off, pl.dt, pl.block, pl.mbits, st));
+    ag.njobs = 0;
+    return r;
+  };
+  for (int c = 0; c < n; ++c) {
+    size_t lo, hi;
+    chunk_range(pl.count, pl.L, c, &lo, &hi);
+    for (size_t u = 0; u < pl.upc; ++u) {
+      const size_t ulo = lo + u * pl.U;
+      if (ulo >= hi) break;
+      const int j = ag.njobs++;
+      ag.msg[j] = slot((n - 1) & 1, c, u);
+      ag.len[j] = std::min(pl.U, hi - ulo);
+      off[j] = ulo;
+      if (ag.njobs == kMaxRanks && (rc = flush_ag())) return rc;
+    }
+  }
+  return flush_ag();
 }
 
 void fused_bfp_traffic(const CompPlan& pl, Traffic& tr) {
@@ -761,6 +826,9 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
       if ((rc = hip_rc(launch_bfp_ring_fold(make_ptrs(bufs, nranks), nranks, count, pl.L, dtype, pl.block,
                                             pl.mbits, st))))
         return rc;
+    } else if (pl.sched == RAR_SCHED_FORWARD) {
+      fused_bfp_traffic(pl, tr);
+      if ((rc = forward_bfp(pl, bufs, (char*)workspace, st))) return rc;
     } else {
       if ((rc = staged_bfp(pl, bufs, (char*)workspace, tr, st))) return rc;
     }

@@ -50,6 +50,40 @@ __global__ __launch_bounds__(kThreads) void bfp_encode_kernel(BfpJobs jobs, int 
   }
 }
 
+// Forwarding hop: decode the incoming message (if any), add it to the local
+// partial (local + received, rounded to the dtype) and encode the sum as the
+// outgoing message, in one pass; the sum itself is not written back.  Same
+// grid and lane rules as the encoder.
+template <int DT, int LPB>
+__global__ __launch_bounds__(kThreads) void bfp_forward_kernel(FwdJobs jobs, int lpb_rt, int mbits,
+                                                                uint32_t blocks_per_job) {
+  const int j = (int)(blockIdx.x / blocks_per_job);
+  const uint32_t b = blockIdx.x - (uint32_t)j * blocks_per_job;
+  const int lpb = LPB > 0 ? LPB : lpb_rt;
+  const uint64_t block = (uint64_t)lpb * 8;
+  const uint64_t count = jobs.len[j];
+  const char* local = jobs.local[j];
+  const uint8_t* in = jobs.in[j];
+  uint8_t* out = jobs.out[j];
+  const uint64_t nb = (count + block - 1) / block;
+  const uint64_t eb = (nb + 15) / 16 * 16;
+  const float qmax = (float)((1 << (mbits - 1)) - 1);
+  if (b == 0 && threadIdx.x < eb - nb) out[nb + threadIdx.x] = 0;  // exponent padding
+  const uint64_t ngroups = (count + 7) / 8;
+  const uint64_t stride = (uint64_t)blocks_per_job * kThreads;
+  for (uint64_t g0 = (uint64_t)b * kThreads; g0 < ngroups; g0 += stride) {
+    const uint64_t elem = (g0 + threadIdx.x) * 8;
+    const int nv = elem >= count ? 0 : (count - elem >= 8 ? 8 : (int)(count - elem));
+    G8 p = load_group<DT>(local, elem, nv);
+    if (in && nv > 0) {
+      const G8 d = dequant_group(in, eb, elem, nv, block, mbits);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p.v[i] = i < nv ? round_to<DT>(p.v[i] + d.v[i]) : 0.0f;
+    }
+    encode_group<DT, LPB>(p, nv, elem, out, out + eb, lpb, mbits, qmax);
+  }
+}
+
 template <int DT, bool ACC>
 __global__ __launch_bounds__(kThreads) void bfp_decode_kernel(BfpJobs jobs, int block, int mbits,
                                                                uint32_t blocks_per_job) {
@@ -547,6 +581,26 @@ void fold_state_dispatch(const RankPtrs& bufs, const RankPtrs& st, int n, uint64
 }
 
 }  // namespace
+
+hipError_t launch_bfp_forward(const FwdJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
+  uint64_t ml = 0;
+  for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
+  if (jobs.njobs == 0 || ml == 0) return hipSuccess;
+  const uint32_t bpj = blocks_for(ml);
+  dim3 grid((unsigned)(jobs.njobs * bpj));
+#define RAR_FWD(DTV)                                                                                          \
+  if (block == 128)                                                                                           \
+    hipLaunchKernelGGL((bfp_forward_kernel<DTV, 16>), grid, dim3(kThreads), 0, stream, jobs, 16, mbits, bpj); \
+  else                                                                                                        \
+    hipLaunchKernelGGL((bfp_forward_kernel<DTV, 0>), grid, dim3(kThreads), 0, stream, jobs, block / 8, mbits, bpj);
+  switch (dt) {
+    case DT_F32: RAR_FWD(DT_F32) break;
+    case DT_F16: RAR_FWD(DT_F16) break;
+    default: RAR_FWD(DT_BF16) break;
+  }
+#undef RAR_FWD
+  return hipGetLastError();
+}
 
 hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
   const uint64_t ml = max_len(jobs);

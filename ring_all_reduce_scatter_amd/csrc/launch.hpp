@@ -70,6 +70,17 @@ struct BfpJobs {
 };
 
 hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
+
+// Forwarding hop jobs: out <- encode(local (+) decode(in)), or encode(local)
+// when in is NULL; `len` elements each.
+struct FwdJobs {
+  const uint8_t* in[kMaxRanks];
+  const char* local[kMaxRanks];
+  uint8_t* out[kMaxRanks];
+  uint64_t len[kMaxRanks];
+  int njobs;
+};
+hipError_t launch_bfp_forward(const FwdJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
 // accumulate: dst <- dst (+) decoded; otherwise dst <- decoded.
 hipError_t launch_bfp_decode(const BfpJobs& jobs, int dt, int block, int mbits, bool accumulate,
                              hipStream_t stream);

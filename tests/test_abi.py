@@ -69,6 +69,9 @@ def test_compressed_workspace_sizes():
     ws = rar.compressed_workspace_bytes(8, 128 << 20, rar.F16, cfg)
     slot = (16384 + 2097152 + 255) // 256 * 256
     assert ws == 1024 + 8 * 8 * slot
+    cfg.schedule = rar.SCHED_FORWARD  # two slots per (rank, unit)
+    assert rar.compressed_workspace_bytes(8, 128 << 20, rar.F16, cfg) == 1024 + 2 * 8 * 8 * slot
+    cfg.schedule = rar.SCHED_STAGED
     cfg.unit_bytes = 1000  # not a multiple of the block
     assert rar.compressed_workspace_bytes(8, 1 << 20, rar.F16, cfg) == 0
 

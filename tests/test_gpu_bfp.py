@@ -95,7 +95,7 @@ def test_special_blocks_match_oracle():
 
 # ------------------------------------------------------------------ compressed ring
 
-SCHEDS = {"fused": rar.SCHED_FUSED, "staged": rar.SCHED_STAGED}
+SCHEDS = {"fused": rar.SCHED_FUSED, "staged": rar.SCHED_STAGED, "forward": rar.SCHED_FORWARD}
 
 
 def _run_compressed(xs, dt, sched, block=128, mbits=8, unit_elems=4096, method=rar.COMP_BFP):
@@ -114,7 +114,7 @@ def _run_compressed(xs, dt, sched, block=128, mbits=8, unit_elems=4096, method=r
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("sched", ["fused", "staged"])
+@pytest.mark.parametrize("sched", ["fused", "staged", "forward"])
 @pytest.mark.parametrize("mbits", [8, 4])
 def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
     count = n * 4096 * 2 + 1000  # several units per chunk and a ragged last chunk
@@ -128,7 +128,7 @@ def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
 
 
 @pytest.mark.parametrize("block", [16, 64, 256, 512])
-@pytest.mark.parametrize("sched", ["fused", "staged"])
+@pytest.mark.parametrize("sched", ["fused", "staged", "forward"])
 def test_compressed_allreduce_other_blocks(block, sched):
     n, count = 4, 4 * 8192 + 900
     xs = inputs.block_scaled(n, count, block=block, salt=block)
@@ -143,7 +143,7 @@ def test_compressed_integer_inputs_are_exact():
     n, count = 8, 8 * 4096
     xs = inputs.integers(n, count, dtype="f16", salt=5)
     exact = sum(x.astype(np.float64) for x in xs)
-    for sched in ("fused", "staged"):
+    for sched in ("fused", "staged", "forward"):
         got, _, _ = _run_compressed(xs, "f16", sched)
         for g in got:
             assert np.array_equal(g.astype(np.float64), exact)
@@ -217,12 +217,13 @@ def test_bfp8_workload_full_size_sampled():
 
 @pytest.mark.slow
 def test_bfp8_staged_equals_fused_full_size():
-    """The staged two-stream pipeline (4 MiB units) gives the fused kernel's bits."""
+    """The staged two-stream pipeline and the forwarding schedule (4 MiB
+    units) give the fused kernel's bits."""
     w = inputs.WORKLOADS["bfp8"]
     n, count = w["n"], w["count"] // 4
     xs = inputs.block_scaled(n, count, salt=3)
     outs = []
-    for sched in (rar.SCHED_FUSED, rar.SCHED_STAGED):
+    for sched in (rar.SCHED_FUSED, rar.SCHED_STAGED, rar.SCHED_FORWARD):
         cfg = rar.compress_cfg(mbits=8, unit_bytes=w["unit_bytes"], schedule=sched)
         ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8,
                          device="cuda:0")
@@ -230,7 +231,8 @@ def test_bfp8_staged_equals_fused_full_size():
         rar.ring_allreduce_compressed(bufs, cfg, ws)
         outs.append(bufs)
     for r in range(n):
-        assert torch.equal(outs[0][r].view(torch.int16), outs[1][r].view(torch.int16)), f"rank {r}"
+        assert torch.equal(outs[0][r].view(torch.int16), outs[1][r].view(torch.int16)), f"staged rank {r}"
+        assert torch.equal(outs[0][r].view(torch.int16), outs[2][r].view(torch.int16)), f"forward rank {r}"
 
 
 @pytest.mark.parametrize("mbits", [8, 4, 2])

@@ -91,6 +91,7 @@ def test_compressed_paths_stay_in_bounds(dt, n, count):
     xs = inputs.sparse_mix(n, count, dtype=dt, salt=n) if dt != "f32" else inputs.gradient_like(n, count, salt=n)
     cfgs = [("bfp fused", rar.compress_cfg(unit_bytes=8192)),
             ("bfp staged", rar.compress_cfg(unit_bytes=8192, schedule=rar.SCHED_STAGED)),
+            ("bfp forward", rar.compress_cfg(unit_bytes=8192, schedule=rar.SCHED_FORWARD)),
             ("bfp4 staged block 32", rar.compress_cfg(unit_bytes=4096, mbits=4, block=32, schedule=rar.SCHED_STAGED)),
             ("sparse auto", rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=4, unit_bytes=8192,
                                              schedule=rar.SCHED_STAGED))]
