@@ -405,6 +405,18 @@ def extra_legs(args):
         "ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
         "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del ws
+    # standalone encode (K4) and decode-accumulate (K5) over one rank's 256 MiB
+    x0 = sets[1][0]
+    msg = torch.empty(rar.bfp_bytes(wb["count"], 128, 8), dtype=torch.uint8, device="cuda:0")
+    mbytes = msg.numel()
+    ms, k, _ = time_leg(lambda b: rar.bfp_compress(b[0], 128, 8, msg), sets, 2, steps)
+    out["bfp8_compress_256MiB"] = {"ms": round(ms, 4), "bytes": Sb + mbytes,
+                                   "frac_of_roofline": round((Sb + mbytes) / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms, k, _ = time_leg(lambda b: rar.bfp_decompress_accumulate(msg, wb["count"], 128, 8, b[1]), sets, 2, steps)
+    out["bfp8_decompress_accumulate_256MiB"] = {
+        "ms": round(ms, 4), "bytes": mbytes + 2 * Sb,
+        "frac_of_roofline": round((mbytes + 2 * Sb) / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del msg, x0
     # forwarding schedule: materialised messages, one decode+add+encode kernel per hop.
     # Its own traffic per element: hop 0 encode 2 + 1.008, N-1 forwarding hops
     # 1.008 + 2 + 1.008, allgather fan-out 1.008 + 2N (fp16, m = 8).
