@@ -313,6 +313,116 @@ struct U64Vals {
   uint64_t v[kFillWords];
 };
 
+// ---------------------------------------------------------------- fp32 fused ring, quad layout
+// The fused compressed ring for binary32 buffers.  Eight consecutive floats
+// per lane would make every load and store instruction touch 16-byte pieces
+// 32 bytes apart; here a wavefront owns 512 consecutive elements and lane l
+// holds the quads [4l, 4l+4) ("A") and [256+4l, 256+4l+4) ("B"), so every
+// instruction covers 1 KiB of contiguous memory.  A block of b <= 256
+// elements is b/4 consecutive lanes of one quad set; a 512-element block is
+// the whole wavefront, both sets.  The arithmetic is the binary32 hop chain
+// of bfp_ring_fold_kernel, element for element.
+struct Q8 {
+  float v[8];
+};
+
+template <int NR, int LPBQ>
+__global__ __launch_bounds__(kThreads) void bfp_ring_fold_f32q_kernel(RankPtrs bufs, int nranks, uint64_t count,
+                                                                       uint64_t L, int block, int mbits) {
+  const int N = NR > 0 ? NR : nranks;
+  const uint32_t c = blockIdx.x % (uint32_t)N;
+  const uint32_t t = blockIdx.x / (uint32_t)N;
+  const uint64_t lo = (uint64_t)c * L;
+  if (lo >= count) return;
+  const uint64_t hi = lo + L < count ? lo + L : count;
+  const uint64_t tile0 = lo + (uint64_t)t * kThreads * kGroupElems;
+  if (tile0 >= hi) return;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t eA = tile0 + (uint64_t)(threadIdx.x >> 6) * 512 + 4 * lane, eB = eA + 256;
+  auto nq = [&](uint64_t e) { return e >= hi ? 0 : (hi - e >= 4 ? 4 : (int)(hi - e)); };
+  const int nA = nq(eA), nB = nq(eB);
+  const int lpbq = LPBQ > 0 ? LPBQ : (block >= 256 ? 64 : block / 4);
+  const bool whole = block == 512;
+  const float qmax = (float)((1 << (mbits - 1)) - 1);
+  auto ldq = [&](const char* base, uint64_t e, int nv, float* out) {
+    if (nv == 4) {
+      const u32x4 w = ld16<true>(base + e * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = i < nv ? ((const float*)base)[e + i] : 0.0f;
+    }
+  };
+  auto stq = [&](char* base, uint64_t e, int nv, const float* v) {
+    if (nv == 4) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+      st16<true>(base + e * 4, w);
+    } else {
+      for (int i = 0; i < nv; ++i) ((float*)base)[e + i] = v[i];
+    }
+  };
+  auto load = [&](int rank, Q8& q) {
+    ldq(bufs.p[rank], eA, nA, q.v);
+    ldq(bufs.p[rank], eB, nB, q.v + 4);
+  };
+  auto qdq = [&](const Q8& p) -> Q8 {
+    uint32_t ma = 0, mb = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ma = max(ma, absbits(p.v[i]));
+      mb = max(mb, absbits(p.v[4 + i]));
+    }
+    if (whole) {
+      ma = mb = group_max_u32<64>(max(ma, mb));
+    } else {
+      ma = group_max_sel<LPBQ>(ma, lpbq);
+      mb = group_max_sel<LPBQ>(mb, lpbq);
+    }
+    const BfpScale sa = bfp_scale(ma, mbits), sb = bfp_scale(mb, mbits);
+    const float nanv = __builtin_nanf("");
+    Q8 d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const BfpScale& sc = i < 4 ? sa : sb;
+      d.v[i] = sc.nan ? nanv : bfp_dq(bfp_q(p.v[i], sc.k, qmax), sc.k);
+    }
+    return d;
+  };
+  const int first = (int)c + 1 < N ? (int)c + 1 : 0;
+  Q8 p;
+  if constexpr (NR > 0) {
+    Q8 x[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) load(first + j < NR ? first + j : first + j - NR, x[j]);
+    p = x[0];
+#pragma unroll
+    for (int j = 1; j < NR; ++j) {
+      const Q8 d = qdq(p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p.v[i] = x[j].v[i] + d.v[i];
+    }
+  } else {
+    load(first, p);
+    int r = first;
+    for (int k = 2; k <= N; ++k) {
+      r = r + 1 == N ? 0 : r + 1;
+      Q8 x;
+      load(r, x);
+      const Q8 d = qdq(p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p.v[i] = x.v[i] + d.v[i];
+    }
+  }
+  const Q8 y = qdq(p);
+  for (int d = 0; d < N; ++d) {
+    stq(bufs.p[d], eA, nA, y.v);
+    stq(bufs.p[d], eB, nB, y.v + 4);
+  }
+}
+
 // ---------------------------------------------------------------- stateful fused ring
 // Error feedback (FB = 1) or delta coding (FB = 2) on the fused compressed
 // ring ("CCCL..." page, section 2.1 differential layer, section 5 error
@@ -543,11 +653,30 @@ void fold_dispatch_lpb(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, 
                        L, block / 8, mbits);
 }
 
+template <int NR>
+void fold_f32q_dispatch(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
+                        hipStream_t stream) {
+  const uint64_t tile = (uint64_t)kThreads * kGroupElems;
+  dim3 grid((unsigned)((uint64_t)n * ((L + tile - 1) / tile)));
+  const size_t lds = residency_lds(bfp_fold_wgs_per_cu(DT_F32));
+  if (block == 128)
+    hipLaunchKernelGGL((bfp_ring_fold_f32q_kernel<NR, 32>), grid, dim3(kThreads), lds, stream, bufs, n, count, L,
+                       block, mbits);
+  else
+    hipLaunchKernelGGL((bfp_ring_fold_f32q_kernel<NR, 0>), grid, dim3(kThreads), lds, stream, bufs, n, count, L,
+                       block, mbits);
+}
+
 template <int DT>
 void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int block, int mbits,
                       hipStream_t stream) {
-  if (n == 8) fold_dispatch_lpb<DT, 8>(bufs, n, count, L, block, mbits, stream);
-  else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, stream);
+  if constexpr (DT == DT_F32) {
+    if (n == 8) fold_f32q_dispatch<8>(bufs, n, count, L, block, mbits, stream);
+    else fold_f32q_dispatch<0>(bufs, n, count, L, block, mbits, stream);
+  } else {
+    if (n == 8) fold_dispatch_lpb<DT, 8>(bufs, n, count, L, block, mbits, stream);
+    else fold_dispatch_lpb<DT, 0>(bufs, n, count, L, block, mbits, stream);
+  }
 }
 
 // Workgroups per CU of the stateful fold.  Each lane holds N inputs and N
