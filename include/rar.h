@@ -19,7 +19,12 @@
  *       2.2 chunked compress -> communicate -> decompress -> reduce pipeline on
  *       separate streams synchronised by events, section 3.3 configuration
  *       (compression type, sparsity threshold, collective filter, 1-4 MB
- *       chunks), section 4.3 (compressed staging buffers cost memory).
+ *       chunks), section 4.3 (compressed staging buffers cost memory),
+ *       section 5 (error feedback).
+ *  [P1] "Prime Intellect 发布 PCCL 分布式训练通信库", section "PCCL 模型":
+ *       a shared state checked by hash and re-sent to peers off the
+ *       majority; a collective cut short by a failing peer is retried on the
+ *       remaining peers.
  *
  * Conventions for every call:
  *  - Device pointers are HIP device addresses, 16-byte aligned.  Host arrays
@@ -27,7 +32,10 @@
  *    read or written during the call only and may be reused on return.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously and is stream-ordered: buffers must stay alive until the
- *    stream has executed it.  The library allocates no device memory; where
+ *    stream has executed it.  The few calls that return device results to
+ *    the host (byte counters of the compressed calls, hashes, the
+ *    fault-tolerant ring) say so and synchronise the stream; every other
+ *    call can be captured in a HIP graph.  The library allocates no device memory; where
  *    scratch is needed the caller passes a workspace.
  *  - Errors in the arguments are reported synchronously, before anything is
  *    enqueued, by a nonzero rar_status; nothing is modified then.  A failed
