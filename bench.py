@@ -373,6 +373,10 @@ def extra_legs(args):
     out["fp32_reduce_scatter_fused"] = {"ms": round(ms, 4),
                                         "busbw_GBs": round(S * (n - 1) / n / (ms * 1e-3) / 1e9, 1),
                                         "frac_of_roofline": round((n * S + S) / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # tree allreduce at the same size (binomial reduce + broadcast, fused: N reads + N writes)
+    ms, k, _ = time_leg(lambda b: rar.tree_allreduce(b), sets, 2, steps)
+    out["fp32_tree_allreduce_fused"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S, n, ms), 1),
+                                        "frac_of_roofline": round(2 * n * S / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # shared-state hash of every rank's buffer (reads N*S bytes; one host sync)
     hws = torch.empty(rar.HASH_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
     ms, k, _ = time_leg(lambda b: rar.rank_hashes(b, hws), sets, 2, steps)
