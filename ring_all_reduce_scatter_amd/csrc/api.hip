@@ -1,6 +1,8 @@
 // C-ABI of librar.so: argument checking, the ring's chunk scheduler, byte
-// accounting and the staged compress/decompress pipeline.  Kernels live in
-// ring_kernels.hip and bfp_kernels.hip; this file only plans and launches.
+// accounting, the staged and forwarding compressed schedules, the tree,
+// bucket, stateful and fault-tolerant entry points.  Kernels live in
+// ring_kernels.hip, bfp_kernels.hip, sparse_kernels.hip, bucket_kernels.hip
+// and hash_kernels.hip; this file only plans, checks and launches.
 //
 // Ring schedule (page "从零实现集合通信", two-pass ring allreduce section):
 // reduce-scatter step s = 1..N-1: rank r receives chunk (r-s-1) mod N from

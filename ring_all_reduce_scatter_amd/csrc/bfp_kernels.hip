@@ -4,7 +4,9 @@
 // communicate -> decompress -> reduce).
 //
 // Lane layout: a lane owns 8 consecutive elements, so a block of B elements
-// is B/8 consecutive lanes (16 lanes = one DPP row for B = 128).  The block's
+// is B/8 consecutive lanes (16 lanes = one DPP row for B = 128).  (The fused
+// ring over binary32 buffers uses a quad layout instead; see
+// bfp_ring_fold_f32q_kernel.)  The block's
 // exponent is the max of |x| bit patterns, reduced across those lanes with
 // DPP (group_max_u32): E = bits >> 23 (255 when an Inf/NaN is present).
 // With e = max(E,1) - 127 and k = m - 2 - e every element is
