@@ -197,6 +197,7 @@ def fp32_leg(args):
     S = count * 4
     log(f"[bench] fp32 leg: timing {args.steps} steps on {nsets - 1} sets")
     ms, kern_ms, kern_min = time_leg(lambda bufs: rar.ring_allreduce(bufs), sets, args.warmup, args.steps)
+    sent, recv = rar.last_traffic(n)  # logical bytes per rank of the last call
     first = [t.cpu().numpy() for t in sets[1]]
     del sets
     torch.cuda.empty_cache()
@@ -205,6 +206,7 @@ def fp32_leg(args):
     sources = COUNTER_KERNELS["ring_fold_f32_n8"]["sources"]
     res = {
         "n": n, "count": count, "S": S, "ms": ms, "kern_ms": kern_ms, "kern_min_ms": kern_min,
+        "bytes_per_rank": {"sent": sent, "recv": recv},
         "busbw": busbw(S, n, ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -560,6 +562,27 @@ def counters_run(reps=3):
     log("[bench] counters run done")
 
 
+def write_jsonl(path, line, f):
+    """Per-leg records for the byte-counter log ([P2] exercise: per-rank byte
+    counters written as JSON lines): the headline leg with every rank's
+    logical bytes, the BFP-8 leg with its wire bytes, one record per extra leg."""
+    stamp = time.strftime("%Y-%m-%dT%H:%M:%S")
+    recs = [{"time": stamp, "leg": "fp32_allreduce_fused", "workload": line["config"]["workload"],
+             "ms_per_step": line["ms_per_step"], "kernel_ms": line["kernel_ms"], "busbw_rank_GBs": line["value"],
+             "roofline": line["roofline"], "sent_bytes_per_rank": f["bytes_per_rank"]["sent"],
+             "recv_bytes_per_rank": f["bytes_per_rank"]["recv"]}]
+    if "bfp8" in line:
+        b = line["bfp8"]
+        recs.append({"time": stamp, "leg": "bfp8_allreduce_fused", "workload": b["config"]["workload"],
+                     "ms_per_step": b["ms_per_step"], "busbw_rank_GBs": b["value"], "roofline": b["roofline"],
+                     "wire_bytes_rank0": b["wire_bytes_per_rank"]})
+    for k, v in line.get("extra", {}).items():
+        recs.append({"time": stamp, "leg": k, **v})
+    with open(path, "a") as fh:
+        for r in recs:
+            fh.write(json.dumps(r) + "\n")
+
+
 def _counter_values(path, counter, match):
     import csv
     vals = []
@@ -618,6 +641,8 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time stepwise, staged and other collectives")
     ap.add_argument("--counters", action="store_true",
                     help="only run the short launch sequence used for rocprofv3 --pmc passes")
+    ap.add_argument("--jsonl", metavar="PATH",
+                    help="also append one JSON record per leg (timing, bandwidth, roofline, per-rank bytes)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="(no GPU) write profiles/counters.json from two rocprofv3 --pmc passes over --counters")
     args = ap.parse_args()
@@ -665,11 +690,14 @@ def main():
         "roofline": f["roofline"],
         "cpu_baseline": f["cpu_baseline"],
         "parity": f["parity_first_timed_output"],
+        "bytes_per_rank_sent": f["bytes_per_rank"]["sent"][0],
     }
     if not args.skip_bfp8:
         line["bfp8"] = bfp8_leg(args)
     if args.extra:
         line["extra"] = extra_legs(args)
+    if args.jsonl:
+        write_jsonl(args.jsonl, line, f)
     print(json.dumps(line), flush=True)
 
 
