@@ -11,13 +11,15 @@
 //   kind 0 (BFP):    nnz = 0, then the BFP layout of the whole unit.
 // A unit is sparse iff zeros > threshold * len (zeros are +0 and -0).
 //
-// Encoding takes three launches over 2048-element tiles (256 lanes x 8):
+// Encoding takes two launches over 2048-element tiles (256 lanes x 8):
 //   count  - non-zeros per tile;
-//   plan   - one workgroup per message: exclusive scan of the tile counts,
-//            the threshold decision, the header, and the wire byte counters;
-//   write  - sparse: each tile compacts its non-zeros to the scanned offsets
-//            (ballot-free: a block-wide exclusive scan of per-lane counts
-//            keeps the indices ascending); BFP: the tile's blocks.
+//   write  - every workgroup sums the unit's tile counts (the total and the
+//            ones before its tile) and takes the threshold decision itself,
+//            the same integers giving the same decision everywhere; the
+//            first tile's workgroup writes the header and the wire byte
+//            counters.  Sparse: each tile compacts its non-zeros to its
+//            offset (ballot-free: a block-wide exclusive scan of per-lane
+//            counts keeps the indices ascending); BFP: the tile's blocks.
 // Decoding works per destination tile: a binary search finds the tile's
 // slice of the ascending index array, so no two workgroups touch the same
 // element and no atomics are needed.
@@ -75,45 +77,24 @@ __global__ __launch_bounds__(kThreads) void comp_count_kernel(CompJobs jobs, uin
   if (threadIdx.x == 0) jobs.tiles[j][t] = total;
 }
 
-__global__ __launch_bounds__(kThreads) void comp_plan_kernel(CompJobs jobs, float theta, uint64_t* traffic,
-                                                              int block, int mbits, int es) {
-  const int j = blockIdx.x;
-  const uint64_t len = jobs.len[j];
-  const uint32_t T = (uint32_t)((len + kTileElems - 1) / kTileElems);
-  uint32_t* nnzs = jobs.tiles[j];
-  uint32_t* offs = jobs.tiles[j] + T;
-  const uint32_t per = (T + kThreads - 1) / kThreads;
-  const uint32_t lo = threadIdx.x * per < T ? threadIdx.x * per : T;
-  const uint32_t hi = lo + per < T ? lo + per : T;
-  uint32_t local = 0;
-  for (uint32_t t = lo; t < hi; ++t) local += nnzs[t];
-  uint32_t total;
-  uint32_t run = block_exclusive_scan(local, &total);
-  for (uint32_t t = lo; t < hi; ++t) {
-    offs[t] = run;
-    run += nnzs[t];
+// Sum of the unit's tile counts before tile t, and of all of them, computed
+// by the whole workgroup (T is at most a few thousand).
+__device__ __forceinline__ void tile_prefix(const uint32_t* nnzs, uint32_t T, uint32_t t, uint32_t* before,
+                                            uint32_t* total) {
+  uint32_t a = 0, b = 0;
+  for (uint32_t i = threadIdx.x; i < T; i += kThreads) {
+    const uint32_t v = nnzs[i];
+    b += v;
+    if (i < t) a += v;
   }
-  if (threadIdx.x == 0) {
-    const uint64_t nnz = total;
-    const bool sparse = (double)(len - nnz) > (double)theta * (double)len;
-    uint32_t* hdr = (uint32_t*)jobs.msg[j];
-    hdr[0] = sparse ? (uint32_t)nnz : 0u;
-    hdr[1] = sparse ? 1u : 0u;
-    hdr[2] = (uint32_t)len;
-    hdr[3] = 0u;
-    const uint64_t bytes = sparse ? 16 + round16(nnz * (uint64_t)es) + 4 * nnz
-                                  : 16 + bfp_msg_bytes(len, block, mbits);
-    const int n = jobs.nranks;
-    for (int h = 0; h < jobs.hops[j]; ++h) {
-      atomicAdd((unsigned long long*)&traffic[(jobs.from[j] + h) % n], (unsigned long long)bytes);
-      atomicAdd((unsigned long long*)&traffic[kMaxRanks + (jobs.from[j] + h + 1) % n], (unsigned long long)bytes);
-    }
-  }
+  block_exclusive_scan(a, before);
+  block_exclusive_scan(b, total);
 }
 
 template <int DT, int LPB>
 __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uint32_t tiles_max, int lpb_rt,
-                                                               int mbits) {
+                                                               int mbits, float theta, uint64_t* traffic,
+                                                               int block) {
   constexpr int ES = DtypeSize<DT>::value;
   const int j = (int)(blockIdx.x / tiles_max);
   const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
@@ -122,16 +103,32 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
   const uint32_t T = (uint32_t)((len + kTileElems - 1) / kTileElems);
   const char* src = jobs.src[j];
   uint8_t* msg = jobs.msg[j];
-  const uint32_t kind = ((const uint32_t*)msg)[1];
+  uint32_t before, nnz32;
+  tile_prefix(jobs.tiles[j], T, t, &before, &nnz32);
+  const uint64_t nnz = nnz32;
+  const bool sparse = (double)(len - nnz) > (double)theta * (double)len;  // zeros > theta * len
+  if (t == 0 && threadIdx.x == 0) {
+    uint32_t* hdr = (uint32_t*)msg;
+    hdr[0] = sparse ? (uint32_t)nnz : 0u;
+    hdr[1] = sparse ? 1u : 0u;
+    hdr[2] = (uint32_t)len;
+    hdr[3] = 0u;
+    const uint64_t bytes = sparse ? 16 + round16(nnz * (uint64_t)ES) + 4 * nnz
+                                  : 16 + bfp_msg_bytes(len, block, mbits);
+    const int n = jobs.nranks;
+    for (int h = 0; h < jobs.hops[j]; ++h) {
+      atomicAdd((unsigned long long*)&traffic[(jobs.from[j] + h) % n], (unsigned long long)bytes);
+      atomicAdd((unsigned long long*)&traffic[kMaxRanks + (jobs.from[j] + h + 1) % n], (unsigned long long)bytes);
+    }
+  }
   const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
   const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
   const G8 x = load_group<DT>(src, elem, nv);
-  if (kind == 1u) {
-    const uint64_t nnz = ((const uint32_t*)msg)[0];
+  if (sparse) {
     uint8_t* vals = msg + 16;
     uint32_t* idx = (uint32_t*)(msg + 16 + round16(nnz * ES));
     uint32_t total;
-    uint64_t pos = jobs.tiles[j][T + t] + block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
+    uint64_t pos = before + block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
     for (int i = 0; i < nv; ++i) {
       if (x.v[i] == 0.0f) continue;
       if constexpr (ES == 4) ((uint32_t*)vals)[pos] = ((const uint32_t*)src)[elem + i];
@@ -263,12 +260,12 @@ hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, ui
   if (jobs.njobs == 0 || tm == 0) return hipSuccess;
   dim3 grid((unsigned)(jobs.njobs * tm)), blk(kThreads);
   hipLaunchKernelGGL((comp_count_kernel<DT>), grid, blk, 0, stream, jobs, tm);
-  hipLaunchKernelGGL(comp_plan_kernel, dim3((unsigned)jobs.njobs), blk, 0, stream, jobs, theta, traffic, block,
-                     mbits, (int)DtypeSize<DT>::value);
   if (block == 128)
-    hipLaunchKernelGGL((comp_write_kernel<DT, 16>), grid, blk, 0, stream, jobs, tm, 16, mbits);
+    hipLaunchKernelGGL((comp_write_kernel<DT, 16>), grid, blk, 0, stream, jobs, tm, 16, mbits, theta, traffic,
+                       block);
   else
-    hipLaunchKernelGGL((comp_write_kernel<DT, 0>), grid, blk, 0, stream, jobs, tm, block / 8, mbits);
+    hipLaunchKernelGGL((comp_write_kernel<DT, 0>), grid, blk, 0, stream, jobs, tm, block / 8, mbits, theta,
+                       traffic, block);
   return hipGetLastError();
 }
 
