@@ -367,7 +367,7 @@ int staged_sparse(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t s
   for (int s = 1; s <= n - 1; ++s) {
     for (size_t u = 0; u < pl.upc; ++u) {
       CompJobs enc{};
-      BfpJobs dec{};
+      CompAccJobs dec{};
       int j = 0;
       for (int r = 0; r < n; ++r) {
         const int src = modn(r - 1, n), c = modn(r - s - 1, n);
@@ -385,6 +385,7 @@ int staged_sparse(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t s
         dec.dst[j] = (char*)bufs[r] + ulo * pl.es;
         dec.msg[j] = slot(src, u);
         dec.len[j] = len;
+        dec.counts[j] = scratch(r, u);  // r encodes this partial next (or, at s = N-1, as the owner)
         ++j;
       }
       if (!j) continue;
@@ -392,7 +393,8 @@ int staged_sparse(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t s
       enc.nranks = n;
       hipEvent_t eE = ctx->evE[u % kMaxEvents], eD = ctx->evD[u % kMaxEvents];
       if (s > 1 && hipStreamWaitEvent(E, eD, 0) != hipSuccess) return RAR_EHIP;
-      if ((rc = hip_rc(launch_comp_encode(enc, pl.dt, pl.block, pl.mbits, pl.theta, traffic, E)))) return rc;
+      // from step 2 on, the sender's tile counts came with the decode that made its partial
+      if ((rc = hip_rc(launch_comp_encode(enc, pl.dt, pl.block, pl.mbits, pl.theta, traffic, s > 1, E)))) return rc;
       if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
       if ((rc = hip_rc(launch_comp_decode_acc(dec, pl.dt, pl.block, pl.mbits, D)))) return rc;
       if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;
@@ -426,7 +428,8 @@ int staged_sparse(const CompPlan& pl, void* const* bufs, char* ws, hipStream_t s
     enc.nranks = n;
     hipEvent_t eE = ctx->evE[u % kMaxEvents], eD = ctx->evD[u % kMaxEvents];
     if (hipStreamWaitEvent(E, eD, 0) != hipSuccess) return RAR_EHIP;
-    if ((rc = hip_rc(launch_comp_encode(enc, pl.dt, pl.block, pl.mbits, pl.theta, traffic, E)))) return rc;
+    // the owner's counts came with the last reduce-scatter decode
+    if ((rc = hip_rc(launch_comp_encode(enc, pl.dt, pl.block, pl.mbits, pl.theta, traffic, true, E)))) return rc;
     if (hipEventRecord(eE, E) != hipSuccess || hipStreamWaitEvent(D, eE, 0) != hipSuccess) return RAR_EHIP;
     if ((rc = hip_rc(launch_comp_decode_fanout(dec, fan, n, off, pl.dt, pl.block, pl.mbits, D)))) return rc;
     if (hipEventRecord(eD, D) != hipSuccess) return RAR_EHIP;

@@ -114,10 +114,22 @@ struct CompJobs {
 uint64_t comp_tiles_per_unit(uint64_t unit_elems);
 // count -> plan (threshold, header, byte counters) -> write; traffic points
 // at u64 sent[kMaxRanks] followed by recv[kMaxRanks] in device memory.
+// counted: the per-tile non-zero counts are already in jobs.tiles (written
+// by the decode that produced the data), so the count pass is skipped.
 hipError_t launch_comp_encode(const CompJobs& jobs, int dt, int block, int mbits, float theta, uint64_t* traffic,
-                              hipStream_t stream);
+                              bool counted, hipStream_t stream);
 // dst <- dst (+) decoded message (job dst / msg / len).
-hipError_t launch_comp_decode_acc(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
+// Receiver side: dst <- dst (+) decode(msg), per 2048-element tile; when
+// counts[j] is set, the tile's non-zero count after the add goes to
+// counts[j][tile] (the count the next encode of dst needs).
+struct CompAccJobs {
+  uint8_t* msg[kMaxRanks];
+  char* dst[kMaxRanks];
+  uint64_t len[kMaxRanks];
+  uint32_t* counts[kMaxRanks];
+  int njobs;
+};
+hipError_t launch_comp_decode_acc(const CompAccJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
 // Store each decoded message to elem_off[j] of every rank in `fan`.
 hipError_t launch_comp_decode_fanout(const BfpJobs& jobs, const RankPtrs& fan, int nfan, const uint64_t* elem_off,
                                      int dt, int block, int mbits, hipStream_t stream);

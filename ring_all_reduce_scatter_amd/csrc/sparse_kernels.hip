@@ -228,15 +228,77 @@ __device__ __forceinline__ void comp_decode_tile(const uint8_t* msg, uint64_t le
   }
 }
 
+// Decode + accumulate one tile and count the non-zeros the tile holds
+// afterwards (the receiver's partial is what it encodes next, so the count
+// its encoder would take is produced here).  BFP messages: the sums are in
+// registers.  Sparse messages: the tile's non-zeros before the scatter, plus
+// the change at every scattered element (indices are unique).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void comp_decode_acc_kernel(BfpJobs jobs, uint32_t tiles_max, int block,
+__device__ __forceinline__ void comp_decode_acc_count_tile(const uint8_t* msg, uint64_t len, uint32_t t, char* dst,
+                                                           uint32_t* count_out, int block, int mbits) {
+  constexpr int ES = DtypeSize<DT>::value;
+  __shared__ uint64_t range[2];
+  const uint32_t* hdr = (const uint32_t*)msg;
+  const uint64_t tlo = (uint64_t)t * kTileElems;
+  const uint64_t thi = tlo + kTileElems < len ? tlo + kTileElems : len;
+  const uint64_t elem = tlo + (uint64_t)threadIdx.x * 8;
+  const int nv = elem >= thi ? 0 : (thi - elem >= 8 ? 8 : (int)(thi - elem));
+  uint32_t mine = 0;
+  if (hdr[1] == 0u) {
+    if (nv > 0) {
+      const G8 d = dequant_group(msg + 16, bfp_exp_bytes(len, block), elem, nv, (uint64_t)block, mbits);
+      G8 out = load_group<DT>(dst, elem, nv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out.v[i] = round_to<DT>(out.v[i] + d.v[i]);
+      store_group<DT>(dst, elem, nv, out);
+      mine = (uint32_t)nonzeros<DT>(out, nv);
+    }
+  } else {
+    const uint64_t nnz = hdr[0];
+    const uint8_t* vals = msg + 16;
+    const uint32_t* idx = (const uint32_t*)(msg + 16 + round16(nnz * ES));
+    if (threadIdx.x == 0) {
+      range[0] = lower_bound_u32(idx, nnz, tlo);
+      range[1] = lower_bound_u32(idx, nnz, thi);
+    }
+    if (nv > 0) mine = (uint32_t)nonzeros<DT>(load_group<DT>(dst, elem, nv), nv);
+    __syncthreads();  // every lane has read its elements before any scatter writes one
+    const uint64_t j0 = range[0], j1 = range[1];
+    for (uint64_t q = j0 + threadIdx.x; q < j1; q += kThreads) {
+      const uint64_t i = idx[q];
+      float before, after;
+      if constexpr (ES == 4) {
+        float* p = (float*)dst + i;
+        before = *p;
+        after = before + __uint_as_float(((const uint32_t*)vals)[q]);
+        *p = after;
+      } else {
+        uint16_t* p = (uint16_t*)dst + i;
+        const uint16_t old = *p;
+        const uint16_t nw = (uint16_t)narrow16<DT>(widen16<DT>(old) + widen16<DT>(((const uint16_t*)vals)[q]));
+        *p = nw;
+        before = widen16<DT>(old);
+        after = widen16<DT>(nw);
+      }
+      mine += (after != 0.0f ? 1u : 0u);
+      mine -= (before != 0.0f ? 1u : 0u);
+    }
+  }
+  uint32_t total;
+  block_exclusive_scan(mine, &total);
+  if (threadIdx.x == 0) *count_out = total;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void comp_decode_acc_kernel(CompAccJobs jobs, uint32_t tiles_max, int block,
                                                                     int mbits) {
   const int j = (int)(blockIdx.x / tiles_max);
   const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
   const uint64_t len = jobs.len[j];
   if ((uint64_t)t * kTileElems >= len) return;
   char* dst = jobs.dst[j];
-  comp_decode_tile<DT, true>(jobs.msg[j], len, t, &dst, 1, 0, block, mbits);
+  if (jobs.counts[j]) comp_decode_acc_count_tile<DT>(jobs.msg[j], len, t, dst, jobs.counts[j] + t, block, mbits);
+  else comp_decode_tile<DT, true>(jobs.msg[j], len, t, &dst, 1, 0, block, mbits);
 }
 
 template <int DT>
@@ -252,14 +314,14 @@ __global__ __launch_bounds__(kThreads) void comp_decode_fanout_kernel(BfpJobs jo
 uint32_t tiles_of(uint64_t len) { return (uint32_t)((len + kTileElems - 1) / kTileElems); }
 
 template <int DT>
-hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, uint64_t* traffic,
+hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, uint64_t* traffic, bool counted,
                      hipStream_t stream) {
   uint64_t ml = 0;
   for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
   const uint32_t tm = tiles_of(ml);
   if (jobs.njobs == 0 || tm == 0) return hipSuccess;
   dim3 grid((unsigned)(jobs.njobs * tm)), blk(kThreads);
-  hipLaunchKernelGGL((comp_count_kernel<DT>), grid, blk, 0, stream, jobs, tm);
+  if (!counted) hipLaunchKernelGGL((comp_count_kernel<DT>), grid, blk, 0, stream, jobs, tm);
   if (block == 128)
     hipLaunchKernelGGL((comp_write_kernel<DT, 16>), grid, blk, 0, stream, jobs, tm, 16, mbits, theta, traffic,
                        block);
@@ -274,15 +336,15 @@ hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, ui
 uint64_t comp_tiles_per_unit(uint64_t unit_elems) { return tiles_of(unit_elems); }
 
 hipError_t launch_comp_encode(const CompJobs& jobs, int dt, int block, int mbits, float theta, uint64_t* traffic,
-                              hipStream_t stream) {
+                              bool counted, hipStream_t stream) {
   switch (dt) {
-    case DT_F32: return encode_dt<DT_F32>(jobs, block, mbits, theta, traffic, stream);
-    case DT_F16: return encode_dt<DT_F16>(jobs, block, mbits, theta, traffic, stream);
-    default: return encode_dt<DT_BF16>(jobs, block, mbits, theta, traffic, stream);
+    case DT_F32: return encode_dt<DT_F32>(jobs, block, mbits, theta, traffic, counted, stream);
+    case DT_F16: return encode_dt<DT_F16>(jobs, block, mbits, theta, traffic, counted, stream);
+    default: return encode_dt<DT_BF16>(jobs, block, mbits, theta, traffic, counted, stream);
   }
 }
 
-hipError_t launch_comp_decode_acc(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
+hipError_t launch_comp_decode_acc(const CompAccJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
   uint64_t ml = 0;
   for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
   const uint32_t tm = tiles_of(ml);
