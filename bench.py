@@ -470,6 +470,10 @@ def extra_legs(args):
     out["sparse_bfp4_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S5, w5["n"], ms), 1),
                                            "wire_bytes_rank0": sent[0],
                                            "frac_of_roofline": round(2 * w5["n"] * S5 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms, k, _ = time_graph_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, steps)
+    out["sparse_bfp4_allreduce_staged_graph_replay"] = {
+        "ms": round(ms, 4), "busbw_GBs": round(busbw(S5, w5["n"], ms), 1),
+        "frac_of_roofline": round(2 * w5["n"] * S5 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del sets, pristine, ws
     torch.cuda.empty_cache()
     wk = inputs.WORKLOADS["buckets"]
