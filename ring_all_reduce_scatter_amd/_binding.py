@@ -159,6 +159,14 @@ def _stream(stream, t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _dptr(t) -> int:
+    """Device address of a tensor; host tensors are refused here, since the
+    kernels would read host addresses as device memory."""
+    if t.device.type != "cuda":
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    return t.data_ptr()
+
+
 def _rank_ptrs(bufs: Sequence):
     if len(bufs) < 1:
         raise ValueError("need at least one rank buffer")
@@ -168,7 +176,7 @@ def _rank_ptrs(bufs: Sequence):
             raise ValueError("rank buffers must share dtype, size and device")
         if not b.is_contiguous():
             raise ValueError("rank buffers must be contiguous")
-    return (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+    return (ctypes.c_void_p * len(bufs))(*[_dptr(b) for b in bufs])
 
 
 def _call_bufs(name: str, bufs, *extra, stream=None):
@@ -256,19 +264,19 @@ def bfp_bytes(count: int, block: int = 128, mbits: int = 8) -> int:
 
 
 def bfp_compress(src, block: int, mbits: int, dst, stream=None):
-    rc = lib().rar_bfp_compress(src.data_ptr(), dtype_code(src), src.numel(), block, mbits, dst.data_ptr(),
+    rc = lib().rar_bfp_compress(_dptr(src), dtype_code(src), src.numel(), block, mbits, _dptr(dst),
                                 _stream(stream, src))
     _check(rc, "rar_bfp_compress")
 
 
 def bfp_decompress_accumulate(msg, count: int, block: int, mbits: int, acc, stream=None):
-    rc = lib().rar_bfp_decompress_accumulate(msg.data_ptr(), count, block, mbits, acc.data_ptr(),
+    rc = lib().rar_bfp_decompress_accumulate(_dptr(msg), count, block, mbits, _dptr(acc),
                                              dtype_code(acc), _stream(stream, acc))
     _check(rc, "rar_bfp_decompress_accumulate")
 
 
 def bfp_decompress(msg, count: int, block: int, mbits: int, dst, stream=None):
-    rc = lib().rar_bfp_decompress(msg.data_ptr(), count, block, mbits, dst.data_ptr(), dtype_code(dst),
+    rc = lib().rar_bfp_decompress(_dptr(msg), count, block, mbits, _dptr(dst), dtype_code(dst),
                                   _stream(stream, dst))
     _check(rc, "rar_bfp_decompress")
 
@@ -299,7 +307,7 @@ def compressed_workspace_bytes(nranks: int, count: int, dtype: int, cfg: Compres
 def ring_allreduce_compressed(bufs, cfg: CompressCfg, workspace, stream=None):
     rc = lib().rar_ring_allreduce_compressed(
         _rank_ptrs(bufs), len(bufs), bufs[0].numel(), dtype_code(bufs[0]), ctypes.byref(cfg),
-        workspace.data_ptr() if workspace is not None else None,
+        _dptr(workspace) if workspace is not None else None,
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream, bufs[0]))
     _check(rc, "rar_ring_allreduce_compressed")
@@ -314,9 +322,9 @@ def ring_allreduce_compressed_state(bufs, state, feedback: int, cfg: CompressCfg
         if s_.numel() != bufs[0].numel() or s_.element_size() != 4 or not s_.is_contiguous():
             raise ValueError("state tensors must be contiguous float32 of the rank buffers' length")
     rc = lib().rar_ring_allreduce_compressed_state(
-        _rank_ptrs(bufs), (ctypes.c_void_p * len(state))(*[t.data_ptr() for t in state]), len(bufs),
+        _rank_ptrs(bufs), (ctypes.c_void_p * len(state))(*[_dptr(t) for t in state]), len(bufs),
         bufs[0].numel(), dtype_code(bufs[0]), feedback, ctypes.byref(cfg),
-        workspace.data_ptr() if workspace is not None else None,
+        _dptr(workspace) if workspace is not None else None,
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream, bufs[0]))
     _check(rc, "rar_ring_allreduce_compressed_state")
@@ -325,7 +333,7 @@ def ring_allreduce_compressed_state(bufs, state, feedback: int, cfg: CompressCfg
 def compressed_traffic(workspace, nranks: int, stream=None):
     sent = (ctypes.c_uint64 * nranks)()
     recv = (ctypes.c_uint64 * nranks)()
-    _check(lib().rar_compressed_traffic(workspace.data_ptr(), nranks, sent, recv, _stream(stream, workspace)),
+    _check(lib().rar_compressed_traffic(_dptr(workspace), nranks, sent, recv, _stream(stream, workspace)),
            "rar_compressed_traffic")
     return list(sent), list(recv)
 
@@ -337,14 +345,14 @@ def _nbytes(t):
 
 
 def _ws(workspace):
-    return (workspace.data_ptr(), _nbytes(workspace)) if workspace is not None else (None, 0)
+    return (_dptr(workspace), _nbytes(workspace)) if workspace is not None else (None, 0)
 
 
 def rank_hashes(bufs, workspace, nbytes=None, stream=None):
     """64-bit hash of each rank buffer's first nbytes bytes (default: all)."""
     nb = _nbytes(bufs[0]) if nbytes is None else nbytes
     out = (ctypes.c_uint64 * len(bufs))()
-    ptrs = (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+    ptrs = (ctypes.c_void_p * len(bufs))(*[_dptr(b) for b in bufs])
     _check(lib().rar_rank_hashes(ptrs, len(bufs), nb, *_ws(workspace), out, _stream(stream, bufs[0])),
            "rar_rank_hashes")
     return list(out)
@@ -419,10 +427,10 @@ class BucketedAllreduce:
         if any(x.dtype != t0.dtype for x in flat) or not all(x.is_contiguous() for x in flat):
             raise ValueError("tensors must share one dtype and be contiguous")
         self._keep = (tensors, workspace)
-        self._ptrs = (ctypes.c_void_p * len(flat))(*[x.data_ptr() for x in flat])
+        self._ptrs = (ctypes.c_void_p * len(flat))(*[_dptr(x) for x in flat])
         self._counts = _sizes(counts)
         self._args = (nt, n, dtype_code(t0), cap_bytes, algo,
-                      workspace.data_ptr() if workspace is not None else None,
+                      _dptr(workspace) if workspace is not None else None,
                       workspace.numel() * workspace.element_size() if workspace is not None else 0)
         self._t0 = t0
 

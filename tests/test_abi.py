@@ -99,7 +99,7 @@ class _FakeTensor:
     def __init__(self, ptr, numel, dtype):
         import torch
         self._ptr, self._n, self.dtype = ptr, numel, dtype
-        self.device = torch.device("cpu")
+        self.device = torch.device("cuda", 0)  # claims a GPU address; never launched
 
     def data_ptr(self):
         return self._ptr
@@ -258,3 +258,13 @@ def test_ft_scheduler_matches_oracle_on_empty_buffers(orc, n):
         assert list(rep.dead_attempt)[:n] == ref["dead_attempt"], plan
         assert list(rep.dead_step)[:n] == ref["dead_step"], plan
         assert rar.last_traffic(n) == ([0] * n, [0] * n)
+
+
+def test_binding_refuses_host_tensors():
+    """A host tensor's address is not device memory: the binding stops it."""
+    import torch
+    x = [torch.zeros(1024), torch.zeros(1024)]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rar.ring_allreduce(x, stream=0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rar.bfp_compress(x[0], 128, 8, torch.zeros(2048, dtype=torch.uint8), stream=0)
