@@ -733,7 +733,7 @@ hipError_t launch_bfp_forward(const FwdJobs& jobs, int dt, int block, int mbits,
     default: RAR_FWD(DT_BF16) break;
   }
 #undef RAR_FWD
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
@@ -746,7 +746,7 @@ hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, 
     case DT_F16: encode_dispatch<DT_F16>(jobs, block, mbits, grid, bpj, stream); break;
     default: encode_dispatch<DT_BF16>(jobs, block, mbits, grid, bpj, stream); break;
   }
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_bfp_decode(const BfpJobs& jobs, int dt, int block, int mbits, bool accumulate,
@@ -766,7 +766,7 @@ hipError_t launch_bfp_decode(const BfpJobs& jobs, int dt, int block, int mbits, 
     default: RAR_DEC(DT_BF16) break;
   }
 #undef RAR_DEC
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan, int nfan,
@@ -789,7 +789,7 @@ hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan,
       hipLaunchKernelGGL((bfp_decode_fanout_kernel<DT_BF16>), grid, blk, 0, stream, jobs, fan, nfan, block, mbits, bpj);
       break;
   }
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, int dt,
@@ -800,7 +800,7 @@ hipError_t launch_bfp_ring_fold(const RankPtrs& bufs, int n, uint64_t count, uin
     case DT_F16: fold_dispatch_nr<DT_F16>(bufs, n, count, L, block, mbits, stream); break;
     default: fold_dispatch_nr<DT_BF16>(bufs, n, count, L, block, mbits, stream); break;
   }
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_bfp_ring_fold_state(const RankPtrs& bufs, const RankPtrs& state, int n, uint64_t count, uint64_t L,
@@ -815,7 +815,7 @@ hipError_t launch_bfp_ring_fold_state(const RankPtrs& bufs, const RankPtrs& stat
     default: RAR_FS(DT_BF16) break;
   }
 #undef RAR_FS
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_fill_u64(uint64_t* dst, const uint64_t* host_vals, int nvals, hipStream_t stream) {

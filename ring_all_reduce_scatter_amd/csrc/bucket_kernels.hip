@@ -56,7 +56,7 @@ hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream) {
   if (tiles == 0) tiles = 1;
   dim3 grid((unsigned)((uint64_t)jobs.njobs * tiles)), block(kThreads);
   hipLaunchKernelGGL(seg_copy_kernel, grid, block, 0, stream, jobs, tiles);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 }  // namespace rar
@@ -202,7 +202,7 @@ hipError_t bucket_fold_dispatch(const uint64_t* tab, int n, uint64_t ntensors, u
   constexpr int V = DT == DT_BF16 ? 1 : 2;
   hipLaunchKernelGGL((bucket_fold_kernel<DT, NR, V>), dim3((unsigned)grid), dim3(kThreads),
                      residency_lds(fold_wgs_per_cu(DT, n)), stream, tab, n, ntensors);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 template <int DT>

@@ -69,7 +69,7 @@ hipError_t launch_rank_hash(const RankPtrs& bufs, int n, uint64_t nbytes, uint64
   if (per_rank < 1) per_rank = 1;
   hipLaunchKernelGGL(rank_hash_kernel, dim3((unsigned)per_rank, (unsigned)n), dim3(kThreads), 0, stream, bufs, nbytes,
                      acc);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 }  // namespace rar

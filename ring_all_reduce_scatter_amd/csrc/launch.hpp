@@ -10,6 +10,13 @@
 
 namespace rar {
 
+// -------------------------------------------------------------- launch status
+// Result of the launch just enqueued on `stream`.  With RAR_DEBUG_SYNC set to
+// a value other than 0 in the environment, the stream is also synchronised
+// so an execution error surfaces at the call that caused it (a debugging
+// aid: it serialises every call and must not be used under graph capture).
+hipError_t launch_status(hipStream_t stream);
+
 // -------------------------------------------------------------- residency control
 // Streaming kernels keep most HBM efficiency with about 64 KiB of loads in
 // flight per CU; at full occupancy the memory controllers see too many

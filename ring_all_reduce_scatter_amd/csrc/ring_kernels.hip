@@ -17,6 +17,9 @@
 //    N*S written.
 #include <atomic>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "launch.hpp"
 
 namespace rar {
@@ -312,7 +315,7 @@ hipError_t fold_dispatch_store(const RankPtrs& bufs, int n, uint64_t count, uint
     hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, true>), grid, block, lds, stream, bufs, n, count, L);
   else
     hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, false>), grid, block, lds, stream, bufs, n, count, L);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 template <int DT>
@@ -333,7 +336,7 @@ hipError_t step_dispatch(const RankPtrs& bufs, int n, uint64_t count, uint64_t L
   const uint64_t tiles = (L + tile - 1) / tile;
   dim3 grid((unsigned)((uint64_t)n * tiles)), block(kThreads);
   hipLaunchKernelGGL((rs_step_kernel<DT, kStepVecs>), grid, block, 0, stream, bufs, n, count, L, s);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 template <int DT, int NR>
@@ -343,7 +346,7 @@ hipError_t tree_dispatch_v(const RankPtrs& bufs, uint64_t count, hipStream_t str
   const uint64_t tiles = (count + tile - 1) / tile;
   hipLaunchKernelGGL((tree_fold_kernel<DT, NR, V>), dim3((unsigned)tiles), dim3(kThreads),
                      residency_lds(fold_wgs_per_cu(DT, NR)), stream, bufs, count);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 template <int DT>
@@ -368,7 +371,7 @@ hipError_t pair_dispatch(const RankPtrs& bufs, const PairJobs& pairs, uint64_t c
   const uint64_t tiles = (count + tile - 1) / tile;
   hipLaunchKernelGGL((pair_add_kernel<DT, V>), dim3((unsigned)(tiles * (uint64_t)pairs.npairs)), dim3(kThreads), 0,
                      stream, bufs, pairs, count, (uint32_t)tiles);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 }  // namespace
@@ -389,6 +392,16 @@ int fold_wgs_per_cu(int dt, int n) {
     default: return 2;
   }
 }
+hipError_t launch_status(hipStream_t stream) {
+  static const bool sync = [] {
+    const char* v = std::getenv("RAR_DEBUG_SYNC");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !sync) return e;
+  return hipStreamSynchronize(stream);
+}
+
 size_t residency_lds(int wgs_per_cu) {
   if (wgs_per_cu <= 0) return 0;
   static std::atomic<uint64_t> cache[kMaxRanks];  // per device: LDS per CU << 32 | LDS per workgroup
@@ -444,7 +457,7 @@ hipError_t launch_copy_jobs(const CopyJobs& jobs, hipStream_t stream) {
   // CU (+8% over uncapped), a 1-to-1 copy at 6 (+3%).
   const size_t lds = residency_lds(fanout >= 4 ? 3 : 6);
   hipLaunchKernelGGL(copy_jobs_kernel, grid, block, lds, stream, jobs, tiles);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 bool tree_fold_supported(int n) { return (n >= 2 && n <= 8) || n == 16; }

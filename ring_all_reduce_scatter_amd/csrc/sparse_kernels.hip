@@ -328,7 +328,7 @@ hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, ui
   else
     hipLaunchKernelGGL((comp_write_kernel<DT, 0>), grid, blk, 0, stream, jobs, tm, block / 8, mbits, theta,
                        traffic, block);
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 }  // namespace
@@ -355,7 +355,7 @@ hipError_t launch_comp_decode_acc(const CompAccJobs& jobs, int dt, int block, in
     case DT_F16: hipLaunchKernelGGL((comp_decode_acc_kernel<DT_F16>), grid, blk, 0, stream, jobs, tm, block, mbits); break;
     default: hipLaunchKernelGGL((comp_decode_acc_kernel<DT_BF16>), grid, blk, 0, stream, jobs, tm, block, mbits); break;
   }
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 hipError_t launch_comp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan, int nfan,
@@ -378,7 +378,7 @@ hipError_t launch_comp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan
       hipLaunchKernelGGL((comp_decode_fanout_kernel<DT_BF16>), grid, blk, 0, stream, jobs, fan, nfan, tm, block, mbits);
       break;
   }
-  return hipGetLastError();
+  return launch_status(stream);
 }
 
 }  // namespace rar

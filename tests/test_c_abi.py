@@ -27,3 +27,14 @@ def test_c_program_collectives_on_device():
     p = _run()
     assert p.returncode == 0, p.stderr
     assert "c_abi_check OK" in p.stdout
+
+
+@pytest.mark.gpu
+def test_c_program_with_debug_sync():
+    """RAR_DEBUG_SYNC=1 synchronises after every launch; results are unchanged."""
+    env = dict(os.environ, RAR_DEBUG_SYNC="1")
+    if not os.path.exists(EXE):
+        pytest.fail(f"{EXE} is missing: run __graft_entry__.build() first")
+    p = subprocess.run([EXE], capture_output=True, text=True, timeout=120, env=env)
+    assert p.returncode == 0, p.stderr
+    assert "c_abi_check OK" in p.stdout
