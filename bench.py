@@ -479,8 +479,12 @@ def extra_legs(args):
     wk = inputs.WORKLOADS["buckets"]
     sizes = inputs.bucket_sizes(wk["ntensors"])
     th = inputs.bucket_tensors(wk["n"], sizes)
-    dev = [[torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to("cuda:0") for t in th[r]]
-           for r in range(wk["n"])]
+    # each rank's gradients in one region, regions a power of two apart (as a
+    # gradient arena sits at the same address on every real GPU)
+    arena, dev = rar.rank_tensors(wk["n"], sizes, torch.bfloat16, "cuda:0")
+    for r in range(wk["n"]):
+        for t, x in zip(th[r], dev[r]):
+            x.copy_(torch.from_numpy(t.view(np.int16)).view(torch.bfloat16))
     del th
     ws = torch.empty(rar.bucketed_workspace_bytes(sizes, wk["n"], rar.BF16, wk["cap_bytes"]), dtype=torch.uint8,
                      device="cuda:0")
@@ -493,7 +497,7 @@ def extra_legs(args):
     out["buckets_bf16_allreduce"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S3, wk["n"], ms), 1),
                                      "buckets": nb, "elements_per_rank": sum(sizes),
                                      "frac_of_roofline_fold_only_bytes": round(2 * wk["n"] * S3 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del dev, ws, step
+    del dev, arena, ws, step
     torch.cuda.empty_cache()
     # [P2] exercise: ring vs tree wall-clock on 4 ranks at 1 KB, 1 MB and 16 MB
     rvt = {}

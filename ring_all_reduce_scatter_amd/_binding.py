@@ -439,6 +439,32 @@ class BucketedAllreduce:
         _check(rc, "rar_bucketed_allreduce_ex")
 
 
+def rank_tensors(nranks: int, counts, dtype, device="cuda", align_elems: int = 256):
+    """N simulated ranks' copies of a list of tensors, placed for the folds.
+
+    Returns (arena, views) with views[r][t] rank r's tensor t.  Every rank's
+    tensors lie in one region of the arena, tensor t at the same offset in
+    each region (a multiple of align_elems), and the regions are a power of
+    two bytes apart.  The fused folds read all N copies of an element at
+    once; on MI355X copies a power of two apart spread evenly over the HBM
+    channels, while copies at arbitrary distances collide (measured on a
+    16-rank bf16 fold: 5.5 TB/s against 4.2-4.6 TB/s).  On real GPUs each
+    rank's tensor sits in its own HBM, so this placement only removes an
+    artefact of simulating the ranks on one device."""
+    import torch
+    offs, off = [], 0
+    for c in counts:
+        offs.append(off)
+        off += -(-int(c) // align_elems) * align_elems
+    es = torch.empty((), dtype=dtype).element_size()
+    region = max(off * es, 1)
+    stride_bytes = 1 << (region - 1).bit_length()
+    stride = stride_bytes // es
+    arena = torch.empty(nranks * stride, dtype=dtype, device=device)
+    views = [[arena[r * stride + o: r * stride + o + int(c)] for o, c in zip(offs, counts)] for r in range(nranks)]
+    return arena, views
+
+
 def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None, algo: int = ALGO_FUSED):
     """tensors[r][t]: rank r's gradient tensor t (device tensors, in place)."""
     BucketedAllreduce(tensors, cap_bytes, workspace, algo)(stream)

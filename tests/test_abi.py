@@ -268,3 +268,24 @@ def test_binding_refuses_host_tensors():
         rar.ring_allreduce(x, stream=0)
     with pytest.raises(ValueError, match="GPU tensor"):
         rar.bfp_compress(x[0], 128, 8, torch.zeros(2048, dtype=torch.uint8), stream=0)
+
+
+def test_rank_tensors_placement():
+    """rank_tensors: tensor t at the same aligned offset in every rank's
+    region, regions a power of two bytes apart and disjoint."""
+    import torch
+    counts = [5, 300, 7, 1, 4096]
+    arena, views = rar.rank_tensors(3, counts, torch.bfloat16, "cpu", align_elems=64)
+    base = arena.data_ptr()
+    stride = (views[1][0].data_ptr() - base)
+    assert stride > 0 and stride & (stride - 1) == 0
+    for r in range(3):
+        for t, c in enumerate(counts):
+            x = views[r][t]
+            assert x.numel() == c and x.is_contiguous()
+            off = x.data_ptr() - base - r * stride
+            assert off == views[0][t].data_ptr() - base and off % (64 * 2) == 0
+            assert off + c * 2 <= stride
+    ends = [(v.data_ptr(), v.data_ptr() + v.numel() * 2) for row in views for v in row]
+    ends.sort()
+    assert all(a[1] <= b[0] for a, b in zip(ends, ends[1:]))
