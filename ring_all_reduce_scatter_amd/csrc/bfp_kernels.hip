@@ -363,7 +363,9 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_f32q_kernel(RankPtrs b
       for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
       st16<true>(base + e * 4, w);
     } else {
-      for (int i = 0; i < nv; ++i) ((float*)base)[e + i] = v[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nv) ((float*)base)[e + i] = v[i];
     }
   };
   auto load = [&](int rank, Q8& q) {

@@ -129,8 +129,9 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
     uint32_t* idx = (uint32_t*)(msg + 16 + round16(nnz * ES));
     uint32_t total;
     uint64_t pos = before + block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
-    for (int i = 0; i < nv; ++i) {
-      if (x.v[i] == 0.0f) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i >= nv || x.v[i] == 0.0f) continue;
       if constexpr (ES == 4) ((uint32_t*)vals)[pos] = ((const uint32_t*)src)[elem + i];
       else ((uint16_t*)vals)[pos] = ((const uint16_t*)src)[elem + i];
       idx[pos] = (uint32_t)(elem + i);

@@ -45,8 +45,8 @@ def _run(dt, n, count, block, mbits, fb, calls=3, kind="grad"):
 
 @pytest.mark.parametrize("fb", ["error", "delta"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("n", [1, 2, 3, 8])
-@pytest.mark.parametrize("block,mbits", [(128, 8), (128, 4), (32, 3), (512, 5)])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("block,mbits", [(128, 8), (128, 4), (32, 3), (256, 6), (512, 5)])
 def test_stateful_ring_matches_oracle(fb, dt, n, block, mbits):
     _run(dt, n, 3 * 4096 + 517, block, mbits, fb)
 
