@@ -388,8 +388,10 @@ size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t 
 
 /* Workspace for rar_bucketed_allreduce(_ex) (0 on bad args).
  * FUSED: the launch table, 8 * (2 + 5*nbuckets + (2 + nranks)*ntensors)
- * bytes rounded up to 256.  STEPWISE: nranks flat buffers of the largest
- * padded bucket. */
+ * bytes rounded up to 256, then 16 bytes per workgroup of the fold launch
+ * (nranks * ceil(L_b / tile) per bucket b, L_b its chunk length; tile =
+ * 2048 elements for f32 and bf16, 4096 for f16), rounded up to 256.
+ * STEPWISE: nranks flat buffers of the largest padded bucket. */
 size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
                                     size_t cap_bytes);
 size_t rar_bucketed_workspace_bytes_ex(const size_t* counts, size_t ntensors, int nranks, int dtype,

@@ -1122,10 +1122,11 @@ size_t rar_bucketed_workspace_bytes_ex(const size_t* counts, size_t ntensors, in
                                        size_t cap_bytes, int algo) {
   if (nranks < 1 || nranks > RAR_MAX_RANKS || !dt_ok(dtype) || (ntensors && !counts)) return 0;
   if (algo == RAR_ALGO_FUSED) {
+    // launch table, then 16 bytes of descriptor per workgroup
     std::vector<uint64_t> tab;
     uint64_t grid = 0;
     bucket_table(counts, ntensors, nranks, dtype, cap_bytes, nullptr, tab, &grid, nullptr);
-    return round_up(tab.size() * sizeof(uint64_t), kAlign);
+    return round_up(tab.size() * sizeof(uint64_t), kAlign) + round_up((size_t)grid * 16, kAlign);
   }
   if (algo != RAR_ALGO_STEPWISE) return 0;
   std::vector<int> plan;
@@ -1225,7 +1226,8 @@ int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t
   if (nranks == 1 || grid == 0) return RAR_OK;
   int rc = hip_rc(launch_fill_u64((uint64_t*)workspace, tab.data(), (int)tab.size(), st));
   if (rc) return rc;
-  return hip_rc(launch_bucket_fold((const uint64_t*)workspace, nranks, ntensors, grid, dtype, st));
+  char* desc = (char*)workspace + round_up(tab.size() * sizeof(uint64_t), kAlign);
+  return hip_rc(launch_bucket_fold((const uint64_t*)workspace, desc, nranks, ntensors, grid, dtype, st));
 }
 
 int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors, int nranks, int dtype,

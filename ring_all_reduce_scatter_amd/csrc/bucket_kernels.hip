@@ -93,124 +93,203 @@ __device__ __forceinline__ uint64_t upper_index(uint64_t lo, uint64_t hi, uint64
   return lo;
 }
 
-template <int DT, int NR, int V>
-__global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* __restrict__ tab, int nranks,
-                                                                uint64_t ntensors) {
-  constexpr int E = Vec<DT>::E;
-  constexpr int ES = DtypeSize<DT>::value;
-  const int N = NR > 0 ? NR : nranks;
+// Where workgroup g of the launch works: bucket b, chunk c, and the flat
+// element range [tile0, tile1) of its tile (empty when the chunk or the
+// tile lies past the bucket's end).
+struct TileLoc {
+  uint64_t tile0, tile1, t0, nt;
+  int c;
+  bool empty;
+};
+
+__device__ __forceinline__ TileLoc locate_tile(const uint64_t* tab, int N, uint64_t g, uint64_t kTile) {
+  TileLoc loc{};
   const uint64_t nb = ld_u64(tab);
   const uint64_t* start = tab + 1;
   const uint64_t* hdr = tab + 2 + nb;
-  const uint64_t* ten = hdr + 4 * nb;
-  const uint64_t* ptr = ten + 2 * ntensors;
-  // which bucket this workgroup belongs to (uniform)
-  const uint64_t b = upper_index(0, nb, blockIdx.x, [&](uint64_t i) { return ld_u64(start + i); });
-  const uint64_t local = blockIdx.x - ld_u64(start + b);
+  const uint64_t b = upper_index(0, nb, g, [&](uint64_t i) { return ld_u64(start + i); });
+  const uint64_t local = g - ld_u64(start + b);
   const uint64_t total = ld_u64(hdr + 4 * b), L = ld_u64(hdr + 4 * b + 1);
-  const uint64_t t0 = ld_u64(hdr + 4 * b + 2), nt = ld_u64(hdr + 4 * b + 3);
-  const int c = (int)(local % (uint64_t)N);
+  loc.t0 = ld_u64(hdr + 4 * b + 2);
+  loc.nt = ld_u64(hdr + 4 * b + 3);
+  loc.c = (int)(local % (uint64_t)N);
   const uint64_t tile = local / (uint64_t)N;
-  const uint64_t lo = (uint64_t)c * L;
-  if (lo >= total) return;
+  const uint64_t lo = (uint64_t)loc.c * L;
+  loc.empty = true;
+  if (lo >= total) return loc;
   const uint64_t hi = lo + L < total ? lo + L : total;
-  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
-  const uint64_t tile0 = lo + tile * kTile;
-  if (tile0 >= hi) return;
-  const uint64_t tile1 = tile0 + kTile < hi ? tile0 + kTile : hi;
-  const int first = c + 1 < N ? c + 1 : 0;
-  auto tensor_of = [&](uint64_t f) {  // index into the bucket's tensors
-    return upper_index(0, nt, f, [&](uint64_t i) { return ld_u64(ten + 2 * (t0 + i)); });
-  };
-  const uint64_t ja = tensor_of(tile0), jb = tensor_of(tile1 - 1);
-  auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
+  loc.tile0 = lo + tile * kTile;
+  if (loc.tile0 >= hi) return loc;
+  loc.tile1 = loc.tile0 + kTile < hi ? loc.tile0 + kTile : hi;
+  loc.empty = false;
+  return loc;
+}
 
-  if (ja == jb) {
-    // The whole tile lies in one tensor: uniform pointers, vector loads.
-    const uint64_t t = t0 + ja;
+// Per-workgroup descriptor of the fold, 16 bytes: word 0 the tensor index
+// of a whole tile inside one tensor (or kDescEmpty / kDescSlow), word 1 the
+// chunk, words 2-3 the tile's first element inside that tensor.  Computed
+// once per call by bucket_desc_kernel, so a fold workgroup starts its loads
+// after two dependent scalar loads (descriptor, then the N tensor pointers)
+// instead of the searches through the bucket and tensor tables.
+constexpr uint32_t kDescEmpty = 0xffffffffu;
+constexpr uint32_t kDescSlow = 0xfffffffeu;
+
+__global__ __launch_bounds__(kThreads) void bucket_desc_kernel(const uint64_t* __restrict__ tab, int N,
+                                                                uint64_t ntensors, uint64_t grid, uint64_t kTile,
+                                                                u32x4* __restrict__ desc) {
+  const uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= grid) return;
+  const uint64_t nb = ld_u64(tab);
+  const uint64_t* ten = tab + 2 + 5 * nb;
+  const TileLoc loc = locate_tile(tab, N, g, kTile);
+  u32x4 d = {kDescEmpty, 0u, 0u, 0u};
+  if (!loc.empty) {
+    auto tensor_of = [&](uint64_t f) {
+      return upper_index(0, loc.nt, f, [&](uint64_t i) { return ld_u64(ten + 2 * (loc.t0 + i)); });
+    };
+    const uint64_t ja = tensor_of(loc.tile0), jb = tensor_of(loc.tile1 - 1);
+    const uint64_t t = loc.t0 + ja;
     const uint64_t off = ld_u64(ten + 2 * t), cnt = ld_u64(ten + 2 * t + 1);
-    if (tile1 <= off + cnt && tile0 + kTile == tile1) {
-      Vec<DT> acc[V];
-      if constexpr (NR > 0) {
-        u32x4 x[NR][V];
-        int r = first;
+    d[0] = kDescSlow;
+    d[1] = (uint32_t)loc.c;
+    if (ja == jb && loc.tile1 <= off + cnt && loc.tile0 + kTile == loc.tile1 && t < (uint64_t)kDescSlow) {
+      const uint64_t e = loc.tile0 - off;
+      d[0] = (uint32_t)t;
+      d[2] = (uint32_t)e;
+      d[3] = (uint32_t)(e >> 32);
+    }
+  }
+  desc[g] = d;
+}
+
+template <int DT, int NR, int V>
+__global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* __restrict__ tab,
+                                                                const u32x4* __restrict__ desc, int nranks,
+                                                                uint64_t ntensors) {
+  constexpr int E = Vec<DT>::E;
+  constexpr int ES = DtypeSize<DT>::value;
+  constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
+  const int N = NR > 0 ? NR : nranks;
+  const u32x4 dsc = desc[blockIdx.x];
+  if (dsc[0] == kDescEmpty) return;
+  const uint64_t nb = ld_u64(tab);
+  const uint64_t* ten = tab + 2 + 5 * nb;
+  const uint64_t* ptr = ten + 2 * ntensors;
+  const int c = (int)dsc[1];
+  const int first = c + 1 < N ? c + 1 : 0;
+
+  if (dsc[0] != kDescSlow) {
+    // The whole tile lies in tensor t: uniform pointers, vector loads.
+    const uint64_t t = dsc[0];
+    const uint64_t e0 = (uint64_t)dsc[2] | ((uint64_t)dsc[3] << 32);
+    auto elem = [&](int v) -> uint64_t { return e0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
+    Vec<DT> acc[V];
+    if constexpr (NR > 0) {
+      u32x4 x[NR][V];
+      int r = first;
 #pragma unroll
-        for (int k = 0; k < NR; ++k) {
-          const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
-#pragma unroll
-          for (int v = 0; v < V; ++v) x[k][v] = ld16<true>(p + (elem(v) - off) * ES);
-          r = r + 1 == NR ? 0 : r + 1;
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          acc[v] = unpack16<DT>(x[0][v]);
-#pragma unroll
-          for (int k = 1; k < NR; ++k) {
-            const Vec<DT> y = unpack16<DT>(x[k][v]);
-#pragma unroll
-            for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
-          }
-        }
-      } else {
-        int r = first;
+      for (int k = 0; k < NR; ++k) {
         const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = unpack16<DT>(ld16<true>(p + (elem(v) - off) * ES));
-        for (int k = 1; k < N; ++k) {
-          r = r + 1 == N ? 0 : r + 1;
-          p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
-#pragma unroll
-          for (int v = 0; v < V; ++v) {
-            const Vec<DT> y = unpack16<DT>(ld16<true>(p + (elem(v) - off) * ES));
-#pragma unroll
-            for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
-          }
-        }
+        for (int v = 0; v < V; ++v) x[k][v] = ld16<true>(p + elem(v) * ES);
+        r = r + 1 == NR ? 0 : r + 1;
       }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const u32x4 out = pack16<DT>(acc[v]);
-        for (int d = 0; d < N; ++d)
-          st16<true>((char*)ld_u64(ptr + (uint64_t)d * ntensors + t) + (elem(v) - off) * ES, out);
+        acc[v] = unpack16<DT>(x[0][v]);
+#pragma unroll
+        for (int k = 1; k < NR; ++k) {
+          const Vec<DT> y = unpack16<DT>(x[k][v]);
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
+        }
       }
-      return;
-    }
-  }
-  // Tiles that cross a tensor boundary, reach into a zero gap, or are the
-  // ragged end of a chunk: element by element, each finding its tensor.
-  for (int v = 0; v < V; ++v) {
-    const uint64_t e = elem(v);
-    for (int i = 0; i < E; ++i) {
-      const uint64_t f = e + i;
-      if (f >= tile1) break;
-      const uint64_t t = t0 + tensor_of(f);
-      const uint64_t off = ld_u64(ten + 2 * t), cnt = ld_u64(ten + 2 * t + 1);
-      if (f - off >= cnt) continue;  // zero gap after the tensor: nothing stored
+    } else {
       int r = first;
-      float acc = load_elem<DT>((const char*)ld_u64(ptr + (uint64_t)r * ntensors + t), f - off);
+      const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = unpack16<DT>(ld16<true>(p + elem(v) * ES));
       for (int k = 1; k < N; ++k) {
         r = r + 1 == N ? 0 : r + 1;
-        acc = round_to<DT>(load_elem<DT>((const char*)ld_u64(ptr + (uint64_t)r * ntensors + t), f - off) + acc);
+        p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const Vec<DT> y = unpack16<DT>(ld16<true>(p + elem(v) * ES));
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[v].v[i] = round_to<DT>(y.v[i] + acc[v].v[i]);
+        }
       }
-      for (int d = 0; d < N; ++d) store_elem<DT>((char*)ld_u64(ptr + (uint64_t)d * ntensors + t), f - off, acc);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const u32x4 out = pack16<DT>(acc[v]);
+      for (int d = 0; d < N; ++d)
+        st16<true>((char*)ld_u64(ptr + (uint64_t)d * ntensors + t) + elem(v) * ES, out);
+    }
+    return;
+  }
+  // Tiles that cross a tensor boundary, reach into a zero gap, or are the
+  // ragged end of a chunk.  Tensors start on 16-byte boundaries inside the
+  // bucket, so each lane's 16-byte vector lies in one tensor (or in its zero
+  // gap): the lane finds that tensor and moves whole vectors, and only a
+  // tensor's last, partial vector goes element by element.  Chunk ends and
+  // padded tensor ends are multiples of the vector, so no vector crosses the
+  // tile's end.
+  const TileLoc loc = locate_tile(tab, N, blockIdx.x, kTile);
+  if (loc.empty) return;
+  auto tensor_of = [&](uint64_t f) {
+    return upper_index(0, loc.nt, f, [&](uint64_t i) { return ld_u64(ten + 2 * (loc.t0 + i)); });
+  };
+  for (int v = 0; v < V; ++v) {
+    const uint64_t f = loc.tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E;
+    if (f >= loc.tile1) continue;
+    const uint64_t t = loc.t0 + tensor_of(f);
+    const uint64_t off = ld_u64(ten + 2 * t), cnt = ld_u64(ten + 2 * t + 1);
+    const uint64_t rel = f - off;
+    if (rel >= cnt) continue;  // zero gap after the tensor: nothing stored
+    auto rank_ptr = [&](int r) { return (char*)ld_u64(ptr + (uint64_t)r * ntensors + t); };
+    if (cnt - rel >= (uint64_t)E) {
+      int r = first;
+      Vec<DT> acc = unpack16<DT>(ld16<true>(rank_ptr(r) + rel * ES));
+      for (int k = 1; k < N; ++k) {
+        r = r + 1 == N ? 0 : r + 1;
+        const Vec<DT> y = unpack16<DT>(ld16<true>(rank_ptr(r) + rel * ES));
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc.v[i] = round_to<DT>(y.v[i] + acc.v[i]);
+      }
+      const u32x4 out = pack16<DT>(acc);
+      for (int d = 0; d < N; ++d) st16<true>(rank_ptr(d) + rel * ES, out);
+      continue;
+    }
+    const int nv = (int)(cnt - rel);
+    for (int i = 0; i < nv; ++i) {
+      int r = first;
+      float acc = load_elem<DT>(rank_ptr(r), rel + i);
+      for (int k = 1; k < N; ++k) {
+        r = r + 1 == N ? 0 : r + 1;
+        acc = round_to<DT>(load_elem<DT>(rank_ptr(r), rel + i) + acc);
+      }
+      for (int d = 0; d < N; ++d) store_elem<DT>(rank_ptr(d), rel + i, acc);
     }
   }
 }
 
 template <int DT, int NR>
-hipError_t bucket_fold_dispatch(const uint64_t* tab, int n, uint64_t ntensors, uint64_t grid, hipStream_t stream) {
+hipError_t bucket_fold_dispatch(const uint64_t* tab, const u32x4* desc, int n, uint64_t ntensors, uint64_t grid,
+                                hipStream_t stream) {
   constexpr int V = DT == DT_BF16 ? 1 : 2;
   hipLaunchKernelGGL((bucket_fold_kernel<DT, NR, V>), dim3((unsigned)grid), dim3(kThreads),
-                     residency_lds(fold_wgs_per_cu(DT, n)), stream, tab, n, ntensors);
+                     residency_lds(fold_wgs_per_cu(DT, n)), stream, tab, desc, n, ntensors);
   return launch_status(stream);
 }
 
 template <int DT>
-hipError_t bucket_fold_n(const uint64_t* tab, int n, uint64_t ntensors, uint64_t grid, hipStream_t stream) {
+hipError_t bucket_fold_n(const uint64_t* tab, const u32x4* desc, int n, uint64_t ntensors, uint64_t grid,
+                         hipStream_t stream) {
   switch (n) {
-    case 8: return bucket_fold_dispatch<DT, 8>(tab, n, ntensors, grid, stream);
-    case 16: return bucket_fold_dispatch<DT, 16>(tab, n, ntensors, grid, stream);
-    default: return bucket_fold_dispatch<DT, 0>(tab, n, ntensors, grid, stream);
+    case 8: return bucket_fold_dispatch<DT, 8>(tab, desc, n, ntensors, grid, stream);
+    case 16: return bucket_fold_dispatch<DT, 16>(tab, desc, n, ntensors, grid, stream);
+    default: return bucket_fold_dispatch<DT, 0>(tab, desc, n, ntensors, grid, stream);
   }
 }
 
@@ -220,13 +299,19 @@ uint64_t bucket_fold_tile_elems(int dt) {
   return (uint64_t)kThreads * (dt == DT_F32 ? 4 : 8) * (dt == DT_BF16 ? 1 : 2);
 }
 
-hipError_t launch_bucket_fold(const uint64_t* dev_table, int n, uint64_t ntensors, uint64_t grid, int dt,
-                              hipStream_t stream) {
+hipError_t launch_bucket_fold(const uint64_t* dev_table, void* dev_desc, int n, uint64_t ntensors, uint64_t grid,
+                              int dt, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
+  u32x4* desc = (u32x4*)dev_desc;
+  const uint64_t dgrid = (grid + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(bucket_desc_kernel, dim3((unsigned)dgrid), dim3(kThreads), 0, stream, dev_table, n, ntensors,
+                     grid, bucket_fold_tile_elems(dt), desc);
+  const hipError_t e = launch_status(stream);
+  if (e != hipSuccess) return e;
   switch (dt) {
-    case DT_F32: return bucket_fold_n<DT_F32>(dev_table, n, ntensors, grid, stream);
-    case DT_F16: return bucket_fold_n<DT_F16>(dev_table, n, ntensors, grid, stream);
-    default: return bucket_fold_n<DT_BF16>(dev_table, n, ntensors, grid, stream);
+    case DT_F32: return bucket_fold_n<DT_F32>(dev_table, desc, n, ntensors, grid, stream);
+    case DT_F16: return bucket_fold_n<DT_F16>(dev_table, desc, n, ntensors, grid, stream);
+    default: return bucket_fold_n<DT_BF16>(dev_table, desc, n, ntensors, grid, stream);
   }
 }
 

@@ -87,8 +87,11 @@ def test_bucket_plan_matches_oracle(orc):
 
 def test_bucketed_workspace_sizes():
     counts = [10, 20, 5, 100, 3, 3]
-    # fused: table of 2 + 5*4 + (2 + 8)*6 words, rounded to 256 bytes
-    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == (2 + 20 + 60) * 8 // 256 * 256 + 256
+    # fused: table of 2 + 5*4 + (2 + 8)*6 words, rounded to 256 bytes, then
+    # 16 bytes per workgroup: 4 buckets, each one 2048-element tile per chunk
+    # for 8 ranks
+    table = (2 + 20 + 60) * 8 // 256 * 256 + 256
+    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == table + 4 * 8 * 16  # 512, a multiple of 256
     # stepwise: 8 flat buffers of the largest padded bucket (100 bf16 -> 208 bytes -> 256)
     assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60, rar.ALGO_STEPWISE) == 8 * 256
 
