@@ -68,13 +68,27 @@ COUNTER_KERNELS = {
     "rank_hash_f32_n8": {
         "match": "::rank_hash_kernel", "workload": "N=8 x 256 MiB",
         "algorithmic": 8 * 256 * MIB, "sources": [_CSRC + "hash_kernels.hip", _CSRC + "common.hpp"]},
+    "bucket_fold_bf16_n16": {
+        "match": "::bucket_fold_kernel<2, 16,", "workload": "N=16 bf16, 200 gradient tensors in 25 MiB buckets",
+        # every rank's copy of every gradient element read once and written once
+        "algorithmic": lambda: 2 * 16 * 2 * _bucket_elements(),
+        "sources": [_CSRC + "bucket_kernels.hip", _CSRC + "common.hpp"]},
 }
+
+
+def _bucket_elements():
+    from ring_all_reduce_scatter_amd import inputs
+    return sum(inputs.bucket_sizes(inputs.WORKLOADS["buckets"]["ntensors"]))
+
+
+def _algorithmic(k):
+    return k["algorithmic"]() if callable(k["algorithmic"]) else k["algorithmic"]
 # calibration copy of the counters run: 256 MiB read and 256 MiB written
 CALIBRATION = {"match": "copy_jobs_kernel", "bytes": 256 * MIB}
 PMC_COMMANDS = [
-    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv "
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv "
     "-d $R/gpurun_out/pmc_fetch -o pmc -- python -u $R/bench.py --counters",
-    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv "
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv "
     "-d $R/gpurun_out/pmc_write -o pmc -- python -u $R/bench.py --counters",
     "python bench.py --ingest-counters gpurun_out/pmc_fetch/pmc_counter_collection.csv "
     "gpurun_out/pmc_write/pmc_counter_collection.csv",
@@ -496,7 +510,9 @@ def extra_legs(args):
     nb, _ = rar.bucket_plan(sizes, rar.BF16, wk["cap_bytes"])
     out["buckets_bf16_allreduce"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S3, wk["n"], ms), 1),
                                      "buckets": nb, "elements_per_rank": sum(sizes),
-                                     "frac_of_roofline_fold_only_bytes": round(2 * wk["n"] * S3 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                                     "frac_of_roofline_fold_only_bytes": round(2 * wk["n"] * S3 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "traffic": counter_traffic("bucket_fold_bf16_n16",
+                                                                COUNTER_KERNELS["bucket_fold_bf16_n16"]["sources"])}
     del dev, arena, ws, step
     torch.cuda.empty_cache()
     # [P2] exercise: ring vs tree wall-clock on 4 ranks at 1 KB, 1 MB and 16 MB
@@ -535,7 +551,8 @@ def extra_legs(args):
 def counters_run(reps=3):
     """Short launch sequence for hardware-counter passes: a plain copy of known
     size (broadcast over 2 ranks of 256 MiB fp32: 256 MiB read, 256 MiB written)
-    to calibrate FETCH_SIZE / WRITE_SIZE, then the two timed kernels."""
+    to calibrate FETCH_SIZE / WRITE_SIZE, then the fused folds (fp32, BFP-8,
+    BFP-8 with error feedback), the rank hash and the bucketed fold."""
     import torch
 
     import ring_all_reduce_scatter_amd as rar
@@ -566,6 +583,17 @@ def counters_run(reps=3):
     hws = torch.empty(rar.HASH_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
     for _ in range(reps):
         rar.rank_hashes(bufs, hws)
+    del bufs, hws
+    # zero-copy bucketed allreduce (values do not change the bytes moved)
+    wk = inputs.WORKLOADS["buckets"]
+    sizes = inputs.bucket_sizes(wk["ntensors"])
+    arena, dev = rar.rank_tensors(wk["n"], sizes, torch.bfloat16, "cuda:0")
+    arena.normal_(0.0, 1e-3)
+    ws = torch.empty(rar.bucketed_workspace_bytes(sizes, wk["n"], rar.BF16, wk["cap_bytes"]), dtype=torch.uint8,
+                     device="cuda:0")
+    step = rar.BucketedAllreduce(dev, wk["cap_bytes"], ws)
+    for _ in range(reps):
+        step()
     torch.cuda.synchronize()
     log("[bench] counters run done")
 
@@ -625,10 +653,11 @@ def ingest_counters(fetch_csv, write_csv):
         hbm = int(round((fk * cal_bytes_kib / cf + wk * cal_bytes_kib / cw) * 1024))
         out[key] = {"kernel_match": k["match"], "workload": k["workload"], "fetch_kib": fk, "write_kib": wk,
                     "dispatches": len(fv), "hbm_bytes_per_launch": hbm,
-                    "algorithmic_bytes_per_launch": k["algorithmic"], "source_sha": source_sha(k["sources"]),
+                    "algorithmic_bytes_per_launch": _algorithmic(k), "source_sha": source_sha(k["sources"]),
                     "sources": k["sources"]}
-        rows.append(f"| `{k['match']}` ({k['workload']}) | {fk:.1f} | {wk:.1f} | {hbm:,} | {k['algorithmic']:,} | "
-                    f"{hbm / k['algorithmic']:.4f} |")
+        alg = _algorithmic(k)
+        rows.append(f"| `{k['match']}` ({k['workload']}) | {fk:.1f} | {wk:.1f} | {hbm:,} | {alg:,} | "
+                    f"{hbm / alg:.4f} |")
     with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
