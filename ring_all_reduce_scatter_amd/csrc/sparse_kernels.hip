@@ -53,6 +53,31 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   return base + x - v;
 }
 
+// Workgroup sums of two per-lane integers (every lane receives both), with
+// one barrier: wavefront butterflies, then the four wavefront sums via LDS.
+__device__ __forceinline__ void block_sum2(uint32_t a, uint32_t b, uint32_t* sa, uint32_t* sb) {
+  __shared__ uint32_t part[2][kThreads / 64];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    a += (uint32_t)__shfl_xor((int)a, d, 64);
+    b += (uint32_t)__shfl_xor((int)b, d, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    part[0][w] = a;
+    part[1][w] = b;
+  }
+  __syncthreads();
+  uint32_t x = 0, y = 0;
+#pragma unroll
+  for (int k = 0; k < kThreads / 64; ++k) {
+    x += part[0][k];
+    y += part[1][k];
+  }
+  *sa = x;
+  *sb = y;
+}
+
 __device__ __forceinline__ uint64_t round16(uint64_t x) { return (x + 15) / 16 * 16; }
 
 template <int DT>
@@ -72,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void comp_count_kernel(CompJobs jobs, uin
   const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
   const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
   const G8 x = load_group<DT>(jobs.src[j], elem, nv);
-  uint32_t total;
-  block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
+  uint32_t total, unused;
+  block_sum2((uint32_t)nonzeros<DT>(x, nv), 0u, &total, &unused);
   if (threadIdx.x == 0) jobs.tiles[j][t] = total;
 }
 
@@ -87,8 +112,7 @@ __device__ __forceinline__ void tile_prefix(const uint32_t* nnzs, uint32_t T, ui
     b += v;
     if (i < t) a += v;
   }
-  block_exclusive_scan(a, before);
-  block_exclusive_scan(b, total);
+  block_sum2(a, b, before, total);
 }
 
 template <int DT, int LPB>
@@ -103,6 +127,10 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
   const uint32_t T = (uint32_t)((len + kTileElems - 1) / kTileElems);
   const char* src = jobs.src[j];
   uint8_t* msg = jobs.msg[j];
+  // the tile's data is loaded first, so its latency overlaps the prefix sums
+  const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
+  const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
+  const G8 x = load_group<DT>(src, elem, nv);
   uint32_t before, nnz32;
   tile_prefix(jobs.tiles[j], T, t, &before, &nnz32);
   const uint64_t nnz = nnz32;
@@ -121,9 +149,6 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
       atomicAdd((unsigned long long*)&traffic[kMaxRanks + (jobs.from[j] + h + 1) % n], (unsigned long long)bytes);
     }
   }
-  const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
-  const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
-  const G8 x = load_group<DT>(src, elem, nv);
   if (sparse) {
     uint8_t* vals = msg + 16;
     uint32_t* idx = (uint32_t*)(msg + 16 + round16(nnz * ES));
@@ -285,8 +310,8 @@ __device__ __forceinline__ void comp_decode_acc_count_tile(const uint8_t* msg, u
       mine -= (before != 0.0f ? 1u : 0u);
     }
   }
-  uint32_t total;
-  block_exclusive_scan(mine, &total);
+  uint32_t total, unused;
+  block_sum2(mine, 0u, &total, &unused);
   if (threadIdx.x == 0) *count_out = total;
 }
 
