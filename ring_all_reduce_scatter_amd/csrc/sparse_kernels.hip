@@ -178,15 +178,28 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
   }
 }
 
-// First position in idx[0, n) whose value is >= key.
-__device__ __forceinline__ uint64_t lower_bound_u32(const uint32_t* idx, uint64_t n, uint64_t key) {
-  uint64_t lo = 0, hi = n;
-  while (lo < hi) {
-    const uint64_t mid = (lo + hi) / 2;
-    if ((uint64_t)idx[mid] < key) lo = mid + 1;
-    else hi = mid;
+// First position in idx[0, n) whose value is >= key (idx ascending),
+// searched by a whole wavefront: each round the 64 lanes probe 64 evenly
+// spaced positions and a ballot narrows the range 64-fold, so a message of
+// nnz indices costs about log64(nnz) rounds of one load per lane instead of
+// log2(nnz) dependent loads.  Every lane of the wavefront must call it and
+// receives the result.
+__device__ __forceinline__ uint64_t wave_lower_bound_u32(const uint32_t* idx, uint64_t n, uint64_t key) {
+  const uint64_t lane = threadIdx.x & 63u;
+  uint64_t lo = 0, hi = n;  // the answer lies in [lo, hi]
+  while (hi - lo > 64) {
+    const uint64_t step = (hi - lo + 63) / 64;
+    const uint64_t pos = lo + lane * step;
+    const bool below = pos < hi && (uint64_t)idx[pos] < key;
+    const uint64_t c = (uint64_t)__popcll(__ballot(below));  // lanes 0..c-1 are below key
+    const uint64_t nlo = c ? lo + (c - 1) * step + 1 : lo;
+    const uint64_t nhi = lo + c * step < hi ? lo + c * step : hi;
+    lo = nlo;
+    hi = nhi;
   }
-  return lo;
+  const uint64_t pos = lo + lane;
+  const bool below = pos < hi && (uint64_t)idx[pos] < key;
+  return lo + (uint64_t)__popcll(__ballot(below));
 }
 
 // Decode one tile of one message into `nfan` destinations (rank buffers at
@@ -220,9 +233,10 @@ __device__ __forceinline__ void comp_decode_tile(const uint8_t* msg, uint64_t le
   const uint64_t nnz = hdr[0];
   const uint8_t* vals = msg + 16;
   const uint32_t* idx = (const uint32_t*)(msg + 16 + round16(nnz * ES));
-  if (threadIdx.x == 0) {
-    range[0] = lower_bound_u32(idx, nnz, tlo);
-    range[1] = lower_bound_u32(idx, nnz, thi);
+  // wavefront 0 finds the slice's start, wavefront 1 its end
+  if (threadIdx.x < 128) {
+    const uint64_t r = wave_lower_bound_u32(idx, nnz, threadIdx.x < 64 ? tlo : thi);
+    if ((threadIdx.x & 63u) == 0) range[threadIdx.x >> 6] = r;
   }
   if constexpr (!ACC) {
     const uint64_t elem = tlo + (uint64_t)threadIdx.x * 8;
@@ -283,9 +297,10 @@ __device__ __forceinline__ void comp_decode_acc_count_tile(const uint8_t* msg, u
     const uint64_t nnz = hdr[0];
     const uint8_t* vals = msg + 16;
     const uint32_t* idx = (const uint32_t*)(msg + 16 + round16(nnz * ES));
-    if (threadIdx.x == 0) {
-      range[0] = lower_bound_u32(idx, nnz, tlo);
-      range[1] = lower_bound_u32(idx, nnz, thi);
+    // wavefront 0 finds the slice's start, wavefront 1 its end
+    if (threadIdx.x < 128) {
+      const uint64_t r = wave_lower_bound_u32(idx, nnz, threadIdx.x < 64 ? tlo : thi);
+      if ((threadIdx.x & 63u) == 0) range[threadIdx.x >> 6] = r;
     }
     if (nv > 0) mine = (uint32_t)nonzeros<DT>(load_group<DT>(dst, elem, nv), nv);
     __syncthreads();  // every lane has read its elements before any scatter writes one
