@@ -113,6 +113,27 @@ def test_compressed_paths_stay_in_bounds(dt, n, count):
         _ws_check(full, used, "stateful")
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("count", [1, 8 * 256 * 2 + 1, 8 * 256 * 3 + 9, 4096 * 5 + 77])
+@pytest.mark.parametrize("block,mbits", [(128, 8), (32, 4)])
+def test_codec_stays_in_bounds(dt, count, block, mbits):
+    """Standalone compress and decompress(-accumulate) write nothing past the
+    message (exactly rar_bfp_bytes long) or the destination, including counts
+    that end inside the last lane group or the second group of a lane."""
+    xs = inputs.block_scaled(2, count, dtype=dt, salt=count) if dt != "f32" else inputs.gradient_like(2, count,
+                                                                                                     salt=count)
+    g = Guarded(xs, dt)
+    nbytes = rar.bfp_bytes(count, block, mbits)
+    msg, full, used = _ws(nbytes)
+    rar.bfp_compress(g.bufs[0], block, mbits, msg)
+    _ws_check(full, used, "compress")
+    rar.bfp_decompress_accumulate(msg, count, block, mbits, g.bufs[1])
+    g.check("decompress-accumulate")
+    rar.bfp_decompress(msg, count, block, mbits, g.bufs[1])
+    g.check("decompress")
+    _ws_check(full, used, "message after decode")
+
+
 def test_bucketed_and_ft_stay_in_bounds():
     n = 4
     sizes = inputs.bucket_sizes(25, lo_exp=2, hi_exp=14, salt=2)
