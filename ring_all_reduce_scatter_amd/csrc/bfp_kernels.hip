@@ -31,7 +31,7 @@ constexpr int kEncBlocksPerJob = 16384;
 // grid: njobs x blocks_per_job; grid-stride over the job's 8-element groups.
 // The loop bound is rounded up to whole workgroups so every lane of a wave
 // takes part in the cross-lane max; lanes past the end hold zeros.
-template <int DT, int LPB, int G>
+template <int DT, int LPB>
 __global__ __launch_bounds__(kThreads) void bfp_encode_kernel(BfpJobs jobs, int lpb_rt, int mbits,
                                                                uint32_t blocks_per_job) {
   const int j = (int)(blockIdx.x / blocks_per_job);
@@ -47,20 +47,11 @@ __global__ __launch_bounds__(kThreads) void bfp_encode_kernel(BfpJobs jobs, int 
   const float qmax = (float)((1 << (mbits - 1)) - 1);
   if (b == 0 && threadIdx.x < eb - nb) msg[nb + threadIdx.x] = 0;  // exponent padding
   const uint64_t ngroups = (count + 7) / 8;
-  const uint64_t stride = (uint64_t)blocks_per_job * kThreads * G;
-  for (uint64_t g0 = (uint64_t)b * kThreads * G; g0 < ngroups; g0 += stride) {
-    // G groups per lane, all loaded before the first encode
-    G8 x[G];
-    int nv[G];
-    uint64_t elem[G];
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      elem[k] = (g0 + (uint64_t)k * kThreads + threadIdx.x) * 8;
-      nv[k] = elem[k] >= count ? 0 : (count - elem[k] >= 8 ? 8 : (int)(count - elem[k]));
-      x[k] = load_group<DT>(src, elem[k], nv[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < G; ++k) encode_group<DT, LPB>(x[k], nv[k], elem[k], msg, mant, lpb, mbits, qmax);
+  const uint64_t stride = (uint64_t)blocks_per_job * kThreads;
+  for (uint64_t g0 = (uint64_t)b * kThreads; g0 < ngroups; g0 += stride) {
+    const uint64_t elem = (g0 + threadIdx.x) * 8;
+    const int nv = elem >= count ? 0 : (count - elem >= 8 ? 8 : (int)(count - elem));
+    encode_group<DT, LPB>(load_group<DT>(src, elem, nv), nv, elem, msg, mant, lpb, mbits, qmax);
   }
 }
 
@@ -98,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void bfp_forward_kernel(FwdJobs jobs, int
   }
 }
 
-template <int DT, bool ACC, int G>
+template <int DT, bool ACC>
 __global__ __launch_bounds__(kThreads) void bfp_decode_kernel(BfpJobs jobs, int block, int mbits,
                                                                uint32_t blocks_per_job) {
   const int j = (int)(blockIdx.x / blocks_per_job);
@@ -108,31 +99,17 @@ __global__ __launch_bounds__(kThreads) void bfp_decode_kernel(BfpJobs jobs, int 
   char* dst = jobs.dst[j];
   const uint64_t eb = bfp_exp_bytes(count, block);
   const uint64_t ngroups = (count + 7) / 8;
-  const uint64_t stride = (uint64_t)blocks_per_job * kThreads * G;
-  for (uint64_t g0 = (uint64_t)b * kThreads * G; g0 < ngroups; g0 += stride) {
-    // G groups per lane, every load issued before the first store
-    G8 d[G], a[G];
-    int nv[G];
+  const uint64_t stride = (uint64_t)blocks_per_job * kThreads;
+  for (uint64_t g = (uint64_t)b * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    const uint64_t elem = g * 8;
+    const int nv = count - elem >= 8 ? 8 : (int)(count - elem);
+    G8 d = dequant_group(msg, eb, elem, nv, (uint64_t)block, mbits);
+    if constexpr (ACC) {
+      G8 a = load_group<DT>(dst, elem, nv);
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const uint64_t g = g0 + (uint64_t)k * kThreads + threadIdx.x;
-      const uint64_t elem = g * 8;
-      nv[k] = g >= ngroups ? 0 : (count - elem >= 8 ? 8 : (int)(count - elem));
-      if (nv[k] > 0) {
-        d[k] = dequant_group(msg, eb, elem, nv[k], (uint64_t)block, mbits);
-        if constexpr (ACC) a[k] = load_group<DT>(dst, elem, nv[k]);
-      }
+      for (int i = 0; i < 8; ++i) d.v[i] = round_to<DT>(a.v[i] + d.v[i]);
     }
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      if (nv[k] == 0) continue;
-      const uint64_t elem = (g0 + (uint64_t)k * kThreads + threadIdx.x) * 8;
-      if constexpr (ACC) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d[k].v[i] = round_to<DT>(a[k].v[i] + d[k].v[i]);
-      }
-      store_group<DT>(dst, elem, nv[k], d[k]);
-    }
+    store_group<DT>(dst, elem, nv, d);
   }
 }
 
@@ -626,16 +603,9 @@ __global__ void fill_u64_kernel(uint64_t* dst, int n, U64Vals vals) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = vals.v[i];
 }
 
-// 8-element groups per lane and iteration of the standalone encoder and
-// decoder: two for 16-bit data (both loaded before either is coded), one for
-// binary32, whose group is already two 16-byte loads.  On MI355X (128M fp16,
-// 8-bit) two groups took decode-accumulate from 5.15 to 5.33 TB/s and the
-// staged BFP-8 allreduce from 2.52 to 2.45 ms; the encoder stayed at 5.0-5.1.
-int codec_groups(int dt) { return dt == DT_F32 ? 1 : 2; }
-
-uint32_t blocks_for(uint64_t maxlen, int g) {
+uint32_t blocks_for(uint64_t maxlen) {
   const uint64_t groups = (maxlen + 7) / 8;
-  uint64_t blocks = (groups + (uint64_t)kThreads * g - 1) / ((uint64_t)kThreads * g);
+  uint64_t blocks = (groups + kThreads - 1) / kThreads;
   if (blocks > kEncBlocksPerJob) blocks = kEncBlocksPerJob;
   return (uint32_t)(blocks ? blocks : 1);
 }
@@ -646,13 +616,13 @@ uint64_t max_len(const BfpJobs& jobs) {
   return m;
 }
 
-template <int DT, int G>
+template <int DT>
 void encode_dispatch(const BfpJobs& jobs, int block, int mbits, dim3 grid, uint32_t bpj,
                      hipStream_t stream) {
   if (block == 128)
-    hipLaunchKernelGGL((bfp_encode_kernel<DT, 16, G>), grid, dim3(kThreads), 0, stream, jobs, 16, mbits, bpj);
+    hipLaunchKernelGGL((bfp_encode_kernel<DT, 16>), grid, dim3(kThreads), 0, stream, jobs, 16, mbits, bpj);
   else
-    hipLaunchKernelGGL((bfp_encode_kernel<DT, 0, G>), grid, dim3(kThreads), 0, stream, jobs, block / 8, mbits,
+    hipLaunchKernelGGL((bfp_encode_kernel<DT, 0>), grid, dim3(kThreads), 0, stream, jobs, block / 8, mbits,
                        bpj);
 }
 
@@ -752,7 +722,7 @@ hipError_t launch_bfp_forward(const FwdJobs& jobs, int dt, int block, int mbits,
   uint64_t ml = 0;
   for (int j = 0; j < jobs.njobs; ++j) ml = jobs.len[j] > ml ? jobs.len[j] : ml;
   if (jobs.njobs == 0 || ml == 0) return hipSuccess;
-  const uint32_t bpj = blocks_for(ml, 1);
+  const uint32_t bpj = blocks_for(ml);
   dim3 grid((unsigned)(jobs.njobs * bpj));
 #define RAR_FWD(DTV)                                                                                          \
   if (block == 128)                                                                                           \
@@ -771,19 +741,12 @@ hipError_t launch_bfp_forward(const FwdJobs& jobs, int dt, int block, int mbits,
 hipError_t launch_bfp_encode(const BfpJobs& jobs, int dt, int block, int mbits, hipStream_t stream) {
   const uint64_t ml = max_len(jobs);
   if (jobs.njobs == 0 || ml == 0) return hipSuccess;
-  const int g = codec_groups(dt);
-  const uint32_t bpj = blocks_for(ml, g);
+  const uint32_t bpj = blocks_for(ml);
   dim3 grid((unsigned)(jobs.njobs * bpj));
   switch (dt) {
-    case DT_F32: encode_dispatch<DT_F32, 1>(jobs, block, mbits, grid, bpj, stream); break;
-    case DT_F16:
-      if (g == 2) encode_dispatch<DT_F16, 2>(jobs, block, mbits, grid, bpj, stream);
-      else encode_dispatch<DT_F16, 1>(jobs, block, mbits, grid, bpj, stream);
-      break;
-    default:
-      if (g == 2) encode_dispatch<DT_BF16, 2>(jobs, block, mbits, grid, bpj, stream);
-      else encode_dispatch<DT_BF16, 1>(jobs, block, mbits, grid, bpj, stream);
-      break;
+    case DT_F32: encode_dispatch<DT_F32>(jobs, block, mbits, grid, bpj, stream); break;
+    case DT_F16: encode_dispatch<DT_F16>(jobs, block, mbits, grid, bpj, stream); break;
+    default: encode_dispatch<DT_BF16>(jobs, block, mbits, grid, bpj, stream); break;
   }
   return launch_status(stream);
 }
@@ -792,22 +755,17 @@ hipError_t launch_bfp_decode(const BfpJobs& jobs, int dt, int block, int mbits, 
                              hipStream_t stream) {
   const uint64_t ml = max_len(jobs);
   if (jobs.njobs == 0 || ml == 0) return hipSuccess;
-  const int g = codec_groups(dt);
-  const uint32_t bpj = blocks_for(ml, g);
+  const uint32_t bpj = blocks_for(ml);
   dim3 grid((unsigned)(jobs.njobs * bpj)), blk(kThreads);
-#define RAR_DEC(DTV, G)                                                                                   \
-  if (accumulate)                                                                                         \
-    hipLaunchKernelGGL((bfp_decode_kernel<DTV, true, G>), grid, blk, 0, stream, jobs, block, mbits, bpj); \
-  else                                                                                                    \
-    hipLaunchKernelGGL((bfp_decode_kernel<DTV, false, G>), grid, blk, 0, stream, jobs, block, mbits, bpj);
+#define RAR_DEC(DTV)                                                                                   \
+  if (accumulate)                                                                                      \
+    hipLaunchKernelGGL((bfp_decode_kernel<DTV, true>), grid, blk, 0, stream, jobs, block, mbits, bpj); \
+  else                                                                                                 \
+    hipLaunchKernelGGL((bfp_decode_kernel<DTV, false>), grid, blk, 0, stream, jobs, block, mbits, bpj);
   switch (dt) {
-    case DT_F32: RAR_DEC(DT_F32, 1) break;
-    case DT_F16:
-      if (g == 2) { RAR_DEC(DT_F16, 2) } else { RAR_DEC(DT_F16, 1) }
-      break;
-    default:
-      if (g == 2) { RAR_DEC(DT_BF16, 2) } else { RAR_DEC(DT_BF16, 1) }
-      break;
+    case DT_F32: RAR_DEC(DT_F32) break;
+    case DT_F16: RAR_DEC(DT_F16) break;
+    default: RAR_DEC(DT_BF16) break;
   }
 #undef RAR_DEC
   return launch_status(stream);
@@ -820,7 +778,7 @@ hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs_in, const RankPtrs& fan,
   for (int j = 0; j < jobs.njobs; ++j) jobs.dst[j] = (char*)(uintptr_t)elem_off[j];
   const uint64_t ml = max_len(jobs);
   if (jobs.njobs == 0 || ml == 0) return hipSuccess;
-  const uint32_t bpj = blocks_for(ml, 1);
+  const uint32_t bpj = blocks_for(ml);
   dim3 grid((unsigned)(jobs.njobs * bpj)), blk(kThreads);
   switch (dt) {
     case DT_F32:
