@@ -290,8 +290,14 @@ def compress_cfg_default() -> CompressCfg:
 
 
 def compress_cfg(**kw) -> CompressCfg:
+    """The library's default configuration with the given fields replaced.
+    Unknown field names raise (a ctypes structure would otherwise keep them
+    as plain Python attributes that the library never sees)."""
     cfg = compress_cfg_default()
+    names = {f[0] for f in CompressCfg._fields_}
     for k, v in kw.items():
+        if k not in names:
+            raise TypeError(f"compress_cfg: unknown field {k!r} (fields: {', '.join(sorted(names))})")
         setattr(cfg, k, v)
     return cfg
 

@@ -292,3 +292,10 @@ def test_rank_tensors_placement():
     ends = [(v.data_ptr(), v.data_ptr() + v.numel() * 2) for row in views for v in row]
     ends.sort()
     assert all(a[1] <= b[0] for a, b in zip(ends, ends[1:]))
+
+
+def test_compress_cfg_rejects_unknown_fields():
+    cfg = rar.compress_cfg(block=32, mbits=4)
+    assert (cfg.block, cfg.mbits) == (32, 4)
+    with pytest.raises(TypeError, match="unknown field 'mbit'"):
+        rar.compress_cfg(mbit=4)
