@@ -181,12 +181,21 @@ __global__ __launch_bounds__(kThreads) void rs_step_kernel(RankPtrs bufs, int N,
 // the sum, which the binomial broadcast then gives to every rank.  The fused
 // kernel applies the same rounds to all N ranks' vectors in registers and
 // stores rank 0's result to every rank.
+//
+// Workgroup -> tile: the launch has kRegions * per workgroups, and workgroup b
+// takes tile (b % kRegions) * per + b / kRegions, so the workgroups dealt to
+// one XCD (b % 8) stream one contiguous region of every rank, as the ring
+// fold's chunk-fastest order does.  The reduction order does not depend on
+// the mapping.
+constexpr uint32_t kRegions = 8;
+
 template <int DT, int NR, int V>
-__global__ __launch_bounds__(kThreads) void tree_fold_kernel(RankPtrs bufs, uint64_t count) {
+__global__ __launch_bounds__(kThreads) void tree_fold_kernel(RankPtrs bufs, uint64_t count, uint32_t per) {
   constexpr int E = Vec<DT>::E;
   constexpr int ES = DtypeSize<DT>::value;
   constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
-  const uint64_t tile0 = (uint64_t)blockIdx.x * kTile;
+  const uint32_t region = blockIdx.x % kRegions;
+  const uint64_t tile0 = ((uint64_t)region * per + blockIdx.x / kRegions) * kTile;
   if (tile0 >= count) return;
   auto elem = [&](int v) -> uint64_t { return tile0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
   if (tile0 + kTile <= count) {
@@ -344,8 +353,9 @@ hipError_t tree_dispatch_v(const RankPtrs& bufs, uint64_t count, hipStream_t str
   constexpr int V = DT == DT_BF16 ? 1 : 2;
   const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * V;
   const uint64_t tiles = (count + tile - 1) / tile;
-  hipLaunchKernelGGL((tree_fold_kernel<DT, NR, V>), dim3((unsigned)tiles), dim3(kThreads),
-                     residency_lds(fold_wgs_per_cu(DT, NR)), stream, bufs, count);
+  const uint64_t per = (tiles + kRegions - 1) / kRegions;
+  hipLaunchKernelGGL((tree_fold_kernel<DT, NR, V>), dim3((unsigned)(per * kRegions)), dim3(kThreads),
+                     residency_lds(fold_wgs_per_cu(DT, NR)), stream, bufs, count, (uint32_t)per);
   return launch_status(stream);
 }
 
