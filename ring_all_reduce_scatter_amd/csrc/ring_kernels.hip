@@ -29,7 +29,7 @@ namespace {
 // 16-byte vectors per thread and workgroups per CU of the fused fold, tuned
 // for N = 8 on MI355X (about 64 KiB of loads in flight per CU).  bf16 spends
 // more ALU per byte on its software rounding, so it keeps one vector per rank
-// and two workgroups per CU to hide that latency.
+// and more workgroups per CU to hide that latency (fold_wgs_per_cu).
 template <int DT>
 struct FoldVecs {
   static constexpr int value = DT == DT_BF16 ? 1 : 2;
@@ -397,7 +397,7 @@ int fold_wgs_per_cu(int dt, int n) {
   switch (n) {
     case 2: return b16 ? 4 : 3;
     case 4: return b16 ? 2 : 1;
-    case 8:
+    case 8: return b16 ? 3 : 1;  // bf16 8 x 128M: 728 us at 3, 766 at 2, 741 at 1, 734 at 4
     case 16: return b16 ? 2 : 1;
     default: return 2;
   }
