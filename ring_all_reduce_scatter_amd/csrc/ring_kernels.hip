@@ -354,8 +354,12 @@ hipError_t tree_dispatch_v(const RankPtrs& bufs, uint64_t count, hipStream_t str
   const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * V;
   const uint64_t tiles = (count + tile - 1) / tile;
   const uint64_t per = (tiles + kRegions - 1) / kRegions;
+  // the ring fold's residency table, except bf16 at 8 ranks: the tree's
+  // shorter add chain runs best at two workgroups per CU (709-715 us for
+  // 8 x 128M against 747 at three)
+  const int wgs = DT == DT_BF16 && NR == 8 ? 2 : fold_wgs_per_cu(DT, NR);
   hipLaunchKernelGGL((tree_fold_kernel<DT, NR, V>), dim3((unsigned)(per * kRegions)), dim3(kThreads),
-                     residency_lds(fold_wgs_per_cu(DT, NR)), stream, bufs, count, (uint32_t)per);
+                     residency_lds(wgs), stream, bufs, count, (uint32_t)per);
   return launch_status(stream);
 }
 
