@@ -193,6 +193,41 @@ def busbw(bytes_per_rank, n, ms):
     return 2.0 * bytes_per_rank * (n - 1) / n / (ms * 1e-3) / 1e9
 
 
+def copy_peak(reps=10):
+    """Achievable HBM rate of a plain copy on this GPU: 1 GiB read and 1 GiB
+    written by the library's copy kernel (a 2-rank broadcast) and by torch's
+    device-to-device copy, median of `reps` launches each, timed with HIP
+    events on the launch stream; the faster of the two is the peak."""
+    import torch
+
+    import ring_all_reduce_scatter_amd as rar
+    count = 256 << 20
+    bufs = [torch.full((count,), float(r + 1), device="cuda:0") for r in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def median_ms(run):
+        run()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run()
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        return ms[len(ms) // 2]
+
+    rates = {"copy_jobs_kernel": median_ms(lambda: rar.broadcast(bufs, 0)),
+             "torch copy_ (device to device)": median_ms(lambda: bufs[1].copy_(bufs[0]))}
+    name = min(rates, key=rates.get)
+    t = rates[name]
+    return {"value": round(2 * count * 4 / (t * 1e-3) / 1e9, 1), "unit": "GB/s", "kernel": name,
+            "bytes": 2 * count * 4,
+            "ms": {k: round(v, 4) for k, v in rates.items()}}
+
+
 def fp32_leg(args):
     import numpy as np
     import torch
@@ -729,8 +764,12 @@ def main():
         "parity": f["parity_first_timed_output"],
         "bytes_per_rank_sent": f["bytes_per_rank"]["sent"][0],
     }
+    cp = copy_peak()
+    line["copy_peak"] = cp
+    line["roofline"]["frac_of_copy_peak"] = round(line["roofline"]["achieved"] / cp["value"], 4)
     if not args.skip_bfp8:
         line["bfp8"] = bfp8_leg(args)
+        line["bfp8"]["roofline"]["frac_of_copy_peak"] = round(line["bfp8"]["roofline"]["achieved"] / cp["value"], 4)
     if args.extra:
         line["extra"] = extra_legs(args)
     if args.jsonl:
