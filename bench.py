@@ -193,6 +193,21 @@ def busbw(bytes_per_rank, n, ms):
     return 2.0 * bytes_per_rank * (n - 1) / n / (ms * 1e-3) / 1e9
 
 
+class pinned_core:
+    """Run the enclosed CPU work on one host core (the last one this process
+    may use), restoring the previous affinity afterwards."""
+
+    def __enter__(self):
+        self.prev = os.sched_getaffinity(0)
+        self.core = max(self.prev)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.prev)
+        return False
+
+
 def copy_peak(reps=10):
     """Achievable HBM rate of a plain copy on this GPU: 1 GiB read and 1 GiB
     written by the library's copy kernel (a 2-rank broadcast) and by torch's
@@ -269,16 +284,17 @@ def fp32_leg(args):
         log("[bench] fp32 leg: oracle on the full workload (single thread), 3 runs")
         times = []
         ref = None
-        for _ in range(3):
-            bufs = [x.copy() for x in xs]
-            t = time.perf_counter()
-            oracle.ring_allreduce(bufs)
-            times.append(time.perf_counter() - t)
-            ref = bufs
+        with pinned_core() as pin:
+            for _ in range(3):
+                bufs = [x.copy() for x in xs]
+                t = time.perf_counter()
+                oracle.ring_allreduce(bufs)
+                times.append(time.perf_counter() - t)
+                ref = bufs
         med = sorted(times)[1]
         cpu = {"value": round(busbw(S, n, med * 1e3), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the whole workload (N={n}, T={count} fp32 per rank), median of 3 single-thread runs "
-                         f"({med:.2f} s each)", **host_info()}
+                         f"({med:.2f} s each) pinned to host core {pin.core}", **host_info()}
         parity = all(np.array_equal(first[r].view(np.uint32), ref[r].view(np.uint32)) for r in range(n))
     if parity is None:
         parity = sampled_fp32_parity(xs, first, rar.chunk_len(count, n))
@@ -362,13 +378,15 @@ def bfp8_leg(args):
         sample = count // 16
         log(f"[bench] bfp8 leg: oracle on a sample of T={sample} per rank")
         xs_s = inputs.block_scaled(n, sample, salt=1)
-        t = time.perf_counter()
-        oracle.ring_allreduce_compressed(xs_s, mbits=mbits, unit=w["unit_bytes"] // 2)
-        dt = time.perf_counter() - t
+        with pinned_core() as pin:
+            t = time.perf_counter()
+            oracle.ring_allreduce_compressed(xs_s, mbits=mbits, unit=w["unit_bytes"] // 2)
+            dt = time.perf_counter() - t
         res["cpu_baseline"] = {"value": round(busbw(sample * 2, n, dt * 1e3), 5), "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"N={n}, T={sample} fp16 per rank (1/16 of the workload, same value "
-                                         f"recipe), one single-thread run ({dt:.1f} s)"}
+                                         f"recipe), one single-thread run ({dt:.1f} s) pinned to host core "
+                                         f"{pin.core}"}
     res["parity_first_timed_output"] = sampled_bfp_parity(xs, got0, rar.compressed_chunk_len(count, n, block), mbits)
     return res
 
