@@ -115,27 +115,38 @@ __device__ __forceinline__ void tile_prefix(const uint32_t* nnzs, uint32_t T, ui
   block_sum2(a, b, before, total);
 }
 
+// Tiles per workgroup of the write kernel: a workgroup loads its tiles'
+// data first, sums the unit's tile counts once, then writes the tiles in
+// order, carrying the running non-zero offset from one to the next.
+constexpr uint32_t kWriteTiles = 4;
+
 template <int DT, int LPB>
-__global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uint32_t tiles_max, int lpb_rt,
+__global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uint32_t groups_per_job, int lpb_rt,
                                                                int mbits, float theta, uint64_t* traffic,
                                                                int block) {
   constexpr int ES = DtypeSize<DT>::value;
-  const int j = (int)(blockIdx.x / tiles_max);
-  const uint32_t t = blockIdx.x - (uint32_t)j * tiles_max;
+  const int j = (int)(blockIdx.x / groups_per_job);
+  const uint32_t t0 = (blockIdx.x - (uint32_t)j * groups_per_job) * kWriteTiles;
   const uint64_t len = jobs.len[j];
-  if ((uint64_t)t * kTileElems >= len) return;
+  if ((uint64_t)t0 * kTileElems >= len) return;
   const uint32_t T = (uint32_t)((len + kTileElems - 1) / kTileElems);
   const char* src = jobs.src[j];
   uint8_t* msg = jobs.msg[j];
-  // the tile's data is loaded first, so its latency overlaps the prefix sums
-  const uint64_t elem = (uint64_t)t * kTileElems + (uint64_t)threadIdx.x * 8;
-  const int nv = elem >= len ? 0 : (len - elem >= 8 ? 8 : (int)(len - elem));
-  const G8 x = load_group<DT>(src, elem, nv);
+  // the tiles' data is loaded first, so its latency overlaps the prefix sums
+  G8 x[kWriteTiles];
+  int nv[kWriteTiles];
+  uint64_t elem[kWriteTiles];
+#pragma unroll
+  for (uint32_t k = 0; k < kWriteTiles; ++k) {
+    elem[k] = (uint64_t)(t0 + k) * kTileElems + (uint64_t)threadIdx.x * 8;
+    nv[k] = elem[k] >= len ? 0 : (len - elem[k] >= 8 ? 8 : (int)(len - elem[k]));
+    x[k] = load_group<DT>(src, elem[k], nv[k]);
+  }
   uint32_t before, nnz32;
-  tile_prefix(jobs.tiles[j], T, t, &before, &nnz32);
+  tile_prefix(jobs.tiles[j], T, t0, &before, &nnz32);
   const uint64_t nnz = nnz32;
   const bool sparse = (double)(len - nnz) > (double)theta * (double)len;  // zeros > theta * len
-  if (t == 0 && threadIdx.x == 0) {
+  if (t0 == 0 && threadIdx.x == 0) {
     uint32_t* hdr = (uint32_t*)msg;
     hdr[0] = sparse ? (uint32_t)nnz : 0u;
     hdr[1] = sparse ? 1u : 0u;
@@ -152,17 +163,23 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
   if (sparse) {
     uint8_t* vals = msg + 16;
     uint32_t* idx = (uint32_t*)(msg + 16 + round16(nnz * ES));
-    uint32_t total;
-    uint64_t pos = before + block_exclusive_scan((uint32_t)nonzeros<DT>(x, nv), &total);
+    uint64_t base = before;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i >= nv || x.v[i] == 0.0f) continue;
-      if constexpr (ES == 4) ((uint32_t*)vals)[pos] = ((const uint32_t*)src)[elem + i];
-      else ((uint16_t*)vals)[pos] = ((const uint16_t*)src)[elem + i];
-      idx[pos] = (uint32_t)(elem + i);
-      ++pos;
+    for (uint32_t k = 0; k < kWriteTiles; ++k) {
+      if (t0 + k >= T) break;  // uniform in the workgroup
+      uint32_t total;
+      uint64_t pos = base + block_exclusive_scan((uint32_t)nonzeros<DT>(x[k], nv[k]), &total);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i >= nv[k] || x[k].v[i] == 0.0f) continue;
+        if constexpr (ES == 4) ((uint32_t*)vals)[pos] = ((const uint32_t*)src)[elem[k] + i];
+        else ((uint16_t*)vals)[pos] = ((const uint16_t*)src)[elem[k] + i];
+        idx[pos] = (uint32_t)(elem[k] + i);
+        ++pos;
+      }
+      base += total;
     }
-    if (t == 0 && threadIdx.x < 16) {
+    if (t0 == 0 && threadIdx.x < 16) {
       // zero padding between the values and the indices
       const uint64_t pad0 = 16 + nnz * ES, pad1 = 16 + round16(nnz * ES);
       if (pad0 + threadIdx.x < pad1) msg[pad0 + threadIdx.x] = 0;
@@ -173,8 +190,13 @@ __global__ __launch_bounds__(kThreads) void comp_write_kernel(CompJobs jobs, uin
     uint8_t* payload = msg + 16;
     const uint64_t nb = (len + block - 1) / block;
     const uint64_t eb = (nb + 15) / 16 * 16;
-    if (t == 0 && threadIdx.x < eb - nb) payload[nb + threadIdx.x] = 0;
-    encode_group<DT, LPB>(x, nv, elem, payload, payload + eb, lpb, mbits, (float)((1 << (mbits - 1)) - 1));
+    if (t0 == 0 && threadIdx.x < eb - nb) payload[nb + threadIdx.x] = 0;
+    const float qmax = (float)((1 << (mbits - 1)) - 1);
+#pragma unroll
+    for (uint32_t k = 0; k < kWriteTiles; ++k) {
+      if (t0 + k >= T) break;  // uniform: every lane takes part in the block maxima
+      encode_group<DT, LPB>(x[k], nv[k], elem[k], payload, payload + eb, lpb, mbits, qmax);
+    }
   }
 }
 
@@ -363,11 +385,13 @@ hipError_t encode_dt(const CompJobs& jobs, int block, int mbits, float theta, ui
   if (jobs.njobs == 0 || tm == 0) return hipSuccess;
   dim3 grid((unsigned)(jobs.njobs * tm)), blk(kThreads);
   if (!counted) hipLaunchKernelGGL((comp_count_kernel<DT>), grid, blk, 0, stream, jobs, tm);
+  const uint32_t gpj = (tm + kWriteTiles - 1) / kWriteTiles;
+  dim3 wgrid((unsigned)(jobs.njobs * gpj));
   if (block == 128)
-    hipLaunchKernelGGL((comp_write_kernel<DT, 16>), grid, blk, 0, stream, jobs, tm, 16, mbits, theta, traffic,
+    hipLaunchKernelGGL((comp_write_kernel<DT, 16>), wgrid, blk, 0, stream, jobs, gpj, 16, mbits, theta, traffic,
                        block);
   else
-    hipLaunchKernelGGL((comp_write_kernel<DT, 0>), grid, blk, 0, stream, jobs, tm, block / 8, mbits, theta,
+    hipLaunchKernelGGL((comp_write_kernel<DT, 0>), wgrid, blk, 0, stream, jobs, gpj, block / 8, mbits, theta,
                        traffic, block);
   return launch_status(stream);
 }
