@@ -113,6 +113,45 @@ def test_f16_accumulate_is_correctly_rounded_add(orc):
     assert np.all(got[~nz] == 0)
 
 
+def test_f16_accumulate_exhaustive(orc):
+    """Every pair of finite binary16 codes (2^32 pairs, in batches of 64 first
+    operands): the oracle's accumulate equals the exact sum rounded once to
+    binary16 (numpy's binary64 -> binary16 conversion, round-to-nearest-even);
+    exact zeros come out as a zero of either sign.  The batches run on a
+    thread pool (the oracle is plain C without global state, and ctypes and
+    numpy release the GIL), about 40 s on 8 cores."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    codes = _all_f16_codes()
+    finite = codes[np.isfinite(codes.view(np.float16))]
+    b64 = finite.view(np.float16).astype(np.float64)
+    per = 64
+
+    def batch(i):
+        ac = finite[i:i + per]
+        a = np.repeat(ac, finite.size)
+        b = np.tile(finite, ac.size)
+        got = _pairs_via_ring(orc, a.view(np.float16), b.view(np.float16), orc.F16)
+        with np.errstate(over="ignore"):
+            exact = (np.repeat(ac.view(np.float16).astype(np.float64), finite.size)
+                     + np.tile(b64, ac.size))  # exact: binary16 pairs need < 53 bits
+            ref = exact.astype(np.float16)
+        nz = exact != 0
+        gu, ru = got.view(np.uint16)[nz], ref.view(np.uint16)[nz]
+        if not np.array_equal(gu, ru):
+            k = np.flatnonzero(gu != ru)[0]
+            return (f"pair {a[nz][k]:#06x} + {b[nz][k]:#06x}: got {gu[k]:#06x}, expected {ru[k]:#06x}")
+        if not np.all(got[~nz].astype(np.float32) == 0):
+            return f"a non-zero result for an exact zero sum in the batch from {ac[0]:#06x}"
+        return None
+
+    orc.lib()  # load once before the threads
+    with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        errors = [e for e in ex.map(batch, range(0, finite.size, per)) if e]
+    assert not errors, errors[:3]
+
+
 def test_bf16_accumulate_is_correctly_rounded_add(orc):
     g = np.random.default_rng(5)
     n = 1 << 18
