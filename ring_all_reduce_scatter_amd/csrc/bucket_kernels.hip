@@ -77,6 +77,8 @@ hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream) {
 //   per bucket b at hdr+4b:   padded length, chunk length L, first tensor, tensors
 //   per tensor t at ten+2t:   flat offset inside its bucket, element count
 //   pointers at ptr + r*nt+t: rank r's copy of tensor t
+// followed (256-byte aligned) by 16 bytes of descriptor per fold workgroup,
+// written on the device by bucket_desc_kernel.
 namespace rar {
 namespace {
 
