@@ -40,6 +40,34 @@ def test_bucketed_matches_oracle(dt, n, algo):
     assert sent == osent and recv == orecv
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [4, 16])
+def test_bucketed_in_rank_arena_matches_oracle(dt, n):
+    """The placement the benchmark uses (rank_tensors: every rank's tensors in
+    one region, regions a power of two apart, tensors 256-element aligned)
+    gives the oracle's bits too, for both schedules."""
+    sizes = inputs.bucket_sizes(30, lo_exp=2, hi_exp=15, salt=10 + n)
+    th = inputs.bucket_tensors(n, sizes, dtype=dt, salt=10 + n)
+    ref = [[t.copy() for t in th[r]] for r in range(n)]
+    cap = 48 << 10
+    osent, orecv = oracle.bucketed_allreduce(ref, cap, dt=DT_NAMES[dt])
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dt]
+    for algo in (rar.ALGO_FUSED, rar.ALGO_STEPWISE):
+        arena, dev = rar.rank_tensors(n, sizes, tdt, "cuda:0")
+        for r in range(n):
+            for x, h in zip(dev[r], to_dev(th[r], dt)):
+                x.copy_(h)
+        ws = torch.empty(rar.bucketed_workspace_bytes(sizes, n, DT_NAMES[dt], cap, algo), dtype=torch.uint8,
+                         device="cuda:0")
+        rar.bucketed_allreduce(dev, cap, ws, algo=algo)
+        sent, recv = rar.last_traffic(n)
+        for r in range(n):
+            got = to_host(dev[r], dt)
+            for t in range(len(sizes)):
+                assert_bits_equal(got[t], ref[r][t], f"algo {algo} rank {r} tensor {t}")
+        assert sent == osent and recv == orecv
+
+
 @pytest.mark.slow
 def test_buckets_workload_full_size_sampled():
     """N=16 bf16, 200 log-uniform tensors, 25 MiB buckets.  Every rank ends
