@@ -209,14 +209,15 @@ class pinned_core:
 
 
 def copy_peak(reps=10):
-    """Achievable HBM rate of a plain copy on this GPU: 1 GiB read and 1 GiB
-    written by the library's copy kernel (a 2-rank broadcast) and by torch's
-    device-to-device copy, median of `reps` launches each, timed with HIP
-    events on the launch stream; the faster of the two is the peak."""
+    """Achievable HBM rate of a plain copy on this GPU: 2 GiB read and 2 GiB
+    written (the fused folds' 4 GiB per launch) by the library's copy kernel
+    (a 2-rank broadcast) and by torch's device-to-device copy, median of
+    `reps` launches each, timed with HIP events on the launch stream; the
+    faster of the two is the peak."""
     import torch
 
     import ring_all_reduce_scatter_amd as rar
-    count = 256 << 20
+    count = 512 << 20
     bufs = [torch.full((count,), float(r + 1), device="cuda:0") for r in range(2)]
     stream = torch.cuda.current_stream()
 
