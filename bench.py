@@ -133,9 +133,15 @@ def make_sets(pristine, nsets):
     return sets
 
 
+class LegTimes(tuple):
+    """(wall ms per step, mean event ms, min event ms) with .median_ms."""
+    median_ms = None
+
+
 def time_leg(run, sets, warmup, steps):
     """Warm up on set 0, then time `steps` calls, each on a fresh set.
-    Returns wall ms per step and the HIP-event kernel ms (mean, min)."""
+    Returns wall ms per step and the HIP-event kernel ms (mean, min); the
+    median of the event times is the result's median_ms."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -152,7 +158,9 @@ def time_leg(run, sets, warmup, steps):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return (t1 - t0) * 1e3 / steps, sum(ev) / len(ev), min(ev)
+    out = LegTimes(((t1 - t0) * 1e3 / steps, sum(ev) / len(ev), min(ev)))
+    out.median_ms = sorted(ev)[len(ev) // 2]
+    return out
 
 
 def time_graph_leg(run, sets, steps):
@@ -261,7 +269,8 @@ def fp32_leg(args):
     del pristine
     S = count * 4
     log(f"[bench] fp32 leg: timing {args.steps} steps on {nsets - 1} sets")
-    ms, kern_ms, kern_min = time_leg(lambda bufs: rar.ring_allreduce(bufs), sets, args.warmup, args.steps)
+    tl = time_leg(lambda bufs: rar.ring_allreduce(bufs), sets, args.warmup, args.steps)
+    ms, kern_ms, kern_min = tl
     sent, recv = rar.last_traffic(n)  # logical bytes per rank of the last call
     first = [t.cpu().numpy() for t in sets[1]]
     del sets
@@ -271,6 +280,7 @@ def fp32_leg(args):
     sources = COUNTER_KERNELS["ring_fold_f32_n8"]["sources"]
     res = {
         "n": n, "count": count, "S": S, "ms": ms, "kern_ms": kern_ms, "kern_min_ms": kern_min,
+        "kern_median_ms": tl.median_ms,
         "bytes_per_rank": {"sent": sent, "recv": recv},
         "busbw": busbw(S, n, ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -785,6 +795,8 @@ def main():
         "busbw_aggregate_GBs": round(f["busbw"] * f["n"], 1),
         "pct_hbm_peak": round(100 * f["roofline"]["frac"], 2),
         "kernel_ms": round(f["kern_ms"], 4),
+        "kernel_ms_median": round(f["kern_median_ms"], 4),
+        "kernel_ms_min": round(f["kern_min_ms"], 4),
         "roofline": f["roofline"],
         "cpu_baseline": f["cpu_baseline"],
         "parity": f["parity_first_timed_output"],
