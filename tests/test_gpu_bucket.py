@@ -41,6 +41,24 @@ def test_bucketed_matches_oracle(dt, n, algo):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("algo", [rar.ALGO_FUSED, rar.ALGO_STEPWISE])
+def test_bucketed_with_empty_tensors_matches_oracle(dt, algo):
+    """Zero-length tensors between, before and after others (they share a
+    flat offset with their neighbour inside a bucket) change nothing."""
+    n = 4
+    sizes = [0, 5, 0, 300, 0, 0, 2049, 7, 0, 4096 * 3 + 1, 0, 16, 0]
+    th = inputs.bucket_tensors(n, sizes, dtype=dt, salt=5)
+    ref = [[t.copy() for t in th[r]] for r in range(n)]
+    cap = 4096
+    osent, orecv = oracle.bucketed_allreduce(ref, cap, dt=DT_NAMES[dt])
+    got, sent, recv = _run(th, dt, cap, algo)
+    for r in range(n):
+        for t in range(len(sizes)):
+            assert_bits_equal(got[r][t], ref[r][t], f"rank {r} tensor {t}")
+    assert sent == osent and recv == orecv
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("n", [4, 16])
 def test_bucketed_in_rank_arena_matches_oracle(dt, n):
     """The placement the benchmark uses (rank_tensors: every rank's tensors in
