@@ -76,6 +76,35 @@ COUNTER_KERNELS = {
 }
 
 
+# Multi-launch pipelines whose HBM bytes per call the counter passes measure:
+# every dispatch of the listed kernels in the counters run belongs to one of
+# `calls` calls of that pipeline.
+PIPELINE_COUNTERS = {
+    "bfp8_allreduce_staged": {
+        "matches": ["::bfp_encode_kernel<", "::bfp_decode_kernel<", "::bfp_decode_fanout_kernel<"], "calls": 3,
+        "workload": "staged BFP-8 allreduce, N=8 x 128M fp16, 4 MiB units",
+        "sources": [_CSRC + "bfp_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp", _CSRC + "api.hip"]},
+    "sparse_bfp4_allreduce_staged": {
+        "matches": ["::comp_count_kernel<", "::comp_write_kernel<", "::comp_decode_acc_kernel<",
+                    "::comp_decode_fanout_kernel<"], "calls": 3,
+        "workload": "staged sparse + BFP-4 allreduce, N=8 x 64M fp16, ranks 0-3 95% zeros",
+        "sources": [_CSRC + "sparse_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp", _CSRC + "api.hip"]},
+}
+
+
+def pipeline_traffic(key):
+    """HBM bytes per call of a multi-launch pipeline from profiles/counters.json,
+    or None when absent or taken on other sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
+            rec = json.load(f).get("pipelines", {}).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(PIPELINE_COUNTERS[key]["sources"]):
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
 def _bucket_elements():
     from ring_all_reduce_scatter_amd import inputs
     return sum(inputs.bucket_sizes(inputs.WORKLOADS["buckets"]["ntensors"]))
@@ -491,6 +520,10 @@ def extra_legs(args):
     Sb = wb["count"] * 2
     out["bfp8_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
                                     "frac_of_roofline": round(2 * wb["n"] * Sb / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    tr = pipeline_traffic("bfp8_allreduce_staged")
+    out["bfp8_allreduce_staged"]["traffic_per_call"] = tr
+    if tr:
+        out["bfp8_allreduce_staged"]["frac_of_roofline_own_bytes"] = round(tr / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     ms, k, _ = time_graph_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, steps)
     out["bfp8_allreduce_staged_graph_replay"] = {
         "ms": round(ms, 4), "busbw_GBs": round(busbw(Sb, wb["n"], ms), 1),
@@ -555,6 +588,11 @@ def extra_legs(args):
     out["sparse_bfp4_allreduce_staged"] = {"ms": round(ms, 4), "busbw_GBs": round(busbw(S5, w5["n"], ms), 1),
                                            "wire_bytes_rank0": sent[0],
                                            "frac_of_roofline": round(2 * w5["n"] * S5 / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    tr = pipeline_traffic("sparse_bfp4_allreduce_staged")
+    out["sparse_bfp4_allreduce_staged"]["traffic_per_call"] = tr
+    if tr:
+        out["sparse_bfp4_allreduce_staged"]["frac_of_roofline_own_bytes"] = round(
+            tr / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     ms, k, _ = time_graph_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, steps)
     out["sparse_bfp4_allreduce_staged_graph_replay"] = {
         "ms": round(ms, 4), "busbw_GBs": round(busbw(S5, w5["n"], ms), 1),
@@ -666,6 +704,34 @@ def counters_run(reps=3):
     for _ in range(reps):
         step()
     torch.cuda.synchronize()
+    del arena, dev, ws, step
+    log("[bench] counters run: folds, hash and buckets done")
+    # the staged BFP-8 pipeline (its bytes do not depend on the values)
+    wb = inputs.WORKLOADS["bfp8"]
+    big = torch.empty(wb["n"] * wb["count"], dtype=torch.float16, device="cuda:0").normal_(0.0, 1e-3)
+    bufs = [big[r * wb["count"]:(r + 1) * wb["count"]] for r in range(wb["n"])]
+    cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"], schedule=rar.SCHED_STAGED)
+    ws = torch.empty(rar.compressed_workspace_bytes(wb["n"], wb["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    for _ in range(PIPELINE_COUNTERS["bfp8_allreduce_staged"]["calls"]):
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+    torch.cuda.synchronize()
+    del big, bufs, ws
+    log("[bench] counters run: staged BFP-8 done")
+    # the staged sparse + BFP-4 pipeline on the workload's own zero pattern,
+    # restored before every call (torch copies, not counted)
+    w5 = inputs.WORKLOADS["sparse_bfp4"]
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in inputs.sparse_mix(w5["n"], w5["count"])]
+    bufs = [p.clone() for p in pristine]
+    cfg = rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=w5["mbits"], unit_bytes=w5["unit_bytes"],
+                           sparsity_threshold=w5["theta"], schedule=rar.SCHED_STAGED)
+    ws = torch.empty(rar.compressed_workspace_bytes(w5["n"], w5["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    for _ in range(PIPELINE_COUNTERS["sparse_bfp4_allreduce_staged"]["calls"]):
+        for b, p in zip(bufs, pristine):
+            b.copy_(p)
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+    torch.cuda.synchronize()
     log("[bench] counters run done")
 
 
@@ -729,6 +795,21 @@ def ingest_counters(fetch_csv, write_csv):
         alg = _algorithmic(k)
         rows.append(f"| `{k['match']}` ({k['workload']}) | {fk:.1f} | {wk:.1f} | {hbm:,} | {alg:,} | "
                     f"{hbm / alg:.4f} |")
+    pipes = {}
+    for key, pdef in PIPELINE_COUNTERS.items():
+        fk = sum(sum(_counter_values(fetch_csv, "FETCH_SIZE", m)) for m in pdef["matches"])
+        wk = sum(sum(_counter_values(write_csv, "WRITE_SIZE", m)) for m in pdef["matches"])
+        nd = sum(len(_counter_values(fetch_csv, "FETCH_SIZE", m)) for m in pdef["matches"])
+        if not nd:
+            continue
+        hbm = int(round((fk * cal_bytes_kib / cf + wk * cal_bytes_kib / cw) * 1024 / pdef["calls"]))
+        pipes[key] = {"workload": pdef["workload"], "kernels": pdef["matches"], "calls": pdef["calls"],
+                      "dispatches": nd, "fetch_kib_per_call": round(fk / pdef["calls"], 1),
+                      "write_kib_per_call": round(wk / pdef["calls"], 1), "hbm_bytes_per_call": hbm,
+                      "source_sha": source_sha(pdef["sources"]), "sources": pdef["sources"]}
+        rows.append(f"| {pdef['workload']} (all {nd} dispatches of {pdef['calls']} calls) | "
+                    f"{fk / pdef['calls']:.1f} | {wk / pdef['calls']:.1f} | {hbm:,} per call | - | - |")
+    out["pipelines"] = pipes
     with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
