@@ -13,16 +13,17 @@
 //
 // Encoding takes two launches over 2048-element tiles (256 lanes x 8):
 //   count  - non-zeros per tile;
-//   write  - every workgroup sums the unit's tile counts (the total and the
-//            ones before its tile) and takes the threshold decision itself,
-//            the same integers giving the same decision everywhere; the
-//            first tile's workgroup writes the header and the wire byte
-//            counters.  Sparse: each tile compacts its non-zeros to its
-//            offset (ballot-free: a block-wide exclusive scan of per-lane
-//            counts keeps the indices ascending); BFP: the tile's blocks.
-// Decoding works per destination tile: a binary search finds the tile's
-// slice of the ascending index array, so no two workgroups touch the same
-// element and no atomics are needed.
+//   write  - a workgroup takes four consecutive tiles, sums the unit's tile
+//            counts (the total and the ones before its first tile) and
+//            takes the threshold decision itself, the same integers giving
+//            the same decision everywhere; the first tile's workgroup writes
+//            the header and the wire byte counters.  Sparse: each tile
+//            compacts its non-zeros to its offset (ballot-free: a
+//            block-wide exclusive scan of per-lane counts keeps the indices
+//            ascending); BFP: the tiles' blocks.
+// Decoding works per destination tile: a 64-way wavefront search finds the
+// tile's slice of the ascending index array, so no two workgroups touch the
+// same element and no atomics are needed.
 #include "bfp_device.hpp"
 
 namespace rar {
