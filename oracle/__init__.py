@@ -88,7 +88,7 @@ def _load():
         "orc_sparse_decode": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int]),
         "orc_ring_allreduce_compressed": (ctypes.c_int, [
             _c_vp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_double, _c_size, _c_vp, _u64p, _u64p]),
+            ctypes.c_float, _c_size, _c_vp, _u64p, _u64p]),
         "orc_bucket_plan": (_c_size, [_c_vp, _c_size, ctypes.c_int, _c_size, _c_vp]),
         "orc_bucketed_allreduce": (ctypes.c_int, [_c_vp, _c_vp, _c_size, ctypes.c_int, ctypes.c_int,
                                                   _c_size, _u64p, _u64p]),
@@ -306,14 +306,18 @@ def sparse_decode(msg, out):
 
 def ring_allreduce_compressed(bufs, method=COMP_BFP, block=128, mbits=8, theta=0.5,
                               unit=2097152, dt=None, with_blockmax=False):
-    """In place; returns (sent, recv[, blockmax per block])."""
+    """In place; returns (sent, recv[, blockmax per block]).
+
+    theta is the sparsity threshold of SPARSE_AUTO.  It is rounded to binary32
+    (the type of a compression configuration's threshold field) and the
+    decision is zeros > theta * len, that product taken in binary64."""
     dt = _dt_of(bufs[0], dt)
     n = len(bufs)
     count = bufs[0].size
     sent, recv = _traffic(n)
     bm = np.zeros((count + block - 1) // block, dtype=np.float64) if with_blockmax else None
     _check(lib().orc_ring_allreduce_compressed(
-        _ptrs(bufs), n, count, dt, method, block, mbits, float(theta), unit,
+        _ptrs(bufs), n, count, dt, method, block, mbits, float(np.float32(theta)), unit,
         bm.ctypes.data if bm is not None else None, sent, recv), "ring_allreduce_compressed")
     if with_blockmax:
         return list(sent), list(recv), bm

@@ -501,7 +501,7 @@ int orc_sparse_decode(const uint8_t* msg, void* dst, int dt) {
 
 typedef struct {
   int method, block, mbits, dt;
-  double theta;
+  float theta; /* binary32, the type a configuration stores it in */
 } comp_t;
 
 /* Encode one unit; returns message size.  For SPARSE_AUTO every message
@@ -514,8 +514,11 @@ static size_t comp_encode(const comp_t* cf, const void* src, size_t len, uint8_t
     orc_bfp_encode(src, cf->dt, len, cf->block, cf->mbits, msg, blockmax);
     return orc_bfp_bytes(len, cf->block, cf->mbits);
   }
+  /* [P4] section 2.1: sparse when the zeros exceed the threshold share of
+   * the unit.  The product of the binary32 threshold and the length is taken
+   * in binary64, where it is exact for units below 2^29 elements. */
   size_t z = orc_count_zeros(src, cf->dt, len);
-  if ((double)z > cf->theta * (double)len) {
+  if ((double)z > (double)cf->theta * (double)len) {
     size_t bytes = orc_sparse_encode(src, cf->dt, len, msg);
     if (blockmax) {
       size_t nb = (len + (size_t)cf->block - 1) / (size_t)cf->block;
@@ -575,7 +578,7 @@ size_t orc_comp_chunk_len(size_t count, int n, int block) {
  * the largest block maximum among all messages that carried that block.
  * unit must be a positive multiple of block. */
 int orc_ring_allreduce_compressed(void* const* bufs, int n, size_t count, int dt, int method,
-                                  int block, int mbits, double theta, size_t unit,
+                                  int block, int mbits, float theta, size_t unit,
                                   double* blockmax_out, uint64_t* sent, uint64_t* recv) {
   if (!check_bufs(bufs, n, dt) || !bfp_args_ok(block, mbits)) return ORC_EINVAL;
   if (method != ORC_COMP_BFP && method != ORC_COMP_SPARSE_AUTO) return ORC_EINVAL;

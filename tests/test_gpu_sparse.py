@@ -65,6 +65,42 @@ def test_threshold_values_match_oracle(theta):
     assert sent == osent
 
 
+def _same_zero_ranks(n, unit, zeros, units, seed=70):
+    """Every unit has the same `zeros` positions at +0 on every rank and
+    positive values elsewhere, so every partial sum keeps exactly them."""
+    g = np.random.default_rng(seed)
+    mask = np.ones(units * unit, dtype=bool)
+    for u in range(units):
+        mask[u * unit + g.choice(unit, size=zeros, replace=False)] = False
+    return [np.where(mask, g.uniform(0.25, 1.0, size=units * unit).astype(np.float16), np.float16(0)).astype(np.float16)
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("n", [2, 4])
+@pytest.mark.parametrize("unit,zeros,block", [(640, 448, 128), (80, 56, 16)])
+def test_threshold_binary32_boundary_matches_oracle(n, unit, zeros, block):
+    """theta = 0.7 with exactly 0.7 * len zeros per unit: the binary32
+    threshold (0.699999988...) sends every message sparse.  Library and
+    oracle must take the same decision: results bit-exact, byte counters
+    equal, and every message sparse (lossless: the plain ring's sums)."""
+    L = 640
+    xs = _same_zero_ranks(n, unit, zeros, n * L // unit, seed=70 + n)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, block=block, mbits=4,
+                                                    unit=unit, theta=0.7)
+    got, sent, recv = _run_auto(xs, "f16", unit_elems=unit, theta=0.7, block=block)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+    assert sent == osent and recv == orecv
+    nnz = unit - zeros
+    sparse_msg = 16 + -(-nnz * 2 // 16) * 16 + 4 * nnz
+    assert sent == [2 * (n - 1) * (L // unit) * sparse_msg] * n
+    plain = [x.copy() for x in xs]
+    oracle.ring_allreduce(plain)
+    for r in range(n):
+        assert np.array_equal(got[r], plain[r])
+
+
 def test_exactly_half_zeros_goes_bfp():
     unit = 256
     x0 = np.zeros(2 * unit, dtype=np.float16)

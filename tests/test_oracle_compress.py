@@ -336,6 +336,54 @@ def test_sparse_threshold_is_strict(orc):
     assert np.array_equal(x0, x1)
 
 
+def _zero_pattern_ranks(n, unit, zeros, units):
+    """n fp16 ranks of units*unit elements; in every unit the same `zeros`
+    positions are +0 on every rank and the rest positive, so every partial
+    sum the ring forms has exactly those zeros (no cancellation)."""
+    g = np.random.default_rng(70)
+    mask = np.ones(units * unit, dtype=bool)
+    for u in range(units):
+        mask[u * unit + g.choice(unit, size=zeros, replace=False)] = False
+    out = []
+    for r in range(n):
+        x = g.uniform(0.25, 1.0, size=units * unit).astype(np.float16)
+        out.append(np.where(mask, x, np.float16(0)).astype(np.float16))
+    return out
+
+
+@pytest.mark.parametrize("unit,zeros,block", [(640, 448, 128), (80, 56, 16)])
+def test_sparse_threshold_is_binary32(orc, unit, zeros, block):
+    """The threshold is the configuration's binary32 value.  0.7 is not
+    representable: float32(0.7) = 0.699999988..., so zeros = 0.7 * len
+    exactly (448 of 640, 56 of 80) exceeds float32(0.7) * len and the unit
+    goes sparse, where the binary64 0.7 would keep it BFP.  Every message
+    of this ring has the same zeros, so the byte counters name the format:
+    sparse = 16 + round16(nnz * 2) + 4 * nnz bytes, BFP = 16 + E bytes
+    padded to 16 + 4-bit mantissas."""
+    assert np.float64(np.float32(0.7)) * unit < zeros == 0.7 * unit
+    n, L = 2, 640  # chunk length: a multiple of 128 and of the unit
+    assert orc.comp_chunk_len(n * L, n, block) == L
+    units = L // unit
+    xs = _zero_pattern_ranks(n, unit, zeros, n * units)
+    nnz = unit - zeros
+    sparse = 16 + -(-nnz * 2 // 16) * 16 + 4 * nnz
+    bfp = 16 + -(-(unit // block) // 16) * 16 + unit // 2
+    assert orc.sparse_bytes(nnz, orc.F16) == sparse and orc.bfp_bytes(unit, block, 4) + 16 == bfp
+    per_rank = 2 * (n - 1) * units  # messages each rank sends: RS hops and AG relays
+    for theta, want in ((0.7, sparse), (0.75, bfp), (np.nextafter(np.float32(0.7), np.float32(1)), bfp)):
+        bufs = [x.copy() for x in xs]
+        sent, recv = orc.ring_allreduce_compressed(bufs, method=orc.COMP_SPARSE_AUTO, block=block, mbits=4,
+                                                   theta=theta, unit=unit)
+        assert sent == [per_rank * want] * n and recv == sent, (theta, sent)
+    # lossless when every message is sparse: the plain ring's sums
+    bufs = [x.copy() for x in xs]
+    orc.ring_allreduce_compressed(bufs, method=orc.COMP_SPARSE_AUTO, block=block, mbits=4, theta=0.7, unit=unit)
+    plain = [x.copy() for x in xs]
+    orc.ring_allreduce(plain)
+    for a, b in zip(bufs, plain):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
 def test_sparse_mix_workload_shape(orc):
     n, count = 8, 8 * 2048
     xs = inputs.sparse_mix(n, count, salt=4)
