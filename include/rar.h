@@ -72,7 +72,9 @@ typedef enum rar_status {
   RAR_EWORKSPACE = 4, /* workspace missing or smaller than required */
   RAR_EHIP = 5,       /* the HIP runtime reported an error (launch, event, stream) */
   RAR_ENOTSUP = 6,    /* valid request that this library does not implement */
-  RAR_EOVERLAP = 7,   /* two rank buffers overlap, or a buffer is NULL */
+  RAR_EOVERLAP = 7,   /* two rank buffers overlap, a workspace overlaps a rank
+                         buffer, two tensors of the bucketed call overlap, or a
+                         buffer is NULL */
   RAR_EABORT = 8      /* fault-tolerant ring: every member failed */
 } rar_status;
 

@@ -13,5 +13,5 @@ from ._binding import (  # noqa: F401
     last_traffic, lib, reduce_scatter, reduce_scatter_ex, ring_allreduce, ring_allreduce_compressed,
     ring_allreduce_ex, rs_step, status_string, version, FEEDBACK_DELTA, FEEDBACK_ERROR,
     ring_allreduce_compressed_state, EABORT, HASH_WORKSPACE_BYTES, Fault, FtReport, ft_workspace_bytes,
-    rank_hashes, ring_allreduce_ft, shared_state_sync, BucketedAllreduce, rank_tensors,
+    rank_hashes, ring_allreduce_ft, shared_state_sync, BucketedAllreduce, rank_tensors, TRAFFIC_BYTES,
 )

@@ -167,6 +167,21 @@ def _dptr(t) -> int:
     return t.data_ptr()
 
 
+def _flat(t, what: str):
+    """A tensor whose storage the kernels may read as `numel` contiguous
+    elements: strided or expanded views are refused (the kernels would walk
+    past the view into other memory)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _need_bytes(t, nbytes: int, what: str):
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes, {nbytes} are needed")
+
+
 def _rank_ptrs(bufs: Sequence):
     if len(bufs) < 1:
         raise ValueError("need at least one rank buffer")
@@ -263,19 +278,38 @@ def bfp_bytes(count: int, block: int = 128, mbits: int = 8) -> int:
     return lib().rar_bfp_bytes(count, block, mbits)
 
 
+def _bfp_msg_check(msg, count: int, block: int, mbits: int, dst, what: str):
+    """count elements fit dst, and msg holds a whole message for them."""
+    _flat(msg, f"{what}: message")
+    _flat(dst, f"{what}: destination")
+    if count < 0 or count > dst.numel():
+        raise ValueError(f"{what}: count {count} is outside the destination's {dst.numel()} elements")
+    need = bfp_bytes(count, block, mbits)
+    if need:  # 0 = invalid block or mbits: the library reports it
+        _need_bytes(msg, need, f"{what}: message")
+
+
 def bfp_compress(src, block: int, mbits: int, dst, stream=None):
+    """Encode all of src into dst, which must hold bfp_bytes(src.numel()) bytes."""
+    _flat(src, "bfp_compress: source")
+    _flat(dst, "bfp_compress: message")
+    need = bfp_bytes(src.numel(), block, mbits)
+    if need:
+        _need_bytes(dst, need, "bfp_compress: message")
     rc = lib().rar_bfp_compress(_dptr(src), dtype_code(src), src.numel(), block, mbits, _dptr(dst),
                                 _stream(stream, src))
     _check(rc, "rar_bfp_compress")
 
 
 def bfp_decompress_accumulate(msg, count: int, block: int, mbits: int, acc, stream=None):
+    _bfp_msg_check(msg, count, block, mbits, acc, "bfp_decompress_accumulate")
     rc = lib().rar_bfp_decompress_accumulate(_dptr(msg), count, block, mbits, _dptr(acc),
                                              dtype_code(acc), _stream(stream, acc))
     _check(rc, "rar_bfp_decompress_accumulate")
 
 
 def bfp_decompress(msg, count: int, block: int, mbits: int, dst, stream=None):
+    _bfp_msg_check(msg, count, block, mbits, dst, "bfp_decompress")
     rc = lib().rar_bfp_decompress(_dptr(msg), count, block, mbits, _dptr(dst), dtype_code(dst),
                                   _stream(stream, dst))
     _check(rc, "rar_bfp_decompress")
@@ -311,6 +345,8 @@ def compressed_workspace_bytes(nranks: int, count: int, dtype: int, cfg: Compres
 
 
 def ring_allreduce_compressed(bufs, cfg: CompressCfg, workspace, stream=None):
+    if workspace is not None:
+        _flat(workspace, "workspace")
     rc = lib().rar_ring_allreduce_compressed(
         _rank_ptrs(bufs), len(bufs), bufs[0].numel(), dtype_code(bufs[0]), ctypes.byref(cfg),
         _dptr(workspace) if workspace is not None else None,
@@ -327,6 +363,8 @@ def ring_allreduce_compressed_state(bufs, state, feedback: int, cfg: CompressCfg
     for s_ in state:
         if s_.numel() != bufs[0].numel() or s_.element_size() != 4 or not s_.is_contiguous():
             raise ValueError("state tensors must be contiguous float32 of the rank buffers' length")
+    if workspace is not None:
+        _flat(workspace, "workspace")
     rc = lib().rar_ring_allreduce_compressed_state(
         _rank_ptrs(bufs), (ctypes.c_void_p * len(state))(*[_dptr(t) for t in state]), len(bufs),
         bufs[0].numel(), dtype_code(bufs[0]), feedback, ctypes.byref(cfg),
@@ -336,7 +374,12 @@ def ring_allreduce_compressed_state(bufs, state, feedback: int, cfg: CompressCfg
     _check(rc, "rar_ring_allreduce_compressed_state")
 
 
+TRAFFIC_BYTES = 2 * MAX_RANKS * 8  # the byte counters at the start of a compressed call's workspace
+
+
 def compressed_traffic(workspace, nranks: int, stream=None):
+    _flat(workspace, "workspace")
+    _need_bytes(workspace, TRAFFIC_BYTES, "compressed_traffic: workspace")
     sent = (ctypes.c_uint64 * nranks)()
     recv = (ctypes.c_uint64 * nranks)()
     _check(lib().rar_compressed_traffic(_dptr(workspace), nranks, sent, recv, _stream(stream, workspace)),
@@ -351,12 +394,19 @@ def _nbytes(t):
 
 
 def _ws(workspace):
-    return (_dptr(workspace), _nbytes(workspace)) if workspace is not None else (None, 0)
+    if workspace is None:
+        return (None, 0)
+    _flat(workspace, "workspace")
+    return (_dptr(workspace), _nbytes(workspace))
 
 
 def rank_hashes(bufs, workspace, nbytes=None, stream=None):
     """64-bit hash of each rank buffer's first nbytes bytes (default: all)."""
-    nb = _nbytes(bufs[0]) if nbytes is None else nbytes
+    nb = _nbytes(bufs[0]) if nbytes is None else int(nbytes)
+    for b in bufs:
+        _flat(b, "rank_hashes: buffer")
+        if nb < 0 or nb > _nbytes(b):
+            raise ValueError(f"rank_hashes: nbytes {nb} is outside a buffer of {_nbytes(b)} bytes")
     out = (ctypes.c_uint64 * len(bufs))()
     ptrs = (ctypes.c_void_p * len(bufs))(*[_dptr(b) for b in bufs])
     _check(lib().rar_rank_hashes(ptrs, len(bufs), nb, *_ws(workspace), out, _stream(stream, bufs[0])),

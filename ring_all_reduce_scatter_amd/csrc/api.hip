@@ -106,6 +106,28 @@ int check_state_bufs(void* const* bufs, void* const* state, int n, size_t bytes,
   return RAR_OK;
 }
 
+// No two of the byte ranges [p, p + len) overlap; empty ranges are ignored.
+int check_disjoint(std::vector<std::pair<uintptr_t, size_t>>& a) {
+  a.erase(std::remove_if(a.begin(), a.end(), [](const std::pair<uintptr_t, size_t>& x) { return x.second == 0; }),
+          a.end());
+  std::sort(a.begin(), a.end());
+  for (size_t i = 0; i + 1 < a.size(); ++i)
+    if (a[i + 1].first - a[i].first < a[i].second) return RAR_EOVERLAP;
+  return RAR_OK;
+}
+
+// The workspace's used bytes clear of every rank buffer (and state buffer).
+int check_ws_clear(void* const* bufs, void* const* state, int n, size_t bytes, size_t sbytes, const void* ws,
+                   size_t ws_used) {
+  std::vector<std::pair<uintptr_t, size_t>> a;
+  for (int r = 0; r < n; ++r) {
+    a.emplace_back((uintptr_t)bufs[r], bytes);
+    if (state) a.emplace_back((uintptr_t)state[r], sbytes);
+  }
+  a.emplace_back((uintptr_t)ws, ws_used);
+  return check_disjoint(a);
+}
+
 RankPtrs make_ptrs(void* const* bufs, int n) {
   RankPtrs p{};
   for (int r = 0; r < n; ++r) p.p[r] = (char*)bufs[r];
@@ -814,6 +836,7 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
   plan_sizes(&pl, nranks, count, dtype);
   if (!workspace || ws_bytes < workspace_need(pl)) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  if ((rc = check_ws_clear(bufs, nullptr, nranks, count * es, 0, workspace, workspace_need(pl)))) return rc;
   hipStream_t st = (hipStream_t)stream;
   Traffic tr;
   tr.reset(nranks);
@@ -856,6 +879,8 @@ int rar_ring_allreduce_compressed_state(void* const* bufs, void* const* state, i
   plan_sizes(&pl, nranks, count, dtype);
   if (!workspace || ws_bytes < workspace_need(pl)) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  if ((rc = check_ws_clear(bufs, state, nranks, count * es, count * sizeof(float), workspace, workspace_need(pl))))
+    return rc;
   hipStream_t st = (hipStream_t)stream;
   Traffic tr;
   tr.reset(nranks);
@@ -953,6 +978,9 @@ int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype
       return RAR_EINVAL;
   if (!workspace || ws_bytes < rar_ft_workspace_bytes(nranks, count, dtype)) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  if ((rc = check_ws_clear(bufs, nullptr, nranks, count * es, 0, workspace,
+                           rar_ft_workspace_bytes(nranks, count, dtype))))
+    return rc;
   hipStream_t st = (hipStream_t)stream;
   const size_t bytes = count * es, slot = round_up(bytes, kAlign);
   char* snap = (char*)workspace + RAR_HASH_WORKSPACE_BYTES;
@@ -1215,6 +1243,15 @@ int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t
   const size_t need = rar_bucketed_workspace_bytes_ex(counts, ntensors, nranks, dtype, cap_bytes, algo);
   if (!workspace || ws_bytes < need) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
+  {  // every tensor of every rank and the workspace: pairwise disjoint
+    std::vector<std::pair<uintptr_t, size_t>> a;
+    a.reserve((size_t)nranks * ntensors + 1);
+    for (int r = 0; r < nranks; ++r)
+      for (size_t t = 0; t < ntensors; ++t) a.emplace_back((uintptr_t)tensors[(size_t)r * ntensors + t], counts[t] * es);
+    a.emplace_back((uintptr_t)workspace, need);
+    const int rc = check_disjoint(a);
+    if (rc) return rc;
+  }
   hipStream_t st = (hipStream_t)stream;
   if (algo == RAR_ALGO_STEPWISE) return bucketed_packed(tensors, counts, ntensors, nranks, dtype, cap_bytes, workspace, st);
   std::vector<uint64_t> tab;

@@ -394,7 +394,8 @@ hipError_t pair_dispatch(const RankPtrs& bufs, const PairJobs& pairs, uint64_t c
 // allreduce, 2 GiB per launch).  fp32/fp16: N = 2 -> 3 (6.28 TB/s against
 // 5.84 uncapped), N = 4 -> 1 (5.77 against 4.94 at 2), N = 8 and 16 -> 1;
 // bf16 needs more waves to hide its rounding ALU: N = 2 -> 4, N = 4 -> 2
-// (6.35), N = 8 and 16 -> 2.  Rank counts without a specialised kernel
+// (6.35), N = 8 -> 3 (8 x 128M: 728 us against 766 at 2), N = 16 -> 2.
+// Rank counts without a specialised kernel
 // (runtime loop, loads not hoisted) -> 2 (N = 5: 5.11 against 4.57 at 1).
 int fold_wgs_per_cu(int dt, int n) {
   const bool b16 = dt == DT_BF16;

@@ -299,3 +299,53 @@ def test_compress_cfg_rejects_unknown_fields():
     assert (cfg.block, cfg.mbits) == (32, 4)
     with pytest.raises(TypeError, match="unknown field 'mbit'"):
         rar.compress_cfg(mbit=4)
+
+
+def test_workspace_overlapping_a_rank_buffer_is_refused():
+    """A workspace that shares bytes with a rank (or state) buffer would be
+    written while the kernels read those buffers: RAR_EOVERLAP before any
+    launch, for every call that takes a workspace next to rank buffers."""
+    base = 1 << 40
+    lib = rar.lib()
+    count = 4096  # 8 KiB of fp16 per rank
+    bufs = (ctypes.c_void_p * 2)(base, base + (1 << 20))
+    for sched in (rar.SCHED_FUSED, rar.SCHED_STAGED, rar.SCHED_FORWARD):
+        cfg = rar.compress_cfg(schedule=sched, unit_bytes=4096)
+        need = rar.compressed_workspace_bytes(2, count, rar.F16, cfg)
+        call = lambda ws: lib.rar_ring_allreduce_compressed(bufs, 2, count, rar.F16, ctypes.byref(cfg), ws, need,
+                                                            None)
+        assert call(base + (1 << 20) + 4096) == 7, sched       # inside rank 1
+        assert call(base + (1 << 20) - need + 16) == 7, sched  # its tail runs into rank 1
+    state = (ctypes.c_void_p * 2)(base + (2 << 20), base + (3 << 20))
+    cfg = rar.compress_cfg()
+    need = rar.compressed_workspace_bytes(2, count, rar.F16, cfg)
+    assert lib.rar_ring_allreduce_compressed_state(bufs, state, 2, count, rar.F16, rar.FEEDBACK_ERROR,
+                                                   ctypes.byref(cfg), base + (3 << 20) + 1024, need, None) == 7
+    ftws = rar.ft_workspace_bytes(2, count, rar.F16)
+    rep = rar.FtReport()
+    faults = (rar.Fault * 1)(rar.Fault(1, 1))
+    assert lib.rar_ring_allreduce_ft(bufs, 2, count, rar.F16, faults, 0, 0, base + 8192 - 512, ftws,
+                                     ctypes.byref(rep), None) == 7
+
+
+def test_bucketed_refuses_overlapping_tensors_and_workspace():
+    base = 1 << 40
+    lib = rar.lib()
+    counts = [1000, 3000]
+    n = 2
+    csz = (ctypes.c_size_t * 2)(*counts)
+    need = rar.bucketed_workspace_bytes(counts, n, rar.BF16, 25 << 20)
+    region = 1 << 20
+
+    def call(tens, ws):
+        arr = (ctypes.c_void_p * len(tens))(*tens)
+        return lib.rar_bucketed_allreduce_ex(arr, csz, 2, n, rar.BF16, 25 << 20, rar.ALGO_FUSED, ws, need, None)
+
+    ok = [base, base + 2048, base + region, base + region + 2048]
+    ws = base + 4 * region
+    # tensor 1 of rank 0 starts inside its tensor 0 (1000 bf16 = 2000 bytes)
+    assert call([base, base + 1024, base + region, base + region + 2048], ws) == 7
+    # rank 1's tensor 0 inside rank 0's tensor 1
+    assert call([base, base + 2048, base + 4096, base + region + 2048], ws) == 7
+    assert call(ok, base + region + 2048 + 16) == 7  # workspace inside rank 1's tensor 1
+    assert call(ok, 0) == 4
