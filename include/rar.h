@@ -258,6 +258,29 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
                                   const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
                                   void* stream);
 
+/* Size of the library's own scratch array for the allocation-free variant
+ * below: 32 MiB of device memory per GPU the library runs on, held from the
+ * first such call on that GPU until the process ends. */
+#define RAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* rar_ring_allreduce_compressed for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and results,
+ * bit for bit, as rar_ring_allreduce_compressed without the workspace: the
+ * message slots and byte counters live in a file-scope device array of
+ * RAR_NOALLOC_SCRATCH_BYTES in the library (its address is looked up once
+ * per device on the first call there).  The call allocates nothing.
+ * Returns RAR_EWORKSPACE when rar_compressed_workspace_bytes for these
+ * arguments exceeds RAR_NOALLOC_SCRATCH_BYTES (the fused schedule needs
+ * 1 KiB at any size; the staged and forwarding schedules hold one or two
+ * messages per (rank, unit)).  Every call on a GPU shares that GPU's array
+ * and leaves its contents behind, so calls that overlap in time on one GPU
+ * (concurrent streams, or threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The byte counters it writes are not
+ * readable by the caller. */
+int rar_ring_allreduce_compressed_noalloc(void* const* bufs, int nranks, size_t count, int dtype,
+                                          const rar_compress_cfg* cfg, void* stream);
+
 /* Stateful compression for the fused BFP ring ([P4] section 2.1, the
  * differential encoding layer; section 5, error feedback as the remedy for
  * the accuracy loss of lossy compression). */

@@ -14,4 +14,5 @@ from ._binding import (  # noqa: F401
     ring_allreduce_ex, rs_step, status_string, version, FEEDBACK_DELTA, FEEDBACK_ERROR,
     ring_allreduce_compressed_state, EABORT, HASH_WORKSPACE_BYTES, Fault, FtReport, ft_workspace_bytes,
     rank_hashes, ring_allreduce_ft, shared_state_sync, BucketedAllreduce, rank_tensors, TRAFFIC_BYTES,
+    ring_allreduce_compressed_noalloc, NOALLOC_SCRATCH_BYTES,
 )

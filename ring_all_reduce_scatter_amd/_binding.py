@@ -89,6 +89,8 @@ _SIGS = {
     "rar_compressed_workspace_bytes": (_c_size, [_c_int, _c_size, _c_int, ctypes.POINTER(CompressCfg)]),
     "rar_ring_allreduce_compressed": (_c_int, [_c_vp, _c_int, _c_size, _c_int, ctypes.POINTER(CompressCfg),
                                                _c_vp, _c_size, _c_vp]),
+    "rar_ring_allreduce_compressed_noalloc": (_c_int, [_c_vp, _c_int, _c_size, _c_int,
+                                                       ctypes.POINTER(CompressCfg), _c_vp]),
     "rar_ring_allreduce_compressed_state": (_c_int, [_c_vp, _c_vp, _c_int, _c_size, _c_int, _c_int,
                                                      ctypes.POINTER(CompressCfg), _c_vp, _c_size, _c_vp]),
     "rar_compressed_traffic": (_c_int, [_c_vp, _c_int, _u64p, _u64p, _c_vp]),
@@ -353,6 +355,17 @@ def ring_allreduce_compressed(bufs, cfg: CompressCfg, workspace, stream=None):
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream, bufs[0]))
     _check(rc, "rar_ring_allreduce_compressed")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ring_allreduce_compressed_noalloc(bufs, cfg: CompressCfg, stream=None):
+    """ring_allreduce_compressed without a workspace: the library's own
+    scratch array holds the messages (RAR_EWORKSPACE beyond its size)."""
+    rc = lib().rar_ring_allreduce_compressed_noalloc(_rank_ptrs(bufs), len(bufs), bufs[0].numel(),
+                                                     dtype_code(bufs[0]), ctypes.byref(cfg), _stream(stream, bufs[0]))
+    _check(rc, "rar_ring_allreduce_compressed_noalloc")
 
 
 def ring_allreduce_compressed_state(bufs, state, feedback: int, cfg: CompressCfg, workspace, stream=None):

@@ -824,20 +824,88 @@ size_t rar_compressed_workspace_bytes(int nranks, size_t count, int dtype, const
   return workspace_need(pl);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks and plan of a compressed allreduce, up to (not including) the
+// workspace.  The caller then checks the workspace it will use.
+int compressed_plan(void* const* bufs, int nranks, size_t count, int dtype, const rar_compress_cfg* cfg,
+                    CompPlan* pl) {
+  int rc = check_bufs(bufs, nranks, dtype, count * es_of(dtype));
+  if (rc) return rc;
+  if ((rc = cfg_check(cfg, dtype, pl))) return rc;
+  if (!(cfg->collective_mask & RAR_OP_ALLREDUCE)) pl->method = RAR_COMP_NONE;
+  plan_sizes(pl, nranks, count, dtype);
+  return RAR_OK;
+}
+
+int compressed_run(const CompPlan& pl, void* const* bufs, void* workspace, hipStream_t st);
+
+// File-scope scratch of the allocation-free compressed allreduce.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device with hipGetSymbolAddress and only
+// that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[RAR_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RAR_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RAR_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rar_ring_allreduce_compressed_noalloc(void* const* bufs, int nranks, size_t count, int dtype,
+                                          const rar_compress_cfg* cfg, void* stream) {
+  CompPlan pl{};
+  int rc = compressed_plan(bufs, nranks, count, dtype, cfg, &pl);
+  if (rc) return rc;
+  if (workspace_need(pl) > (size_t)RAR_NOALLOC_SCRATCH_BYTES) return RAR_EWORKSPACE;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  // the stream and events of the staged schedules are made here, not mid-call
+  if (pl.method != RAR_COMP_NONE && pl.sched == RAR_SCHED_STAGED) {
+    DevCtx* ctx = nullptr;
+    std::lock_guard<std::mutex> lock(g_ctx_mu);
+    if ((rc = get_ctx(&ctx))) return rc;
+  }
+  return compressed_run(pl, bufs, ws, (hipStream_t)stream);
+}
+
 int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, int dtype,
                                   const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
                                   void* stream) {
-  const size_t es = es_of(dtype);
-  int rc = check_bufs(bufs, nranks, dtype, count * es);
-  if (rc) return rc;
   CompPlan pl{};
-  if ((rc = cfg_check(cfg, dtype, &pl))) return rc;
-  if (!(cfg->collective_mask & RAR_OP_ALLREDUCE)) pl.method = RAR_COMP_NONE;
-  plan_sizes(&pl, nranks, count, dtype);
+  int rc = compressed_plan(bufs, nranks, count, dtype, cfg, &pl);
+  if (rc) return rc;
   if (!workspace || ws_bytes < workspace_need(pl)) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
-  if ((rc = check_ws_clear(bufs, nullptr, nranks, count * es, 0, workspace, workspace_need(pl)))) return rc;
-  hipStream_t st = (hipStream_t)stream;
+  if ((rc = check_ws_clear(bufs, nullptr, nranks, count * es_of(dtype), 0, workspace, workspace_need(pl))))
+    return rc;
+  return compressed_run(pl, bufs, workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int compressed_run(const CompPlan& pl, void* const* bufs, void* workspace, hipStream_t st) {
+  const int nranks = pl.n, dtype = pl.dt;
+  const size_t count = pl.count;
+  int rc;
   Traffic tr;
   tr.reset(nranks);
   if (pl.method == RAR_COMP_NONE) {
@@ -863,6 +931,10 @@ int rar_ring_allreduce_compressed(void* const* bufs, int nranks, size_t count, i
   }
   return write_traffic(tr, workspace, st);
 }
+
+}  // namespace
+
+extern "C" {
 
 int rar_ring_allreduce_compressed_state(void* const* bufs, void* const* state, int nranks, size_t count, int dtype,
                                         int feedback, const rar_compress_cfg* cfg, void* workspace, size_t ws_bytes,
