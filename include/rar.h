@@ -217,10 +217,23 @@ typedef enum rar_sched {
   RAR_SCHED_FUSED = 0,   /* one launch, per-block hop chain in registers (BFP only) */
   RAR_SCHED_STAGED = 1,  /* messages materialised per pipeline unit; encode and
                             decode on two streams ordered by events */
-  RAR_SCHED_FORWARD = 2  /* messages materialised per unit (BFP only); hop by
+  RAR_SCHED_FORWARD = 2, /* messages materialised per unit (BFP only); hop by
                             hop, every receiver decodes, adds its own copy and
                             encodes its next message in one kernel, without
                             writing the partial sum back; one launch per hop */
+  RAR_SCHED_PIPELINED = 3 /* messages materialised per (hop, chunk, unit), all
+                            kept in the workspace (BFP only); one launch in
+                            which each tile of a unit runs through the hops
+                            in ring order: the sender stores its message, the
+                            receiver loads it back, decodes, adds its own
+                            copy and encodes the next; tiles at different
+                            hops overlap.  Message h (1..N) of chunk c is
+                            sent by rank (c+h) mod N; message N is the
+                            owner's allgather message.  Slot of (h, c, u):
+                            workspace + 1024 rounded up to 256 +
+                            (((h-1)*N + c)*units_per_chunk + u) * slot, with
+                            slot = rar_bfp_bytes(unit elements) rounded up
+                            to 256 */
 } rar_sched;
 
 typedef struct rar_compress_cfg {

@@ -18,7 +18,7 @@ F32, F16, BF16 = 0, 1, 2
 ALGO_FUSED, ALGO_STEPWISE = 0, 1
 COMP_NONE, COMP_BFP, COMP_SPARSE_AUTO = 0, 1, 2
 OP_ALLREDUCE, OP_ALLGATHER, OP_BROADCAST = 1, 2, 4
-SCHED_FUSED, SCHED_STAGED, SCHED_FORWARD = 0, 1, 2
+SCHED_FUSED, SCHED_STAGED, SCHED_FORWARD, SCHED_PIPELINED = 0, 1, 2, 3
 FEEDBACK_ERROR, FEEDBACK_DELTA = 1, 2
 MAX_RANKS = 64
 HASH_WORKSPACE_BYTES = 512

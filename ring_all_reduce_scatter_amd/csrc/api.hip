@@ -237,7 +237,8 @@ int cfg_check(const rar_compress_cfg* cfg, int dt, CompPlan* pl) {
   if (cfg->method < RAR_COMP_NONE || cfg->method > RAR_COMP_SPARSE_AUTO) return RAR_EINVAL;
   if (cfg->mbits < 2 || cfg->mbits > 8) return RAR_EINVAL;
   if (cfg->block < 16 || cfg->block > 512 || (cfg->block & (cfg->block - 1))) return RAR_EINVAL;
-  if (cfg->schedule != RAR_SCHED_FUSED && cfg->schedule != RAR_SCHED_STAGED && cfg->schedule != RAR_SCHED_FORWARD)
+  if (cfg->schedule != RAR_SCHED_FUSED && cfg->schedule != RAR_SCHED_STAGED && cfg->schedule != RAR_SCHED_FORWARD &&
+      cfg->schedule != RAR_SCHED_PIPELINED)
     return RAR_EINVAL;
   const size_t es = es_of(dt);
   if (cfg->unit_bytes == 0 || cfg->unit_bytes % es) return RAR_EINVAL;
@@ -275,6 +276,7 @@ size_t tiles_per_slot(const CompPlan& pl) { return 2 * (size_t)comp_tiles_per_un
 size_t workspace_need(const CompPlan& pl) {
   if (pl.method == RAR_COMP_NONE || pl.sched == RAR_SCHED_FUSED) return kTrafficBytes;
   if (pl.sched == RAR_SCHED_FORWARD) return slots_offset() + 2 * (size_t)pl.n * pl.upc * pl.slot;
+  if (pl.sched == RAR_SCHED_PIPELINED) return slots_offset() + (size_t)pl.n * pl.n * pl.upc * pl.slot;
   size_t need = tiles_offset(pl);
   if (pl.method == RAR_COMP_SPARSE_AUTO) need += (size_t)pl.n * pl.upc * tiles_per_slot(pl) * sizeof(uint32_t);
   return need;
@@ -925,6 +927,11 @@ int compressed_run(const CompPlan& pl, void* const* bufs, void* workspace, hipSt
     } else if (pl.sched == RAR_SCHED_FORWARD) {
       fused_bfp_traffic(pl, tr);
       if ((rc = forward_bfp(pl, bufs, (char*)workspace, st))) return rc;
+    } else if (pl.sched == RAR_SCHED_PIPELINED) {
+      fused_bfp_traffic(pl, tr);
+      if ((rc = hip_rc(launch_bfp_pipe(make_ptrs(bufs, nranks), nranks, count, pl.L, pl.U, pl.upc, pl.slot,
+                                       (uint8_t*)workspace + slots_offset(), dtype, pl.block, pl.mbits, st))))
+        return rc;
     } else {
       if ((rc = staged_bfp(pl, bufs, (char*)workspace, tr, st))) return rc;
     }

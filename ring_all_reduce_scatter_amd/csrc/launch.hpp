@@ -97,6 +97,13 @@ hipError_t launch_bfp_decode_fanout(const BfpJobs& jobs, const RankPtrs& fan, in
                                     uint64_t elem_off[kMaxRanks], int dt, int block, int mbits,
                                     hipStream_t stream);
 
+// Pipelined compressed ring, one launch: every message (hop h = 1..N of
+// chunk c, unit u) is stored to slots + (((h-1)*n + c)*upc + u)*slot and
+// loaded back by its receiver; hop N is the owner's allgather message, whose
+// decode goes to every rank.  A workgroup carries one tile through the hops.
+hipError_t launch_bfp_pipe(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, uint64_t U, uint64_t upc,
+                           uint64_t slot, uint8_t* slots, int dt, int block, int mbits, hipStream_t stream);
+
 // Fused compressed ring fold: per block, the RS hop chain with an encode /
 // decode per hop kept in registers, then the allgather encode / decode;
 // the result is stored to every rank.

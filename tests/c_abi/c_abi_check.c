@@ -165,9 +165,9 @@ int main(int argc, char** argv) {
   run_case(8, count, RAR_F32, "fused fp32 allreduce", op_fused, NULL);
   run_case(5, count, RAR_F16, "stepwise fp16 allreduce", op_stepwise, NULL);
   run_case(4, count, RAR_F32, "tree fp32 allreduce", op_tree, NULL);
-  int scheds[3] = {RAR_SCHED_FUSED, RAR_SCHED_STAGED, RAR_SCHED_FORWARD};
-  const char* names[3] = {"BFP-8 fused", "BFP-8 staged", "BFP-8 forward"};
-  for (int k = 0; k < 3; ++k) run_case(4, 64 * 1024 + 300, RAR_F16, names[k], op_bfp, &scheds[k]);
+  int scheds[4] = {RAR_SCHED_FUSED, RAR_SCHED_STAGED, RAR_SCHED_FORWARD, RAR_SCHED_PIPELINED};
+  const char* names[4] = {"BFP-8 fused", "BFP-8 staged", "BFP-8 forward", "BFP-8 pipelined"};
+  for (int k = 0; k < 4; ++k) run_case(4, 64 * 1024 + 300, RAR_F16, names[k], op_bfp, &scheds[k]);
   if (failures) return 1;
   printf("c_abi_check OK\n");
   return 0;

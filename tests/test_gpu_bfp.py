@@ -95,7 +95,8 @@ def test_special_blocks_match_oracle():
 
 # ------------------------------------------------------------------ compressed ring
 
-SCHEDS = {"fused": rar.SCHED_FUSED, "staged": rar.SCHED_STAGED, "forward": rar.SCHED_FORWARD}
+SCHEDS = {"fused": rar.SCHED_FUSED, "staged": rar.SCHED_STAGED, "forward": rar.SCHED_FORWARD,
+          "pipelined": rar.SCHED_PIPELINED}
 
 
 def _run_compressed(xs, dt, sched, block=128, mbits=8, unit_elems=4096, method=rar.COMP_BFP):
@@ -114,7 +115,7 @@ def _run_compressed(xs, dt, sched, block=128, mbits=8, unit_elems=4096, method=r
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("sched", ["fused", "staged", "forward"])
+@pytest.mark.parametrize("sched", ["fused", "staged", "forward", "pipelined"])
 @pytest.mark.parametrize("mbits", [8, 4])
 def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
     count = n * 4096 * 2 + 1000  # several units per chunk and a ragged last chunk
@@ -128,7 +129,7 @@ def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
 
 
 @pytest.mark.parametrize("block", [16, 64, 256, 512])
-@pytest.mark.parametrize("sched", ["fused", "staged", "forward"])
+@pytest.mark.parametrize("sched", ["fused", "staged", "forward", "pipelined"])
 def test_compressed_allreduce_other_blocks(block, sched):
     n, count = 4, 4 * 8192 + 900
     xs = inputs.block_scaled(n, count, block=block, salt=block)
@@ -143,7 +144,7 @@ def test_compressed_integer_inputs_are_exact():
     n, count = 8, 8 * 4096
     xs = inputs.integers(n, count, dtype="f16", salt=5)
     exact = sum(x.astype(np.float64) for x in xs)
-    for sched in ("fused", "staged", "forward"):
+    for sched in ("fused", "staged", "forward", "pipelined"):
         got, _, _ = _run_compressed(xs, "f16", sched)
         for g in got:
             assert np.array_equal(g.astype(np.float64), exact)
@@ -233,6 +234,113 @@ def test_bfp8_staged_equals_fused_full_size():
     for r in range(n):
         assert torch.equal(outs[0][r].view(torch.int16), outs[1][r].view(torch.int16)), f"staged rank {r}"
         assert torch.equal(outs[0][r].view(torch.int16), outs[2][r].view(torch.int16)), f"forward rank {r}"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mbits", [8, 4])
+def test_pipelined_equals_fused_full_size(mbits):
+    """N=8, T=128M fp16, 4 MiB units: the pipelined schedule (every message
+    stored and loaded back) gives the fused kernel's bits on every rank."""
+    w = inputs.WORKLOADS["bfp8"]
+    n, count = w["n"], w["count"]
+    xs = inputs.block_scaled(n, count, salt=4)
+    outs = []
+    for sched in (rar.SCHED_FUSED, rar.SCHED_PIPELINED):
+        cfg = rar.compress_cfg(mbits=mbits, unit_bytes=w["unit_bytes"], schedule=sched)
+        ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8,
+                         device="cuda:0")
+        bufs = to_dev(xs, "f16")
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+        del ws
+        outs.append(bufs)
+    for r in range(n):
+        assert torch.equal(outs[0][r].view(torch.int16), outs[1][r].view(torch.int16)), f"rank {r}"
+
+
+def _pipelined_slots(ws, n, count, block, mbits, U, es):
+    """Views of every message slot of the pipelined schedule: (hop, chunk,
+    unit) -> (bytes, unit length)."""
+    L = rar.compressed_chunk_len(count, n, block)
+    upc = -(-L // U)
+    slot = -(-rar.bfp_bytes(U, block, mbits) // 256) * 256
+    out = {}
+    host = ws.cpu().numpy()
+    for h in range(1, n + 1):
+        for c in range(n):
+            lo, hi = min(c * L, count), min((c + 1) * L, count)
+            for u in range(upc):
+                ulo = lo + u * U
+                if ulo >= hi:
+                    break
+                ln = min(U, hi - ulo)
+                base = 1024 + (((h - 1) * n + c) * upc + u) * slot
+                out[h, c, u] = (host[base:base + rar.bfp_bytes(ln, block, mbits)], ulo, ln)
+    return out
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("n,block,mbits", [(4, 128, 8), (3, 128, 4), (5, 64, 6), (2, 256, 3)])
+def test_pipelined_messages_match_oracle_hop_chain(dt, n, block, mbits):
+    """Every message the pipelined schedule leaves in its slots equals the
+    oracle's encode of that hop's partial: message 1 of chunk c encodes rank
+    c+1's unit; message h encodes rank (c+h)'s copy plus the decoded message
+    h-1 (the oracle's decode-accumulate); message N is the owner's allgather
+    message.  Ragged last chunk and several units per chunk."""
+    U = 2048
+    count = n * 3 * U + 700
+    es = 4 if dt == "f32" else 2
+    xs = inputs.block_scaled(n, count, block=block, dtype=dt, salt=n + mbits) if dt != "f32" else \
+        inputs.gradient_like(n, count, salt=n + mbits)
+    cfg = rar.compress_cfg(block=block, mbits=mbits, unit_bytes=U * es, schedule=rar.SCHED_PIPELINED)
+    ws = torch.empty(rar.compressed_workspace_bytes(n, count, DT_NAMES[dt], cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    bufs = to_dev(xs, dt)
+    rar.ring_allreduce_compressed(bufs, cfg, ws)
+    slots = _pipelined_slots(ws, n, count, block, mbits, U, es)
+    assert slots
+    for (h, c, u), (got, ulo, ln) in slots.items():
+        if h != 1:
+            continue
+        p = xs[(c + 1) % n][ulo:ulo + ln].copy()
+        for hh in range(1, n + 1):
+            want = oracle.bfp_encode(p, block=block, mbits=mbits, dt=DT_NAMES[dt])
+            g = slots[hh, c, u][0]
+            bad = np.flatnonzero(g != want)
+            assert bad.size == 0, f"hop {hh} chunk {c} unit {u}: {bad.size} bytes differ, first at {bad[0]}"
+            if hh < n:
+                p = xs[(c + hh + 1) % n][ulo:ulo + ln].copy()
+                oracle.bfp_decode_acc(want, p, block=block, mbits=mbits, dt=DT_NAMES[dt])
+    ref = [x.copy() for x in xs]
+    oracle.ring_allreduce_compressed(ref, block=block, mbits=mbits, unit=U, dt=DT_NAMES[dt])
+    for r, g in enumerate(to_host(bufs, dt)):
+        assert_bits_equal(g, ref[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("mbits", [8, 4])
+def test_pipelined_special_blocks_match_oracle(mbits):
+    """Blocks holding Inf, NaN, zeros, subnormals and the largest halves,
+    through the pipelined ring: results equal the oracle's (NaN where the
+    oracle has NaN)."""
+    n, U = 4, 1024
+    count = n * 2 * U
+    g = np.random.default_rng(mbits)
+    xs = []
+    for r in range(n):
+        x = (g.standard_normal(count) * 1e-2).astype(np.float16)
+        x[0:128] = 0.0
+        x[128:256] = np.float16(6.0e-8) * g.integers(-3, 4, 128)    # binary16 subnormals
+        x[256:384] = np.float16(65504.0) * np.sign(g.standard_normal(128)).astype(np.float16) / n
+        if r == 1:
+            x[384 + 5] = np.inf
+            x[2 * U + 7] = np.nan
+        xs.append(x)
+    ref = [x.copy() for x in xs]
+    oracle.ring_allreduce_compressed(ref, mbits=mbits, unit=U)
+    got, _, _ = _run_compressed(xs, "f16", "pipelined", mbits=mbits, unit_elems=U)
+    for r in range(n):
+        nan = nan_mask(ref[r], "f16")
+        assert np.array_equal(nan_mask(got[r], "f16"), nan), f"rank {r} NaN positions"
+        assert_bits_equal(got[r][~nan], ref[r][~nan], f"rank {r}")
 
 
 @pytest.mark.parametrize("mbits", [8, 4, 2])

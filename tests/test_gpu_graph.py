@@ -61,7 +61,7 @@ def test_ring_allreduce_replays(algo):
     _replay_matches_eager(lambda b: rar.ring_allreduce_ex(b, algo), xs, "f32")
 
 
-@pytest.mark.parametrize("sched", [rar.SCHED_FUSED, rar.SCHED_STAGED, rar.SCHED_FORWARD])
+@pytest.mark.parametrize("sched", [rar.SCHED_FUSED, rar.SCHED_STAGED, rar.SCHED_FORWARD, rar.SCHED_PIPELINED])
 def test_bfp_compressed_replays(sched):
     count = N * 4096 * 3 + 1000
     xs = inputs.block_scaled(N, count, salt=2)

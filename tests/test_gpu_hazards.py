@@ -92,6 +92,9 @@ def test_compressed_paths_stay_in_bounds(dt, n, count):
     cfgs = [("bfp fused", rar.compress_cfg(unit_bytes=8192)),
             ("bfp staged", rar.compress_cfg(unit_bytes=8192, schedule=rar.SCHED_STAGED)),
             ("bfp forward", rar.compress_cfg(unit_bytes=8192, schedule=rar.SCHED_FORWARD)),
+            ("bfp pipelined", rar.compress_cfg(unit_bytes=8192, schedule=rar.SCHED_PIPELINED)),
+            ("bfp4 pipelined block 32", rar.compress_cfg(unit_bytes=4096, mbits=4, block=32,
+                                                         schedule=rar.SCHED_PIPELINED)),
             ("bfp4 staged block 32", rar.compress_cfg(unit_bytes=4096, mbits=4, block=32, schedule=rar.SCHED_STAGED)),
             ("sparse auto", rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=4, unit_bytes=8192,
                                              schedule=rar.SCHED_STAGED))]
