@@ -222,18 +222,25 @@ typedef enum rar_sched {
                             encodes its next message in one kernel, without
                             writing the partial sum back; one launch per hop */
   RAR_SCHED_PIPELINED = 3 /* messages materialised per (hop, chunk, unit), all
-                            kept in the workspace (BFP only); one launch in
-                            which each tile of a unit runs through the hops
-                            in ring order: the sender stores its message, the
+                            kept in the workspace; one launch in which each
+                            tile of a unit runs through the hops in ring
+                            order: the sender stores its message, the
                             receiver loads it back, decodes, adds its own
                             copy and encodes the next; tiles at different
                             hops overlap.  Message h (1..N) of chunk c is
                             sent by rank (c+h) mod N; message N is the
                             owner's allgather message.  Slot of (h, c, u):
-                            workspace + 1024 rounded up to 256 +
-                            (((h-1)*N + c)*units_per_chunk + u) * slot, with
-                            slot = rar_bfp_bytes(unit elements) rounded up
-                            to 256 */
+                            workspace + 1024 + (((h-1)*N + c) *
+                            units_per_chunk + u) * slot, with slot the
+                            unit's largest message (BFP: rar_bfp_bytes;
+                            SPARSE_AUTO: the larger of 16 + BFP and the
+                            all-non-zero sparse message) rounded up to 256.
+                            SPARSE_AUTO: block 128 only (other blocks run
+                            STAGED); the tiles of a unit decide its format
+                            together, so one launch holds whole units on
+                            the chip at once (cooperative launch); a unit
+                            too large for that returns RAR_ENOTSUP before
+                            anything is enqueued */
 } rar_sched;
 
 typedef struct rar_compress_cfg {

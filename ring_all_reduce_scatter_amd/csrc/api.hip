@@ -248,7 +248,12 @@ int cfg_check(const rar_compress_cfg* cfg, int dt, CompPlan* pl) {
   pl->method = cfg->method;
   pl->block = cfg->block;
   pl->mbits = cfg->mbits;
-  pl->sched = cfg->method == RAR_COMP_BFP ? cfg->schedule : RAR_SCHED_STAGED;
+  // SPARSE_AUTO runs staged, or pipelined with 128-element blocks (the fused
+  // and forwarding schedules are BFP-only)
+  pl->sched = cfg->method == RAR_COMP_BFP
+                  ? cfg->schedule
+                  : (cfg->schedule == RAR_SCHED_PIPELINED && cfg->block == 128 ? RAR_SCHED_PIPELINED
+                                                                               : RAR_SCHED_STAGED);
   pl->U = U;
   pl->es = es;
   pl->theta = cfg->sparsity_threshold;
@@ -276,7 +281,11 @@ size_t tiles_per_slot(const CompPlan& pl) { return 2 * (size_t)comp_tiles_per_un
 size_t workspace_need(const CompPlan& pl) {
   if (pl.method == RAR_COMP_NONE || pl.sched == RAR_SCHED_FUSED) return kTrafficBytes;
   if (pl.sched == RAR_SCHED_FORWARD) return slots_offset() + 2 * (size_t)pl.n * pl.upc * pl.slot;
-  if (pl.sched == RAR_SCHED_PIPELINED) return slots_offset() + (size_t)pl.n * pl.n * pl.upc * pl.slot;
+  if (pl.sched == RAR_SCHED_PIPELINED) {
+    const size_t slots = slots_offset() + (size_t)pl.n * pl.n * pl.upc * pl.slot;
+    if (pl.method != RAR_COMP_SPARSE_AUTO) return slots;
+    return slots + 8 * (size_t)sparse_pipe_flag_words(pl.n, pl.upc, pl.U, pl.dt);
+  }
   size_t need = tiles_offset(pl);
   if (pl.method == RAR_COMP_SPARSE_AUTO) need += (size_t)pl.n * pl.upc * tiles_per_slot(pl) * sizeof(uint32_t);
   return need;
@@ -916,6 +925,15 @@ int compressed_run(const CompPlan& pl, void* const* bufs, void* workspace, hipSt
   }
   if (pl.method == RAR_COMP_SPARSE_AUTO) {
     if (nranks == 1 || count == 0) return write_traffic(tr, workspace, st);
+    if (pl.sched == RAR_SCHED_PIPELINED) {
+      char* ws = (char*)workspace;
+      const size_t flags_off = slots_offset() + (size_t)pl.n * pl.n * pl.upc * pl.slot;
+      const hipError_t e = launch_sparse_pipe(make_ptrs(bufs, nranks), nranks, count, pl.L, pl.U, pl.upc, pl.slot,
+                                              (uint8_t*)ws + slots_offset(), (uint64_t*)(ws + flags_off),
+                                              sparse_pipe_flag_words(pl.n, pl.upc, pl.U, pl.dt), (uint64_t*)ws, dtype,
+                                              pl.block, pl.mbits, pl.theta, st);
+      return e == hipErrorCooperativeLaunchTooLarge ? RAR_ENOTSUP : hip_rc(e);
+    }
     return staged_sparse(pl, bufs, (char*)workspace, st);
   }
   if (nranks > 1 && count > 0) {

@@ -144,6 +144,19 @@ struct CompAccJobs {
   int njobs;
 };
 hipError_t launch_comp_decode_acc(const CompAccJobs& jobs, int dt, int block, int mbits, hipStream_t stream);
+// Pipelined SPARSE_AUTO ring in one cooperative launch (sparse_pipe_kernels.hip):
+// messages of hop h = 1..N of (chunk c, unit u) at slots + (((h-1)*n + c)*upc
+// + u)*slot.  flags: sparse_pipe_flag_words() words of device memory for the
+// per-(hop, unit) arrival words, per-tile counts and the abort word (all
+// cleared by the launch itself); traffic: u64 sent[64], recv[64] (cleared
+// too).  Returns hipErrorCooperativeLaunchTooLarge, before enqueuing
+// anything, when one unit's tiles cannot all be resident at once.
+uint64_t sparse_pipe_tiles_per_unit(uint64_t unit_elems, int dt);
+uint64_t sparse_pipe_flag_words(int n, uint64_t upc, uint64_t U, int dt);
+bool sparse_pipe_fits(int n, uint64_t upc, uint64_t U, int dt, int block);
+hipError_t launch_sparse_pipe(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, uint64_t U, uint64_t upc,
+                              uint64_t slot, uint8_t* slots, uint64_t* flags, uint64_t nflag_words,
+                              uint64_t* traffic, int dt, int block, int mbits, float theta, hipStream_t stream);
 // Store each decoded message to elem_off[j] of every rank in `fan`.
 hipError_t launch_comp_decode_fanout(const BfpJobs& jobs, const RankPtrs& fan, int nfan, const uint64_t* elem_off,
                                      int dt, int block, int mbits, hipStream_t stream);

@@ -97,7 +97,9 @@ def test_compressed_paths_stay_in_bounds(dt, n, count):
                                                          schedule=rar.SCHED_PIPELINED)),
             ("bfp4 staged block 32", rar.compress_cfg(unit_bytes=4096, mbits=4, block=32, schedule=rar.SCHED_STAGED)),
             ("sparse auto", rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=4, unit_bytes=8192,
-                                             schedule=rar.SCHED_STAGED))]
+                                             schedule=rar.SCHED_STAGED)),
+            ("sparse auto pipelined", rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=4, unit_bytes=8192,
+                                                       schedule=rar.SCHED_PIPELINED))]
     for name, cfg in cfgs:
         g = Guarded(xs, dt)
         ws, full, used = _ws(rar.compressed_workspace_bytes(n, count, DT_NAMES[dt], cfg))

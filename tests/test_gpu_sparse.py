@@ -15,11 +15,14 @@ from gpu_util import DT_NAMES, assert_bits_equal, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _run_auto(xs, dt, mbits=4, unit_elems=4096, theta=0.5, block=128):
+SCHEDS = {"staged": rar.SCHED_STAGED, "pipelined": rar.SCHED_PIPELINED}
+
+
+def _run_auto(xs, dt, mbits=4, unit_elems=4096, theta=0.5, block=128, sched="staged"):
     n, count = len(xs), xs[0].size
     es = 4 if dt == "f32" else 2
     cfg = rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=mbits, block=block, unit_bytes=unit_elems * es,
-                           sparsity_threshold=theta, schedule=rar.SCHED_STAGED)
+                           sparsity_threshold=theta, schedule=SCHEDS[sched])
     ws = torch.empty(rar.compressed_workspace_bytes(n, count, DT_NAMES[dt], cfg), dtype=torch.uint8, device="cuda:0")
     bufs = to_dev(xs, dt)
     rar.ring_allreduce_compressed(bufs, cfg, ws)
@@ -27,39 +30,42 @@ def _run_auto(xs, dt, mbits=4, unit_elems=4096, theta=0.5, block=128):
     return to_host(bufs, dt), sent, recv
 
 
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("mbits", [4, 8])
-def test_sparse_auto_matches_oracle(dt, n, mbits):
+def test_sparse_auto_matches_oracle(dt, n, mbits, sched):
     count = n * 4096 * 3 + 2500  # several units and tiles per chunk, ragged last chunk
     xs = inputs.sparse_mix(n, count, dtype=dt, salt=n + mbits)
     ref = [x.copy() for x in xs]
     osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=mbits, unit=4096,
                                                     dt=DT_NAMES[dt])
-    got, sent, recv = _run_auto(xs, dt, mbits=mbits)
+    got, sent, recv = _run_auto(xs, dt, mbits=mbits, sched=sched)
     for r in range(n):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
     assert sent == osent and recv == orecv
 
 
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
 @pytest.mark.parametrize("n", [2, 4, 8])
-def test_all_sparse_equals_uncompressed_ring(n):
+def test_all_sparse_equals_uncompressed_ring(n, sched):
     count = n * 8192
     xs = inputs.sparse_mix(n, count, sparse_ranks=n, density=0.01, salt=n)
     ref = [x.copy() for x in xs]
     oracle.ring_allreduce(ref)
-    got, _, _ = _run_auto(xs, "f16")
+    got, _, _ = _run_auto(xs, "f16", sched=sched)
     for r in range(n):
         assert np.array_equal(got[r], ref[r])  # lossless (+0 == -0)
 
 
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
 @pytest.mark.parametrize("theta", [0.1, 0.5, 0.9])
-def test_threshold_values_match_oracle(theta):
+def test_threshold_values_match_oracle(theta, sched):
     n, count = 4, 4 * 6144
     xs = inputs.sparse_mix(n, count, sparse_ranks=2, density=0.3, salt=int(theta * 10))
     ref = [x.copy() for x in xs]
     osent, _ = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=4, unit=2048, theta=theta)
-    got, sent, _ = _run_auto(xs, "f16", unit_elems=2048, theta=theta)
+    got, sent, _ = _run_auto(xs, "f16", unit_elems=2048, theta=theta, sched=sched)
     for r in range(n):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
     assert sent == osent
@@ -76,9 +82,10 @@ def _same_zero_ranks(n, unit, zeros, units, seed=70):
             for _ in range(n)]
 
 
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
 @pytest.mark.parametrize("n", [2, 4])
 @pytest.mark.parametrize("unit,zeros,block", [(640, 448, 128), (80, 56, 16)])
-def test_threshold_binary32_boundary_matches_oracle(n, unit, zeros, block):
+def test_threshold_binary32_boundary_matches_oracle(n, unit, zeros, block, sched):
     """theta = 0.7 with exactly 0.7 * len zeros per unit: the binary32
     threshold (0.699999988...) sends every message sparse.  Library and
     oracle must take the same decision: results bit-exact, byte counters
@@ -88,7 +95,7 @@ def test_threshold_binary32_boundary_matches_oracle(n, unit, zeros, block):
     ref = [x.copy() for x in xs]
     osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, block=block, mbits=4,
                                                     unit=unit, theta=0.7)
-    got, sent, recv = _run_auto(xs, "f16", unit_elems=unit, theta=0.7, block=block)
+    got, sent, recv = _run_auto(xs, "f16", unit_elems=unit, theta=0.7, block=block, sched=sched)
     for r in range(n):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
     assert sent == osent and recv == orecv
@@ -101,7 +108,8 @@ def test_threshold_binary32_boundary_matches_oracle(n, unit, zeros, block):
         assert np.array_equal(got[r], plain[r])
 
 
-def test_exactly_half_zeros_goes_bfp():
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
+def test_exactly_half_zeros_goes_bfp(sched):
     unit = 256
     x0 = np.zeros(2 * unit, dtype=np.float16)
     x1 = np.zeros(2 * unit, dtype=np.float16)
@@ -109,13 +117,14 @@ def test_exactly_half_zeros_goes_bfp():
     x0[unit: unit + unit // 2] = 1.0
     ref = [x0.copy(), x1.copy()]
     osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=4, unit=unit)
-    got, sent, recv = _run_auto([x0, x1], "f16", unit_elems=unit)
+    got, sent, recv = _run_auto([x0, x1], "f16", unit_elems=unit, sched=sched)
     assert sent == osent and recv == orecv
     for r in range(2):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
 
 
-def test_sparse_bfp4_workload_sampled_units():
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
+def test_sparse_bfp4_workload_sampled_units(sched):
     """N=8, T=64M fp16, ranks 0-3 95% zeros, dense BFP-4, 4 MiB units.  All
     ranks identical; sampled units re-run through the oracle in a small ring
     where the unit keeps its chunk index (a unit's messages depend only on
@@ -124,7 +133,7 @@ def test_sparse_bfp4_workload_sampled_units():
     n, count, mbits = w["n"], w["count"], w["mbits"]
     U = w["unit_bytes"] // 2
     xs = inputs.sparse_mix(n, count)
-    got, sent, recv = _run_auto(xs, "f16", mbits=mbits, unit_elems=U)
+    got, sent, recv = _run_auto(xs, "f16", mbits=mbits, unit_elems=U, sched=sched)
     for r in range(1, n):
         assert np.array_equal(got[r].view(np.uint16), got[0].view(np.uint16)), r
     assert sum(sent) == sum(recv)
@@ -162,3 +171,63 @@ def test_sparse_bfp4_workload_broadcast_and_allgather_full_size():
     rar.allgather(bufs)
     for r, g in enumerate(to_host(bufs, "f32")):
         assert_bits_equal(g, ref[r], f"allgather rank {r}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_pipelined_sparse_messages_match_oracle(dt):
+    """Every message the pipelined SPARSE_AUTO schedule leaves in its slots
+    (hop h of chunk c, unit u) equals the oracle's encode of that hop's
+    partial: built hop by hop from the oracle's sparse and BFP primitives,
+    with the unit's format chosen by the oracle's threshold rule."""
+    n, U, mbits, theta = 4, 8192, 4, 0.5
+    es = 4 if dt == "f32" else 2
+    count = n * 2 * U + 3000
+    xs = inputs.sparse_mix(n, count, sparse_ranks=2, density=0.3, dtype=dt, salt=5)
+    cfg = rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=mbits, unit_bytes=U * es, sparsity_threshold=theta,
+                           schedule=rar.SCHED_PIPELINED)
+    ws = torch.empty(rar.compressed_workspace_bytes(n, count, DT_NAMES[dt], cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    bufs = to_dev(xs, dt)
+    rar.ring_allreduce_compressed(bufs, cfg, ws)
+    host = ws.cpu().numpy()
+    L = rar.compressed_chunk_len(count, n, 128)
+    upc = -(-L // U)
+    slot = -(-max(16 + rar.bfp_bytes(U, 128, mbits), 16 + (-(-U * es // 16) * 16) + 4 * U) // 256) * 256
+    odt = DT_NAMES[dt]
+    checked = 0
+    for c in range(n):
+        lo, hi = min(c * L, count), min((c + 1) * L, count)
+        for u in range(upc):
+            ulo = lo + u * U
+            if ulo >= hi:
+                break
+            ln = min(U, hi - ulo)
+            p = xs[(c + 1) % n][ulo:ulo + ln].copy()
+            for h in range(1, n + 1):
+                zeros = int(np.count_nonzero(p == 0))
+                if zeros > np.float64(np.float32(theta)) * ln:
+                    body = oracle.sparse_encode(p, odt)
+                    want = np.concatenate([body[:16], body[16:]])
+                    kind = 1
+                else:
+                    body = oracle.bfp_encode(p, block=128, mbits=mbits, dt=odt)
+                    want = np.concatenate([np.array([0, 0, 0, 0, 0, 0, 0, 0, ln & 0xff, (ln >> 8) & 0xff,
+                                                     (ln >> 16) & 0xff, ln >> 24, 0, 0, 0, 0], np.uint8), body])
+                    kind = 0
+                base = 1024 + (((h - 1) * n + c) * upc + u) * slot
+                got = host[base:base + want.size]
+                bad = np.flatnonzero(got != want)
+                assert bad.size == 0, f"hop {h} chunk {c} unit {u} kind {kind}: {bad.size} bytes differ at {bad[:4]}"
+                checked += 1
+                if h < n:
+                    nxt = xs[(c + h + 1) % n][ulo:ulo + ln].copy()
+                    if kind == 1:
+                        oracle.sparse_decode_acc(body, nxt, odt)
+                    else:
+                        oracle.bfp_decode_acc(body, nxt, block=128, mbits=mbits, dt=odt)
+                    p = nxt
+    assert checked > 0
+    ref = [x.copy() for x in xs]
+    oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=mbits, unit=U, dt=odt)
+    for r, g in enumerate(to_host(bufs, dt)):
+        assert_bits_equal(g, ref[r], f"rank {r}")
