@@ -2,11 +2,9 @@
 
 Encoded bytes, decoded values and the compressed ring's results must equal
 the oracle's bit for bit (the compressed ring is deterministic).  At the full
-N=8, T=128M fp16 size the fused launch the benchmark times is checked on
-sampled blocks: every block's hop chain depends only on that block's N
-inputs and on its chunk's ring order, so the oracle re-runs the sampled
-blocks in a small ring where each sits in the same chunk index.  The result
-must also lie within the stated bound of the exact sum.
+N=8, T=128M fp16 size every element is compared with the oracle run over the
+whole workload (tests/full_size.py), and every block must also lie within
+the stated bound of the exact sum.
 """
 import numpy as np
 import pytest
@@ -163,57 +161,40 @@ def test_collective_mask_without_allreduce_runs_uncompressed():
         assert_bits_equal(g, ref[r], f"rank {r}")
 
 
-def _sampled_blocks_check(xs, got_rank0, got_ranks_equal, L, mbits, nsamp_per_chunk, seed):
-    """Re-run sampled blocks in the oracle; returns the max error ratio to the bound."""
-    n, count = len(xs), xs[0].size
-    g = np.random.default_rng(seed)
-    K = nsamp_per_chunk
-    mini = [np.zeros(n * K * 128, dtype=np.float16) for _ in range(n)]
-    picks = []
-    for c in range(n):
-        nblk = (min((c + 1) * L, count) - c * L) // 128
-        bl = np.sort(g.choice(nblk, size=K, replace=False)) + c * L // 128
-        picks.append(bl)
-        for r in range(n):
-            for k, b in enumerate(bl):
-                mini[r][(c * K + k) * 128:(c * K + k + 1) * 128] = xs[r][b * 128:(b + 1) * 128]
-    raw = [m.copy() for m in mini]
-    _, _, bm = oracle.ring_allreduce_compressed(mini, mbits=mbits, unit=K * 128, with_blockmax=True)
-    worst = 0.0
-    for c in range(n):
-        for k, b in enumerate(picks[c]):
-            sl = slice((c * K + k) * 128, (c * K + k + 1) * 128)
-            gsl = slice(b * 128, (b + 1) * 128)
-            assert_bits_equal(got_rank0[gsl], mini[0][sl], f"block {b}")
-            exact = sum(r_[sl].astype(np.float64) for r_ in raw)
-            err = np.abs(got_rank0[gsl].astype(np.float64) - exact)
-            bound = n * 2.0 ** -(mbits - 1) * bm[c * K + k]
-            if bound > 0:
-                worst = max(worst, float(err.max() / bound))
-            else:
-                assert err.max() == 0
-    return worst
-
-
 @pytest.mark.slow
-def test_bfp8_workload_full_size_sampled():
-    """N=8, T=128M fp16, 128-element blocks, 8-bit mantissas: the fused launch
-    the benchmark times.  All ranks bit-identical; sampled blocks bit-exact
-    against the oracle and within N * 2^-(m-1) * blockmax of the exact sum."""
+@pytest.mark.parametrize("sched", ["fused", "pipelined"])
+def test_bfp8_workload_full_size(sched):
+    """N=8, T=128M fp16, 128-element blocks, 8-bit mantissas, 4 MiB units:
+    the fused launch the benchmark times and the pipelined schedule.  Every
+    element of every rank equals the oracle's (the whole workload, run on
+    host threads one unit index at a time), the byte counters equal the
+    oracle's, and every block lies within N * 2^-(m-1) * blockmax of the
+    exact sum (blockmax: the largest block max among the messages that
+    carried the block)."""
+    import full_size
     w = inputs.WORKLOADS["bfp8"]
-    n, count, mbits = w["n"], w["count"], w["mbits"]
+    n, count, mbits, U = w["n"], w["count"], w["mbits"], w["unit_bytes"] // 2
     xs = inputs.block_scaled(n, count)
-    cfg = rar.compress_cfg(mbits=mbits, unit_bytes=w["unit_bytes"])
+    cfg = rar.compress_cfg(mbits=mbits, unit_bytes=w["unit_bytes"], schedule=SCHEDS[sched])
     ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
     bufs = to_dev(xs, "f16")
     rar.ring_allreduce_compressed(bufs, cfg, ws)
+    sent, recv = rar.compressed_traffic(ws, n)
+    del ws
     for r in range(1, n):
         assert torch.equal(bufs[r].view(torch.int16), bufs[0].view(torch.int16)), f"rank {r} differs"
     got0 = to_host(bufs[:1], "f16")[0]
     del bufs
     L = rar.compressed_chunk_len(count, n, 128)
-    worst = _sampled_blocks_check(xs, got0, True, L, mbits, nsamp_per_chunk=256, seed=1)
-    assert worst <= 1.0, worst
+    want, osent, orecv, bm = full_size.compressed_ring(xs, L, U, mbits=mbits, with_blockmax=True)
+    assert_bits_equal(got0, want, "rank 0")
+    assert sent == osent and recv == orecv
+    exact = np.zeros(count, dtype=np.float64)
+    for x in xs:
+        exact += x
+    err = np.abs(got0.astype(np.float64) - exact).reshape(-1, 128).max(axis=1)
+    bound = n * 2.0 ** -(mbits - 1) * bm
+    assert np.all(err <= bound), int(np.argmax(err - bound))
 
 
 @pytest.mark.slow

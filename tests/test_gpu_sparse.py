@@ -123,12 +123,14 @@ def test_exactly_half_zeros_goes_bfp(sched):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
 
 
+@pytest.mark.slow
 @pytest.mark.parametrize("sched", ["staged", "pipelined"])
-def test_sparse_bfp4_workload_sampled_units(sched):
-    """N=8, T=64M fp16, ranks 0-3 95% zeros, dense BFP-4, 4 MiB units.  All
-    ranks identical; sampled units re-run through the oracle in a small ring
-    where the unit keeps its chunk index (a unit's messages depend only on
-    that unit of every rank), bit-exact; byte counters consistent."""
+def test_sparse_bfp4_workload_full_size(sched):
+    """N=8, T=64M fp16, ranks 0-3 95% zeros, dense BFP-4, 4 MiB units, both
+    schedules: every element of every rank equals the oracle's (the whole
+    workload on host threads, one unit index at a time) and so do the byte
+    counters, which show which messages went sparse."""
+    import full_size
     w = inputs.WORKLOADS["sparse_bfp4"]
     n, count, mbits = w["n"], w["count"], w["mbits"]
     U = w["unit_bytes"] // 2
@@ -136,19 +138,16 @@ def test_sparse_bfp4_workload_sampled_units(sched):
     got, sent, recv = _run_auto(xs, "f16", mbits=mbits, unit_elems=U, sched=sched)
     for r in range(1, n):
         assert np.array_equal(got[r].view(np.uint16), got[0].view(np.uint16)), r
-    assert sum(sent) == sum(recv)
+    L = rar.compressed_chunk_len(count, n, 128)
+    want, osent, orecv, _ = full_size.compressed_ring(xs, L, U, method=oracle.COMP_SPARSE_AUTO, mbits=mbits,
+                                                       theta=w["theta"])
+    assert_bits_equal(got[0], want, "rank 0")
+    assert sent == osent and recv == orecv
     # wire bytes well under the uncompressed ring's 2*S*(N-1)/N per rank
     assert max(sent) < 2 * count * 2 * (n - 1) // n * 0.6
-    L = rar.compressed_chunk_len(count, n, 128)
-    for c, u in ((1, 0), (6, 3)):  # 4 units of 2M elements per 8M-element chunk
-        lo = c * L + u * U
-        mini = [np.zeros(n * U, dtype=np.float16) for _ in range(n)]
-        for r in range(n):
-            mini[r][c * U:(c + 1) * U] = xs[r][lo:lo + U]
-        oracle.ring_allreduce_compressed(mini, method=oracle.COMP_SPARSE_AUTO, mbits=mbits, unit=U)
-        assert_bits_equal(got[0][lo:lo + U], mini[0][c * U:(c + 1) * U], f"chunk {c} unit {u}")
 
 
+@pytest.mark.slow
 def test_sparse_bfp4_workload_broadcast_and_allgather_full_size():
     """Broadcast of a 16M fp32 tensor from rank 0 and allgather of 16M fp32
     shards over 8 ranks (both uncompressed: the operator-aware policy keeps

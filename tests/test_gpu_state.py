@@ -94,14 +94,15 @@ def test_stateful_rejects_unsupported_configs():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("fb", ["error", "delta"])
-def test_stateful_bfp8_workload_full_size_sampled(fb):
+def test_stateful_bfp8_workload_full_size(fb):
     """N=8, T=128M fp16 per rank, 128-element blocks, 8-bit mantissas, with
     128M-float state per rank: two calls of the launch the benchmark times.
-    Every block's chain depends only on its N inputs and N state blocks and
-    its chunk's ring order, so sampled blocks are re-run in a small ring where
-    each keeps its chunk index; result and every rank's state must match."""
+    Every element of the result and of every rank's state equals the
+    oracle's, run over the whole workload on host threads (one unit index at
+    a time, the state sliced alike)."""
+    import full_size
     w = inputs.WORKLOADS["bfp8"]
-    n, count, mbits = w["n"], w["count"], w["mbits"]
+    n, count, mbits, U = w["n"], w["count"], w["mbits"], w["unit_bytes"] // 2
     xs = inputs.block_scaled(n, count)
     cfg = rar.compress_cfg(mbits=mbits, unit_bytes=w["unit_bytes"])
     ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
@@ -112,24 +113,12 @@ def test_stateful_bfp8_workload_full_size_sampled(fb):
         rar.ring_allreduce_compressed_state(bufs, st, FB[fb][0], cfg, ws)
     for r in range(1, n):
         assert torch.equal(bufs[r].view(torch.int16), bufs[0].view(torch.int16)), f"rank {r} differs"
-    L = rar.compressed_chunk_len(count, n, 128)
-    K = 64
-    g = np.random.default_rng(7)
-    picks = []
-    for c in range(n):
-        nblk = (min((c + 1) * L, count) - c * L) // 128
-        picks.append(np.sort(g.choice(nblk, size=K, replace=False)) + c * L // 128)
-    elems = np.concatenate([np.arange(b * 128, (b + 1) * 128) for c in range(n) for b in picks[c]])
-    idx = torch.from_numpy(elems).to("cuda:0")
-    got = bufs[0][idx].cpu().numpy()
-    got_st = [s[idx].cpu().numpy() for s in st]
+    got = to_host(bufs[:1], "f16")[0]
+    got_st = to_host(st, "f32")
     del bufs, st
-    mini_x = [x[elems].copy() for x in xs]
-    mini_st = [np.zeros(elems.size, dtype=np.float32) for _ in range(n)]
-    mini = None
-    for _ in range(2):
-        mini = [m.copy() for m in mini_x]
-        oracle.ring_allreduce_compressed_state(mini, mini_st, FB[fb][1], mbits=mbits, unit=K * 128)
-    assert_bits_equal(got, mini[0], "sampled blocks, result")
+    L = rar.compressed_chunk_len(count, n, 128)
+    want, want_st = full_size.compressed_ring_state(xs, [np.zeros(count, np.float32) for _ in range(n)], L, U,
+                                                    FB[fb][1], 2, mbits=mbits)
+    assert_bits_equal(got, want, "result")
     for r in range(n):
-        assert_bits_equal(got_st[r], mini_st[r], f"sampled blocks, rank {r} state")
+        assert_bits_equal(got_st[r], want_st[r], f"rank {r} state")
