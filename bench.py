@@ -4,11 +4,14 @@
 Headline: ring allreduce, N=8 simulated ranks, T=64M fp32 per rank (256 MiB),
 gradient-like values N(0, 1e-3) with 1% outliers x100, fused schedule.  The
 metric is the per-rank bus bandwidth 2*S*(N-1)/N / t (S = bytes per rank)
-and the fraction of the HBM roofline the fused kernel reaches.  A second
-leg times the BFP-8 compressed allreduce (N=8, T=128M fp16, 128-element
-blocks, block-scaled values).  Inputs are generated on the host once, copied
-into a pool of device sets, and every timed step runs on a fresh set, so no
-restore happens inside the timed region.
+and the fraction of the HBM roofline the fused kernel reaches.  Further
+legs on the same line: the BFP-8 compressed allreduce (N=8, T=128M fp16,
+128-element blocks, block-scaled values) in the fused schedule ("bfp8") and
+in the pipelined 4 MiB-unit schedule with every message materialised
+("bfp8_pipelined"), and the sparse + BFP-4 allreduce (N=8, T=64M fp16)
+pipelined and staged ("sparse_bfp4").  Inputs are generated on the host
+once, copied into a pool of device sets, and every timed step runs on a
+fresh set, so no restore happens inside the timed region.
 
 Prints ONE JSON line.  --gpus above 1 is refused: all simulated ranks share
 one GPU's HBM.
@@ -68,6 +71,11 @@ COUNTER_KERNELS = {
     "rank_hash_f32_n8": {
         "match": "::rank_hash_kernel", "workload": "N=8 x 256 MiB",
         "algorithmic": 8 * 256 * MIB, "sources": [_CSRC + "hash_kernels.hip", _CSRC + "common.hpp"]},
+    "bfp_pipe_f16_n8": {
+        "match": "::bfp_pipe_h16_kernel<8, 1, true>", "workload": "N=8 x 128M fp16, BFP-8, pipelined, 4 MiB units",
+        # inputs read once, outputs written once, every message (N per chunk and unit) written once
+        "algorithmic": 2 * 8 * 256 * MIB + 8 * 8 * 8 * (16384 + 2 * MIB),
+        "sources": [_CSRC + "pipe_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp"]},
     "bucket_fold_bf16_n16": {
         "match": "::bucket_fold_kernel<2, 16,", "workload": "N=16 bf16, 200 gradient tensors in 25 MiB buckets",
         # every rank's copy of every gradient element read once and written once
@@ -89,6 +97,11 @@ PIPELINE_COUNTERS = {
                     "::comp_decode_fanout_kernel<"], "calls": 3,
         "workload": "staged sparse + BFP-4 allreduce, N=8 x 64M fp16, ranks 0-3 95% zeros",
         "sources": [_CSRC + "sparse_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp", _CSRC + "api.hip"]},
+    "sparse_bfp4_allreduce_pipelined": {
+        "matches": ["::sparse_pipe_kernel<", "zero_u64_kernel"], "calls": 3,
+        "workload": "pipelined sparse + BFP-4 allreduce, N=8 x 64M fp16, ranks 0-3 95% zeros",
+        "sources": [_CSRC + "sparse_pipe_kernels.hip", _CSRC + "block_scan.hpp", _CSRC + "bfp_device.hpp",
+                    _CSRC + "common.hpp", _CSRC + "api.hip"]},
 }
 
 
@@ -112,15 +125,20 @@ def _bucket_elements():
 
 def _algorithmic(k):
     return k["algorithmic"]() if callable(k["algorithmic"]) else k["algorithmic"]
-# calibration copy of the counters run: 256 MiB read and 256 MiB written
+# validation copy of the counters run: 256 MiB read and 256 MiB written
 CALIBRATION = {"match": "copy_jobs_kernel", "bytes": 256 * MIB}
+# HBM bytes are measured, not calibrated: the TCC counts every read request
+# sent to DRAM and every write request written to DRAM in 32-byte units (a
+# 64-byte request counts 2, a 128-byte one 4).  The 128-byte read requests
+# and TCC_BUBBLE (which FETCH_SIZE takes as the 128-byte reads) come in the
+# same pass: on gfx950 TCC_BUBBLE stays near zero while the reads are
+# 128-byte requests, so FETCH_SIZE charges them 64 bytes and reads half.
+PMC_COUNTERS = ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "TCC_EA0_RDREQ_128B_sum",
+                "TCC_BUBBLE_sum"]
 PMC_COMMANDS = [
-    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv "
-    "-d $R/gpurun_out/pmc_fetch -o pmc -- python -u $R/bench.py --counters",
-    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv "
-    "-d $R/gpurun_out/pmc_write -o pmc -- python -u $R/bench.py --counters",
-    "python bench.py --ingest-counters gpurun_out/pmc_fetch/pmc_counter_collection.csv "
-    "gpurun_out/pmc_write/pmc_counter_collection.csv",
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc " + " ".join(PMC_COUNTERS) +
+    " --output-format csv -d $R/gpurun_out/pmc_dram -o pmc -- python -u $R/bench.py --counters",
+    "python bench.py --ingest-counters gpurun_out/pmc_dram/pmc_counter_collection.csv",
 ]
 
 
@@ -386,7 +404,6 @@ def bfp8_leg(args):
     pristine = [torch.from_numpy(x).to("cuda:0") for x in xs]
     nsets = 1 + min(args.steps, args.max_sets)
     sets = make_sets(pristine, nsets)
-    del pristine
     cfg = rar.compress_cfg(block=block, mbits=mbits, unit_bytes=w["unit_bytes"], schedule=rar.SCHED_FUSED)
     ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
     S = count * 2
@@ -395,8 +412,21 @@ def bfp8_leg(args):
                                      args.warmup, args.steps)
     sent, _ = rar.compressed_traffic(ws, n)
     got0 = sets[1][0].cpu().numpy()
+    fused_out = sets[1][0].clone()
     same = all(torch.equal(sets[1][r].view(torch.int16), sets[1][0].view(torch.int16)) for r in range(n))
-    del sets
+    # the same calls through the pipelined schedule (every message written to
+    # the workspace and read back by its receiver), on fresh copies of the sets
+    del ws
+    for st in sets:
+        for v, p in zip(st, pristine):
+            v.copy_(p)
+    del pristine
+    pcfg = rar.compress_cfg(block=block, mbits=mbits, unit_bytes=w["unit_bytes"], schedule=rar.SCHED_PIPELINED)
+    pws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, pcfg), dtype=torch.uint8, device="cuda:0")
+    log(f"[bench] bfp8 leg: pipelined schedule, timing {args.steps} steps")
+    ptl = time_leg(lambda bufs: rar.ring_allreduce_compressed(bufs, pcfg, pws), sets, args.warmup, args.steps)
+    psame = bool(torch.equal(sets[1][0].view(torch.int16), fused_out.view(torch.int16)))
+    del sets, pws, fused_out
     torch.cuda.empty_cache()
     alg_bytes = 2 * n * S
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -416,6 +446,20 @@ def bfp8_leg(args):
                      "kernel": "bfp_ring_fold_kernel<f16, N=8, block 128>", "algorithmic_bytes_per_launch": alg_bytes},
         "ranks_identical": bool(same),
     }
+    pk = COUNTER_KERNELS["bfp_pipe_f16_n8"]
+    own = _algorithmic(pk)
+    res["pipelined"] = {
+        "schedule": "pipelined: 4 MiB units, every message written to the workspace and read back by its "
+                    "receiver, one launch",
+        "value": round(busbw(S, n, ptl[0]), 2), "unit": "GB/s", "ms_per_step": round(ptl[0], 4),
+        "kernel_ms": round(ptl[1], 4), "kernel_ms_median": round(ptl.median_ms, 4),
+        "frac_of_roofline": round(alg_bytes / (ptl[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "own_algorithmic_bytes": own,
+        "frac_of_roofline_own_bytes": round(own / (ptl[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": counter_traffic("bfp_pipe_f16_n8", pk["sources"]),
+        "kernel": "bfp_pipe_h16_kernel<N=8, 8-bit>",
+        "equals_fused_bits": psame,
+    }
     if not args.no_cpu_baseline:
         import oracle
         sample = count // 16
@@ -434,8 +478,60 @@ def bfp8_leg(args):
                                "sample": f"N={n}, T={sample} fp16 per rank (1/16 of the workload, same value "
                                          f"recipe), median of 3 single-thread runs ({dt:.1f} s each, "
                                          f"{sum(times):.1f} s in all) pinned to host core {pin.core}"}
-    res["parity_first_timed_output"] = sampled_bfp_parity(xs, got0, rar.compressed_chunk_len(count, n, block), mbits)
+        res["parity_first_timed_output"] = sampled_bfp_parity(xs, got0, rar.compressed_chunk_len(count, n, block),
+                                                              mbits)
     return res
+
+
+def sparse_leg(args):
+    """The sparse + BFP-4 workload (N=8, T=64M fp16, ranks 0-3 95% zeros, 4 MiB
+    units) through the single-launch pipelined SPARSE_AUTO schedule; its first
+    timed output is compared bit for bit with the staged schedule's."""
+    import torch
+
+    import ring_all_reduce_scatter_amd as rar
+    from ring_all_reduce_scatter_amd import inputs
+
+    w = inputs.WORKLOADS["sparse_bfp4"]
+    n, count = w["n"], w["count"]
+    log(f"[bench] sparse leg: generating N={n} x T={count} fp16 inputs")
+    xs = inputs.sparse_mix(n, count)
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xs]
+    del xs
+    steps = max(3, min(args.steps, 10))
+    sets = make_sets(pristine, 1 + steps)
+    S = count * 2
+    out = {}
+    firsts = {}
+    for name, sched in (("pipelined", rar.SCHED_PIPELINED), ("staged", rar.SCHED_STAGED)):
+        for st in sets:
+            for v, p in zip(st, pristine):
+                v.copy_(p)
+        cfg = rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=w["mbits"], unit_bytes=w["unit_bytes"],
+                               sparsity_threshold=w["theta"], schedule=sched)
+        ws = torch.empty(rar.compressed_workspace_bytes(n, count, rar.F16, cfg), dtype=torch.uint8, device="cuda:0")
+        log(f"[bench] sparse leg: {name} schedule, timing {steps} steps")
+        tl = time_leg(lambda b: rar.ring_allreduce_compressed(b, cfg, ws), sets, 2, steps)
+        sent, _ = rar.compressed_traffic(ws, n)
+        firsts[name] = sets[1][0].clone()
+        key = f"sparse_bfp4_allreduce_{name}"
+        tr = pipeline_traffic(key)
+        out[name] = {"value": round(busbw(S, n, tl[0]), 2), "unit": "GB/s", "ms_per_step": round(tl[0], 4),
+                     "kernel_ms": round(tl[1], 4), "kernel_ms_median": round(tl.median_ms, 4),
+                     "frac_of_roofline": round(2 * n * S / (tl[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "wire_bytes_rank0": sent[0], "traffic_per_call": tr}
+        if tr:
+            out[name]["frac_of_roofline_own_bytes"] = round(tr / (tl[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        del ws
+    same = bool(torch.equal(firsts["pipelined"].view(torch.int16), firsts["staged"].view(torch.int16)))
+    del sets, pristine, firsts
+    torch.cuda.empty_cache()
+    return {"metric": "sparse + BFP-4 compressed all-reduce effective bus GB/s (2T(N-1)/N fp16 bytes per rank)",
+            "config": {"workload": f"sparsity-aware compressed ring allreduce, N={n} ranks, T={count} fp16 per rank, "
+                                   f"ranks 0-{n // 2 - 1} 95% zeros, threshold {w['theta']}, dense messages BFP "
+                                   f"4-bit on 128-element blocks, {w['unit_bytes'] >> 20} MiB units"},
+            **out["pipelined"], "schedule": "pipelined (one cooperative launch)", "staged": out["staged"],
+            "pipelined_equals_staged_bits": same}
 
 
 def sampled_bfp_parity(xs, got0, L, mbits, per_chunk=64):
@@ -659,9 +755,10 @@ def extra_legs(args):
 
 def counters_run(reps=3):
     """Short launch sequence for hardware-counter passes: a plain copy of known
-    size (broadcast over 2 ranks of 256 MiB fp32: 256 MiB read, 256 MiB written)
-    to calibrate FETCH_SIZE / WRITE_SIZE, then the fused folds (fp32, BFP-8,
-    BFP-8 with error feedback), the rank hash and the bucketed fold."""
+    size (broadcast over 2 ranks of 256 MiB fp32: 256 MiB read, 256 MiB
+    written) that validates the counters, then the fused folds (fp32, BFP-8,
+    BFP-8 with error feedback), the rank hash, the bucketed fold, the staged
+    and pipelined compressed schedules."""
     import torch
 
     import ring_all_reduce_scatter_amd as rar
@@ -732,6 +829,28 @@ def counters_run(reps=3):
             b.copy_(p)
         rar.ring_allreduce_compressed(bufs, cfg, ws)
     torch.cuda.synchronize()
+    del ws
+    log("[bench] counters run: staged sparse done")
+    # the same workload through the pipelined single-launch schedule
+    cfg = rar.compress_cfg(method=rar.COMP_SPARSE_AUTO, mbits=w5["mbits"], unit_bytes=w5["unit_bytes"],
+                           sparsity_threshold=w5["theta"], schedule=rar.SCHED_PIPELINED)
+    ws = torch.empty(rar.compressed_workspace_bytes(w5["n"], w5["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    for _ in range(PIPELINE_COUNTERS["sparse_bfp4_allreduce_pipelined"]["calls"]):
+        for b, p in zip(bufs, pristine):
+            b.copy_(p)
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+    torch.cuda.synchronize()
+    del ws, bufs, pristine
+    # the pipelined BFP-8 schedule on the bfp8 workload (4 MiB units)
+    wb = inputs.WORKLOADS["bfp8"]
+    bufs = [torch.from_numpy(x).to("cuda:0") for x in inputs.block_scaled(wb["n"], wb["count"])]
+    cfg = rar.compress_cfg(unit_bytes=wb["unit_bytes"], schedule=rar.SCHED_PIPELINED)
+    ws = torch.empty(rar.compressed_workspace_bytes(wb["n"], wb["count"], rar.F16, cfg), dtype=torch.uint8,
+                     device="cuda:0")
+    for _ in range(reps):
+        rar.ring_allreduce_compressed(bufs, cfg, ws)
+    torch.cuda.synchronize()
     log("[bench] counters run done")
 
 
@@ -766,56 +885,67 @@ def _counter_values(path, counter, match):
     return vals
 
 
-def ingest_counters(fetch_csv, write_csv):
-    """Turn two rocprofv3 counter passes over `bench.py --counters` (FETCH_SIZE
-    and WRITE_SIZE, KiB per dispatch) into profiles/counters.json: each
-    counter is scaled by what it reads for the calibration copy of known size,
-    and the median over a kernel's dispatches is kept."""
+def ingest_counters(csv_path):
+    """Turn the rocprofv3 counter pass over `bench.py --counters` into
+    profiles/counters.json: HBM bytes read = 32 x TCC_EA0_RDREQ_DRAM_32B and
+    written = 32 x TCC_EA0_WRREQ_WRITE_DRAM_32B per dispatch (median over a
+    kernel's dispatches), no scale factor.  The copy of known size is
+    reported as a check of the counters."""
     import statistics
-    cal_bytes_kib = CALIBRATION["bytes"] / 1024
-    cf = statistics.median(_counter_values(fetch_csv, "FETCH_SIZE", CALIBRATION["match"]))
-    cw = statistics.median(_counter_values(write_csv, "WRITE_SIZE", CALIBRATION["match"]))
-    out = {"_calibration": {
-        "kernel": "copy_jobs_kernel (broadcast over 2 ranks, 256 MiB fp32: 262144 KiB read and written)",
-        "fetch_kib_measured": cf, "write_kib_measured": cw,
-        "fetch_scale": round(cal_bytes_kib / cf, 5), "write_scale": round(cal_bytes_kib / cw, 5),
-        "commands": PMC_COMMANDS}}
-    rows = []
+    rd, wr, r128, bub = PMC_COUNTERS
+
+    def per_kernel(match):
+        r = _counter_values(csv_path, rd, match)
+        w = _counter_values(csv_path, wr, match)
+        q = _counter_values(csv_path, r128, match)
+        b = _counter_values(csv_path, bub, match)
+        return r, w, q, b
+
+    r, w, q, b = per_kernel(CALIBRATION["match"])
+    cr, cw = 32 * statistics.median(r), 32 * statistics.median(w)
+    out = {"_method": {
+        "read_bytes": "32 x " + rd, "write_bytes": "32 x " + wr, "commands": PMC_COMMANDS,
+        "check_copy": {"kernel": "copy_jobs_kernel (broadcast over 2 ranks, 256 MiB fp32)",
+                       "bytes_each_way": CALIBRATION["bytes"], "read_bytes_measured": int(cr),
+                       "write_bytes_measured": int(cw), "read_ratio": round(cr / CALIBRATION["bytes"], 5),
+                       "write_ratio": round(cw / CALIBRATION["bytes"], 5),
+                       "rdreq_128B": statistics.median(q), "tcc_bubble": statistics.median(b)}}}
+    rows = [f"| copy check: `copy_jobs_kernel` 256 MiB each way | {len(r)} | {int(cr):,} | {int(cw):,} | "
+            f"{int(cr + cw):,} | {2 * CALIBRATION['bytes']:,} | {(cr + cw) / (2 * CALIBRATION['bytes']):.4f} | "
+            f"{statistics.median(q):,.0f} / {statistics.median(b):,.0f} |"]
     for key, k in COUNTER_KERNELS.items():
-        fv = _counter_values(fetch_csv, "FETCH_SIZE", k["match"])
-        wv = _counter_values(write_csv, "WRITE_SIZE", k["match"])
-        if not fv or not wv:
+        r, w, q, b = per_kernel(k["match"])
+        if not r or not w:
             continue
-        fk, wk = statistics.median(fv), statistics.median(wv)
-        hbm = int(round((fk * cal_bytes_kib / cf + wk * cal_bytes_kib / cw) * 1024))
-        out[key] = {"kernel_match": k["match"], "workload": k["workload"], "fetch_kib": fk, "write_kib": wk,
-                    "dispatches": len(fv), "hbm_bytes_per_launch": hbm,
-                    "algorithmic_bytes_per_launch": _algorithmic(k), "source_sha": source_sha(k["sources"]),
-                    "sources": k["sources"]}
+        rb, wb = int(32 * statistics.median(r)), int(32 * statistics.median(w))
         alg = _algorithmic(k)
-        rows.append(f"| `{k['match']}` ({k['workload']}) | {fk:.1f} | {wk:.1f} | {hbm:,} | {alg:,} | "
-                    f"{hbm / alg:.4f} |")
+        out[key] = {"kernel_match": k["match"], "workload": k["workload"], "dispatches": len(r),
+                    "hbm_read_bytes_per_launch": rb, "hbm_write_bytes_per_launch": wb,
+                    "hbm_bytes_per_launch": rb + wb, "algorithmic_bytes_per_launch": alg,
+                    "rdreq_128B": statistics.median(q), "tcc_bubble": statistics.median(b),
+                    "source_sha": source_sha(k["sources"]), "sources": k["sources"]}
+        rows.append(f"| `{k['match']}` ({k['workload']}) | {len(r)} | {rb:,} | {wb:,} | {rb + wb:,} | {alg:,} | "
+                    f"{(rb + wb) / alg:.4f} | {statistics.median(q):,.0f} / {statistics.median(b):,.0f} |")
     pipes = {}
     for key, pdef in PIPELINE_COUNTERS.items():
-        fk = sum(sum(_counter_values(fetch_csv, "FETCH_SIZE", m)) for m in pdef["matches"])
-        wk = sum(sum(_counter_values(write_csv, "WRITE_SIZE", m)) for m in pdef["matches"])
-        nd = sum(len(_counter_values(fetch_csv, "FETCH_SIZE", m)) for m in pdef["matches"])
-        if not nd:
+        rs = [v for m in pdef["matches"] for v in _counter_values(csv_path, rd, m)]
+        ws_ = [v for m in pdef["matches"] for v in _counter_values(csv_path, wr, m)]
+        if not rs:
             continue
-        hbm = int(round((fk * cal_bytes_kib / cf + wk * cal_bytes_kib / cw) * 1024 / pdef["calls"]))
+        rb, wb = int(32 * sum(rs) / pdef["calls"]), int(32 * sum(ws_) / pdef["calls"])
         pipes[key] = {"workload": pdef["workload"], "kernels": pdef["matches"], "calls": pdef["calls"],
-                      "dispatches": nd, "fetch_kib_per_call": round(fk / pdef["calls"], 1),
-                      "write_kib_per_call": round(wk / pdef["calls"], 1), "hbm_bytes_per_call": hbm,
-                      "source_sha": source_sha(pdef["sources"]), "sources": pdef["sources"]}
-        rows.append(f"| {pdef['workload']} (all {nd} dispatches of {pdef['calls']} calls) | "
-                    f"{fk / pdef['calls']:.1f} | {wk / pdef['calls']:.1f} | {hbm:,} per call | - | - |")
+                      "dispatches": len(rs), "hbm_read_bytes_per_call": rb, "hbm_write_bytes_per_call": wb,
+                      "hbm_bytes_per_call": rb + wb, "source_sha": source_sha(pdef["sources"]),
+                      "sources": pdef["sources"]}
+        rows.append(f"| {pdef['workload']} (all {len(rs)} dispatches of {pdef['calls']} calls, per call) | "
+                    f"{len(rs)} | {rb:,} | {wb:,} | {rb + wb:,} | - | - | - |")
     out["pipelines"] = pipes
     with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    print(f"calibration: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB for {cal_bytes_kib:.0f} KiB moved")
-    print("| kernel (workload) | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per launch | algorithmic bytes | ratio |")
-    print("|---|---|---|---|---|---|")
+    print("| kernel (workload) | dispatches | HBM read bytes | HBM write bytes | HBM bytes | algorithmic bytes | "
+          "ratio | 128-byte read requests / TCC_BUBBLE |")
+    print("|---|---|---|---|---|---|---|---|")
     print("\n".join(rows))
 
 
@@ -832,11 +962,11 @@ def main():
                     help="only run the short launch sequence used for rocprofv3 --pmc passes")
     ap.add_argument("--jsonl", metavar="PATH",
                     help="also append one JSON record per leg (timing, bandwidth, roofline, per-rank bytes)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="(no GPU) write profiles/counters.json from two rocprofv3 --pmc passes over --counters")
+    ap.add_argument("--ingest-counters", metavar="PMC_CSV",
+                    help="(no GPU) write profiles/counters.json from the rocprofv3 --pmc pass over --counters")
     args = ap.parse_args()
     if args.ingest_counters:
-        ingest_counters(*args.ingest_counters)
+        ingest_counters(args.ingest_counters)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the N simulated ranks share one MI355X's HBM, so --gpus "
@@ -887,8 +1017,12 @@ def main():
     line["copy_peak"] = cp
     line["roofline"]["frac_of_copy_peak"] = round(line["roofline"]["achieved"] / cp["value"], 4)
     if not args.skip_bfp8:
-        line["bfp8"] = bfp8_leg(args)
-        line["bfp8"]["roofline"]["frac_of_copy_peak"] = round(line["bfp8"]["roofline"]["achieved"] / cp["value"], 4)
+        b = bfp8_leg(args)
+        b["roofline"]["frac_of_copy_peak"] = round(b["roofline"]["achieved"] / cp["value"], 4)
+        line["bfp8_pipelined"] = {"metric": b["metric"], "config": {**b["config"], "schedule": "pipelined"},
+                                  **b.pop("pipelined")}
+        line["bfp8"] = b
+        line["sparse_bfp4"] = sparse_leg(args)
     if args.extra:
         line["extra"] = extra_legs(args)
     if args.jsonl:
