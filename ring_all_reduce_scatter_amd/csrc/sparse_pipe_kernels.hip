@@ -37,6 +37,7 @@
 // lane's span, which is ascending index order.
 #include "bfp_device.hpp"
 #include "block_scan.hpp"
+#include "h16_codec.hpp"
 #include "launch.hpp"
 
 namespace rar {
@@ -147,6 +148,8 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
   const int mbits = a.mbits;
   const uint64_t block = (uint64_t)lpb * 8;
   const float qmax = (float)((1 << (mbits - 1)) - 1);
+  // binary16 with 128-element blocks: the packed codec (h16_codec.hpp)
+  constexpr bool kH16 = DT == DT_F16 && LPB == 16;
   const uint32_t gang = blockIdx.x / a.kmax, k = blockIdx.x - gang * a.kmax;
   const uint32_t nunits = (uint32_t)N * (uint32_t)a.upc;  // units of one hop (< 2^32: at most 64 ranks)
   const uint64_t hstride = nunits * a.slot;  // message h+1 of a unit sits hstride bytes after message h
@@ -212,6 +215,31 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
         }
         return *dst;
       }
+      if constexpr (kH16) {
+        // exponent byte and mantissas of the lane's group, decoded packed
+        const uint8_t* pay = m + 16;
+        u32x2 w = {0u, 0u};
+        uint32_t E = 0;
+        if (nv > 0) {
+          const uint64_t o = off(g);
+          E = pay[o / 128];
+          const uint8_t* mp = pay + eb + (mbits > 4 ? o : o / 2);
+          if (nv == 8) {
+            if (mbits > 4) w = *(const u32x2*)mp;
+            else w[0] = *(const uint32_t*)mp;
+          } else if (mbits > 4) {
+            for (int i = 0; i < nv; ++i) w[i >> 2] |= (uint32_t)mp[i] << (8 * (i & 3));
+          } else {
+            for (int i = 0; i < (nv + 1) / 2; ++i) w[0] |= (uint32_t)mp[i] << (8 * i);
+          }
+        }
+        const u32x4 d = dec_h16x8(E, w, mbits);
+        Raw8<DT> r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.w[0][i] = acc ? h2_bits(as_h2(xr.w[0][i]) + as_h2(d[i])) : d[i];
+        r.w[0] = keep_h16x8(r.w[0], nv);
+        return r;
+      }
       const G8 d = nv > 0 ? dequant_group(m + 16, eb, off(g), nv, block, mbits) : G8{};
       const G8 x = unpack8<DT>(xr);
       G8 r;
@@ -225,7 +253,8 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
     for (int g = 0; g < GP; ++g) {
       const Raw8<DT> x = load(ring(c, 1), g);
       P[slot(g)] = x;
-      lane_nnz += nonzeros<DT>(unpack8<DT>(x), nvof(g));
+      if constexpr (kH16) lane_nnz += nonzeros_h16x8(x.w[0]);
+      else lane_nnz += nonzeros<DT>(unpack8<DT>(x), nvof(g));
     }
     for (int h = 1; h <= N; ++h) {
       uint8_t* msg = msg1 + (uint64_t)(h - 1) * hstride;
@@ -238,7 +267,8 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
         for (int g = 0; g < GP; ++g) {
           const Raw8<DT> p = decode_own(msg - hstride, g, load(r, g), true);
           P[slot(g)] = p;
-          lane_nnz += nonzeros<DT>(unpack8<DT>(p), nvof(g));
+          if constexpr (kH16) lane_nnz += nonzeros_h16x8(p.w[0]);
+          else lane_nnz += nonzeros<DT>(unpack8<DT>(p), nvof(g));
         }
       }
       uint32_t tile_nnz, unused;
@@ -349,8 +379,26 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
         uint8_t* payload = msg + 16;
         if (k == 0 && threadIdx.x < eb - nb) payload[nb + threadIdx.x] = 0;  // exponent padding
 #pragma unroll 2
-        for (int g = 0; g < GP; ++g)
-          encode_group<DT, LPB>(unpack8<DT>(P[slot(g)]), nvof(g), off(g), payload, payload + eb, lpb, mbits, qmax);
+        for (int g = 0; g < GP; ++g) {
+          if constexpr (kH16) {
+            const H16Code q = enc_h16x8(P[slot(g)].w[0], mbits);
+            const int nv = nvof(g);
+            if (nv == 0) continue;
+            const uint64_t o = off(g);
+            if ((threadIdx.x & 15u) == 0) payload[o / 128] = (uint8_t)q.E;
+            uint8_t* mp = payload + eb + (mbits > 4 ? o : o / 2);
+            if (nv == 8) {
+              if (mbits > 4) *(u32x2*)mp = q.bytes;
+              else *(uint32_t*)mp = q.bytes[0];
+            } else if (mbits > 4) {
+              for (int i = 0; i < nv; ++i) mp[i] = (uint8_t)(q.bytes[i >> 2] >> (8 * (i & 3)));
+            } else {
+              for (int i = 0; i < (nv + 1) / 2; ++i) mp[i] = (uint8_t)(q.bytes[0] >> (8 * i));
+            }
+          } else {
+            encode_group<DT, LPB>(unpack8<DT>(P[slot(g)]), nvof(g), off(g), payload, payload + eb, lpb, mbits, qmax);
+          }
+        }
       }
       sp_prev = sparse;
       tot_prev = total;
@@ -384,7 +432,9 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 // (32 KiB of partials plus 4 KiB of entry positions in LDS, four workgroups
 // per CU) or 8192 binary32 elements (the same 32 KiB).
 // Measured on MI355X (N = 8 x 64M fp16, 4 MiB units, ranks 0-3 95% zeros):
-// 0.888 ms.  Loading the next receiver's copy straight into a second LDS
+// 0.888 ms with the binary32 codec, 0.845 ms with the packed binary16 one
+// (77 instead of 112 VGPRs).  Holding the next receiver's copy in registers
+// during the message write needs 140-250 VGPRs (half the occupancy).  Loading the next receiver's copy straight into a second LDS
 // buffer a hop ahead (global_load_lds) measured slower, 0.965 ms at 8192-
 // element tiles and 1.21 ms at 16384: the extra buffer halves the units the
 // chip holds at once, and the rounds of hops cost more than the latency it

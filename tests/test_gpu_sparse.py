@@ -10,7 +10,7 @@ import oracle
 import ring_all_reduce_scatter_amd as rar
 from ring_all_reduce_scatter_amd import inputs
 
-from gpu_util import DT_NAMES, assert_bits_equal, to_dev, to_host
+from gpu_util import DT_NAMES, assert_bits_equal, nan_mask, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -230,3 +230,39 @@ def test_pipelined_sparse_messages_match_oracle(dt):
     oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=mbits, unit=U, dt=odt)
     for r, g in enumerate(to_host(bufs, dt)):
         assert_bits_equal(g, ref[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("mbits", [4, 8])
+def test_pipelined_sparse_special_values_match_oracle(dt, mbits):
+    """Sparse and BFP units holding Inf, NaN, subnormals and the largest
+    binary16 values, with a ragged last chunk, through the pipelined
+    SPARSE_AUTO ring: results equal the oracle's (NaN where the oracle has
+    NaN), and so do the byte counters."""
+    n, U = 4, 4096
+    count = n * 2 * U + 700
+    g = np.random.default_rng(100 + mbits)
+    xs = []
+    for r in range(n):
+        x = (g.standard_normal(count) * 1e-2).astype(np.float32)
+        if r < 2:  # sparse ranks: the first hops of their chunks go as values + indices
+            x[g.random(count) < 0.97] = 0.0
+        x[0:128] = 0.0
+        x[128:256] = np.float32(6.0e-8) * g.integers(-3, 4, 128)  # binary16 subnormals
+        x[256:384] = np.float32(65504.0) * np.sign(g.standard_normal(128)).astype(np.float32) / n
+        if r == 1:
+            x[384 + 5] = np.inf          # in a sparse rank's values
+            x[3 * U + 9] = -np.inf
+        if r == 3:
+            x[2 * U + 7] = np.nan        # in a dense unit
+            x[count - 3] = np.nan        # in the ragged tail
+        xs.append(inputs.cast(x, dt))
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=mbits, unit=U,
+                                                    dt=DT_NAMES[dt])
+    got, sent, recv = _run_auto(xs, dt, mbits=mbits, unit_elems=U, sched="pipelined")
+    for r in range(n):
+        nan = nan_mask(ref[r], dt)
+        assert np.array_equal(nan_mask(got[r], dt), nan), f"rank {r} NaN positions"
+        assert_bits_equal(got[r][~nan], ref[r][~nan], f"rank {r}")
+    assert sent == osent and recv == orecv
