@@ -127,22 +127,18 @@ struct SpPipeArgs {
 };
 
 // Dynamic LDS of one workgroup: the tile's partial sums as stored (group g of
-// lane l at [g * 256 + l]), then each lane's first entry in the last sparse
-// message, per group, relative to the tile's first entry (uint16: a tile has
-// at most 16384 entries... see kSpGroups).
+// lane l at [g * 256 + l], i.e. the tile's elements in order).
 template <int DT, int GP>
 constexpr size_t sp_lds_bytes() {
-  return (size_t)GP * kThreads * sizeof(Raw8<DT>) + (size_t)GP * kThreads * sizeof(uint16_t);
+  return (size_t)GP * kThreads * sizeof(Raw8<DT>);
 }
 
 template <int DT, int LPB, int GP>
 __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
   constexpr uint32_t ES = DtypeSize<DT>::value;
   constexpr uint64_t kTile = (uint64_t)kThreads * kGroupElems * GP;
-  static_assert(kTile <= 65535, "entry positions inside a tile are 16-bit");
   extern __shared__ __align__(16) unsigned char sp_lds[];
   Raw8<DT>* P = (Raw8<DT>*)sp_lds;
-  uint16_t* POS = (uint16_t*)(P + GP * kThreads);
   const int N = a.nranks;
   const int lpb = LPB > 0 ? LPB : a.lpb;
   const int mbits = a.mbits;
@@ -190,31 +186,11 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
     bool sp_prev = false;
     uint32_t tot_prev = 0, tile_first = 0, tile_cnt = 0;
 
-    // The lane's group g of message m, decoded: acc = true adds it to xr
+    // The lane's group g of BFP message m, decoded: acc = true adds it to xr
     // (local + received, as the receiver of a reduce-scatter hop), acc =
-    // false gives the value itself (allgather: zero, then scatter).  A
-    // sparse message's entries are scattered into the lane's LDS slot.
+    // false gives the value itself (allgather).
     auto decode_own = [&](const uint8_t* m, int g, const Raw8<DT>& xr, bool acc) -> Raw8<DT> {
       const int nv = nvof(g);
-      if (sp_prev) {
-        const int sl = slot(g);
-        Raw8<DT>* dst = &P[sl];
-        Raw8<DT> z;
-#pragma unroll
-        for (int w = 0; w < (int)(sizeof(z) / 16); ++w) z.w[w] = (u32x4){0u, 0u, 0u, 0u};
-        *dst = acc ? xr : z;
-        const uint8_t* vals = m + 16;
-        const uint32_t* idx = (const uint32_t*)(m + 16 + round16((uint64_t)tot_prev * ES));
-        const uint32_t b = POS[sl], e = sl + 1 < GP * kThreads ? POS[sl + 1] : tile_cnt;
-        for (uint32_t j = b; j < e; ++j) {
-          const uint32_t q = tile_first + j;
-          const uint32_t raw = ES == 4 ? ((const uint32_t*)vals)[q] : (uint32_t)((const uint16_t*)vals)[q];
-          const int i = (int)((idx[q] - (uint32_t)off(g)) & 7u);
-          lds_set<DT>(dst, i, acc ? raw_bits<DT>(round_to<DT>(from_raw<DT>(lds_elem<DT>(dst, i)) + from_raw<DT>(raw)))
-                                  : raw);
-        }
-        return *dst;
-      }
       if constexpr (kH16) {
         // exponent byte and mantissas of the lane's group, decoded packed
         const uint8_t* pay = m + 16;
@@ -248,6 +224,36 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
       return pack8<DT>(r);
     };
 
+    // This tile's entries of sparse message m, added to (acc) or stored into
+    // the partials in LDS, which hold the tile's elements in order (group g
+    // of lane l is elements (g * 256 + l) * 8 ..).  The entries are one
+    // contiguous run of the message, so the workgroup loads them coalesced,
+    // four per lane at a time; their indices are distinct, so no two lanes
+    // touch one element.  Every lane calls this between two barriers.
+    auto scatter_sparse = [&](const uint8_t* m, bool acc) {
+      const uint8_t* vals = m + 16;
+      const uint32_t* idx = (const uint32_t*)(m + 16 + round16((uint64_t)tot_prev * ES));
+      const uint32_t base = k * (uint32_t)kTile;  // unit-relative first element of the tile
+      for (uint32_t j0 = threadIdx.x; j0 < tile_cnt; j0 += 4 * kThreads) {
+        uint32_t raw[4], e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t j = j0 + (uint32_t)t * kThreads;
+          const uint32_t q = tile_first + (j < tile_cnt ? j : 0u);
+          raw[t] = ES == 4 ? ((const uint32_t*)vals)[q] : (uint32_t)((const uint16_t*)vals)[q];
+          e[t] = j < tile_cnt ? idx[q] - base : (uint32_t)kTile;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (e[t] >= (uint32_t)kTile) continue;
+          Raw8<DT>* grp = &P[e[t] >> 3];
+          const int i = (int)(e[t] & 7u);
+          lds_set<DT>(grp, i, acc ? raw_bits<DT>(round_to<DT>(from_raw<DT>(lds_elem<DT>(grp, i)) + from_raw<DT>(raw[t])))
+                                  : raw[t]);
+        }
+      }
+    };
+
     uint32_t lane_nnz = 0;
 #pragma unroll 4
     for (int g = 0; g < GP; ++g) {
@@ -263,12 +269,26 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
         wave_stores_done();
         lane_nnz = 0;
         const int r = ring(c, h);
+        if (sp_prev) {
+          // the receiver's copy, then the entries (see the allgather below)
+#pragma unroll 4
+          for (int g = 0; g < GP; ++g) P[slot(g)] = load(r, g);
+          __syncthreads();
+          scatter_sparse(msg - hstride, true);
+          __syncthreads();
+#pragma unroll 4
+          for (int g = 0; g < GP; ++g) {
+            if constexpr (kH16) lane_nnz += nonzeros_h16x8(P[slot(g)].w[0]);
+            else lane_nnz += nonzeros<DT>(unpack8<DT>(P[slot(g)]), nvof(g));
+          }
+        } else {
 #pragma unroll 2
-        for (int g = 0; g < GP; ++g) {
-          const Raw8<DT> p = decode_own(msg - hstride, g, load(r, g), true);
-          P[slot(g)] = p;
-          if constexpr (kH16) lane_nnz += nonzeros_h16x8(p.w[0]);
-          else lane_nnz += nonzeros<DT>(unpack8<DT>(p), nvof(g));
+          for (int g = 0; g < GP; ++g) {
+            const Raw8<DT> p = decode_own(msg - hstride, g, load(r, g), true);
+            P[slot(g)] = p;
+            if constexpr (kH16) lane_nnz += nonzeros_h16x8(p.w[0]);
+            else lane_nnz += nonzeros<DT>(unpack8<DT>(p), nvof(g));
+          }
         }
       }
       uint32_t tile_nnz, unused;
@@ -355,7 +375,6 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
           uint32_t m = nz_mask<DT>(x, nvof(g));
           uint32_t gtot;
           const uint32_t lpos = rel + block_exclusive_scan((uint32_t)__builtin_popcount(m), &gtot);
-          POS[slot(g)] = (uint16_t)lpos;
           uint32_t q = before + lpos;
           const uint32_t o = (uint32_t)off(g);
           for (; m; m &= m - 1, ++q) {  // ascending element order
@@ -374,7 +393,6 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
           const uint64_t pad0 = 16 + (uint64_t)total * ES, pad1 = 16 + round16((uint64_t)total * ES);
           if (pad0 + threadIdx.x < pad1) msg[pad0 + threadIdx.x] = 0;
         }
-        __syncthreads();  // every lane's POS is written before any lane reads its neighbour's
       } else {
         uint8_t* payload = msg + 16;
         if (k == 0 && threadIdx.x < eb - nb) payload[nb + threadIdx.x] = 0;  // exponent padding
@@ -406,10 +424,22 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
     // allgather: every rank (owner included) stores the owner's message decoded
     wave_stores_done();
     const uint8_t* last = msg1 + (uint64_t)(N - 1) * hstride;
+    if (sp_prev) {
+      // zeros, then the entries (written by every wavefront of the workgroup:
+      // the barrier orders their completed stores before these loads)
+      Raw8<DT> z;
+#pragma unroll
+      for (int w = 0; w < (int)(sizeof(z) / 16); ++w) z.w[w] = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll 4
+      for (int g = 0; g < GP; ++g) P[slot(g)] = z;
+      __syncthreads();
+      scatter_sparse(last, false);
+      __syncthreads();
+    }
 #pragma unroll 2
     for (int g = 0; g < GP; ++g) {
       const int nv = nvof(g);
-      const Raw8<DT> yr = decode_own(last, g, Raw8<DT>{}, false);
+      const Raw8<DT> yr = sp_prev ? P[slot(g)] : decode_own(last, g, Raw8<DT>{}, false);
       if (full) {
         for (int d = 0; d < N; ++d) store_raw8<DT, true>(a.bufs.p[d], ulo + off(g), yr);
       } else if (nv > 0) {
@@ -417,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
         for (int d = 0; d < N; ++d) store_part8<DT>(a.bufs.p[d], ulo + off(g), nv, y);
       }
     }
-    // the next unit's first hop reuses s_dec, P, POS and the scans' LDS
+    // the next unit's first hop reuses s_dec, P and the scans' LDS
     // only after barriers every lane passes after its last read of them
     __syncthreads();
   }
@@ -429,12 +459,14 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 }
 
 // 8-element groups per lane: tiles of 16384 binary16 / bfloat16 elements
-// (32 KiB of partials plus 4 KiB of entry positions in LDS, four workgroups
-// per CU) or 8192 binary32 elements (the same 32 KiB).
+// or 8192 binary32 elements (32 KiB of partials in LDS, five workgroups per
+// CU).
 // Measured on MI355X (N = 8 x 64M fp16, 4 MiB units, ranks 0-3 95% zeros):
-// 0.888 ms with the binary32 codec, 0.845 ms with the packed binary16 one
-// (77 instead of 112 VGPRs).  Holding the next receiver's copy in registers
-// during the message write needs 140-250 VGPRs (half the occupancy).  Loading the next receiver's copy straight into a second LDS
+// 0.888 ms with the binary32 codec and each lane decoding its own sparse
+// entries one dependent load at a time, 0.845 ms with the packed binary16
+// codec (77 instead of 112 VGPRs).  Holding the next receiver's copy in
+// registers during the message write needs 140-250 VGPRs (half the
+// occupancy).  Loading the next receiver's copy straight into a second LDS
 // buffer a hop ahead (global_load_lds) measured slower, 0.965 ms at 8192-
 // element tiles and 1.21 ms at 16384: the extra buffer halves the units the
 // chip holds at once, and the rounds of hops cost more than the latency it
@@ -465,8 +497,8 @@ const void* sp_kernel_for(int dt) {
   }
 }
 
-// Units in flight: as many whole gangs of kmax workgroups as fit on the
-// device at once (0 when one unit's tiles cannot all be resident).
+// Units in flight: whole gangs of kmax workgroups that fit on the device at
+// once (0 when one unit's tiles cannot all be resident).
 hipError_t sp_gangs(const void* fn, size_t lds, uint64_t kmax, uint64_t nunits, uint64_t* gangs) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e;
@@ -476,6 +508,12 @@ hipError_t sp_gangs(const void* fn, size_t lds, uint64_t kmax, uint64_t nunits, 
   const uint64_t capacity = (uint64_t)cus * (uint64_t)per_cu;
   uint64_t g = kmax ? capacity / kmax : 0;
   if (g > nunits) g = nunits;
+  // as few gangs as give the same number of rounds of units (each round
+  // runs its hops in lock step, so a last, partly filled round costs a full one)
+  if (g > 0) {
+    const uint64_t rounds = (nunits + g - 1) / g;
+    g = (nunits + rounds - 1) / rounds;
+  }
   *gangs = g;
   return hipSuccess;
 }
