@@ -459,18 +459,29 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 }
 
 // 8-element groups per lane: tiles of 16384 binary16 / bfloat16 elements
-// or 8192 binary32 elements (32 KiB of partials in LDS, five workgroups per
-// CU).
+// or 8192 binary32 elements (32 KiB of partials in LDS; with the small
+// static arrays four workgroups fit in a CU's 160 KiB, not five).
 // Measured on MI355X (N = 8 x 64M fp16, 4 MiB units, ranks 0-3 95% zeros):
 // 0.888 ms with the binary32 codec and each lane decoding its own sparse
 // entries one dependent load at a time, 0.845 ms with the packed binary16
-// codec (77 instead of 112 VGPRs).  Holding the next receiver's copy in
+// codec (77 instead of 112 VGPRs), 0.786 ms with the workgroup decoding the
+// sparse entries together.  Per hop of a unit (timestamps of the first
+// unit of each tile): decode 7-10 us, learning the decision 2.4-3.3 us
+// (BFP) or 7-12 us (sparse: every count must be in), message write 3-7 us;
+// the allgather 34 us.  Holding the next receiver's copy in
 // registers during the message write needs 140-250 VGPRs (half the
 // occupancy).  Loading the next receiver's copy straight into a second LDS
 // buffer a hop ahead (global_load_lds) measured slower, 0.965 ms at 8192-
 // element tiles and 1.21 ms at 16384: the extra buffer halves the units the
 // chip holds at once, and the rounds of hops cost more than the latency it
 // hides.  Unrolling the decode loop 4-fold instead of 2 changed nothing.
+// Other measured variants: a decision word per tile (256 bytes apart, so no
+// two waiting tiles read one word) 0.789 ms, no gain; two units per
+// workgroup half a hop apart (8192-element tiles) 0.810 ms, because the
+// count's atomic round trip still holds the workgroup before the other
+// unit's work; the same with the tiles reading the arrival word for the
+// decision instead of a decision word 1.39 ms (the reads queue with the
+// adds on that word).
 template <int DT>
 struct SpGroups {
   static constexpr int value = DT == DT_F32 ? 4 : 8;
