@@ -436,21 +436,13 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_f32q_kernel(RankPtrs b
 //   delta:          v = p - ref, send E(v), ref <- ref + D(E(v)) = value the
 //                   receiver gets
 // The hop chain of a block is the one of bfp_ring_fold_kernel with v in place
-// of p at every encode, in binary32.
-// Orders LDS writes and reads among the lanes of one wavefront: each
-// wavefront only exchanges data inside its own 512-element slice of the tile,
-// so no workgroup barrier is needed.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int DT, int NR, int LPB, int FB>
+// of p at every encode, in binary32.  This kernel takes any N, one hop's
+// loads at a time; N = 4 and 8 run bfp_ring_fold_state_q_kernel below.
+template <int DT, int LPB, int FB>
 __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs bufs, RankPtrs st, int nranks,
                                                                         uint64_t count, uint64_t L, int lpb_rt,
                                                                         int mbits) {
-  const int N = NR > 0 ? NR : nranks;
+  const int N = nranks;
   const int lpb = LPB > 0 ? LPB : lpb_rt;
   const uint32_t c = blockIdx.x % (uint32_t)N;
   const uint32_t t = blockIdx.x / (uint32_t)N;
@@ -495,91 +487,7 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs 
   // ring order of chunk c: ranks c+1, ..., c+N-1 send their partials in the
   // reduce-scatter, c is the receiver of the last hop and the allgather owner
   const int first = (int)c + 1 < N ? (int)c + 1 : 0;
-  if constexpr (NR > 0) {
-    // Every load is issued before the chain (16-bit inputs stay packed until
-    // their hop: half the registers).  The state goes through LDS: a
-    // wavefront moves it with 16-byte lanes over 1 KiB of contiguous memory
-    // per instruction (lane l: floats 4l..4l+3 and 256+4l..), and LDS hands
-    // each lane its 8 consecutive floats.  Loading 8 consecutive floats per
-    // lane straight from memory splits every instruction into 16-byte pieces
-    // 32 bytes apart, which MI355X's HBM serves measurably slower.
-    extern __shared__ __align__(16) float lds_state[];  // [NR][tile of 2048 floats]
-    constexpr int kTileElems = kThreads * kGroupElems;
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t w0 = (threadIdx.x & ~63u) * kGroupElems;  // wavefront's first element in the tile
-    const uint32_t qa = w0 + 4 * lane, qb = qa + 256;            // the lane's two quads in the tile
-    auto quad_n = [&](uint32_t q) { const uint64_t g = tile0 + q; return g >= hi ? 0 : (hi - g >= 4 ? 4 : (int)(hi - g)); };
-    const int na = quad_n(qa), nb = quad_n(qb);
-    auto gload_quad = [&](const char* base, uint32_t q, int nq) -> u32x4 {
-      if (nq == 4) return ld16<true>(base + (tile0 + q) * 4);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      for (int i = 0; i < nq; ++i) v[i] = ((const uint32_t*)base)[tile0 + q + i];
-      return v;
-    };
-    auto gstore_quad = [&](char* base, uint32_t q, int nq, const u32x4& v) {
-      if (nq == 4) st16<true>(base + (tile0 + q) * 4, v);
-      else
-        for (int i = 0; i < nq; ++i) ((uint32_t*)base)[tile0 + q + i] = v[i];
-    };
-    Raw8<DT> x[NR];
-    u32x4 sa[NR], sb[NR];
-    G8 s[NR];
-    auto rank_of = [&](int j) { return first + j < NR ? first + j : first + j - NR; };
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const int q = rank_of(j);
-      x[j] = nv == 8 ? load_raw8<DT, true>(bufs.p[q], e) : pack8<DT>(load_part8<DT>(bufs.p[q], e, nv));
-      sa[j] = gload_quad(st.p[q], qa, na);
-      sb[j] = gload_quad(st.p[q], qb, nb);
-    }
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      *(u32x4*)&lds_state[j * kTileElems + qa] = sa[j];
-      *(u32x4*)&lds_state[j * kTileElems + qb] = sb[j];
-    }
-    wave_lds_sync();
-    const uint32_t mine = threadIdx.x * kGroupElems;  // the lane's 8 consecutive elements
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const u32x4 lo4 = *(const u32x4*)&lds_state[j * kTileElems + mine];
-      const u32x4 hi4 = *(const u32x4*)&lds_state[j * kTileElems + mine + 4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[j].v[i] = __uint_as_float(lo4[i]);
-        s[j].v[4 + i] = __uint_as_float(hi4[i]);
-      }
-    }
-    G8 p = unpack8<DT>(x[0]);
-#pragma unroll
-    for (int j = 1; j < NR; ++j) {
-      const G8 d = message(p, s[j - 1]);
-      const G8 xj = unpack8<DT>(x[j]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p.v[i] = round_to<DT>(xj.v[i] + d.v[i]);
-    }
-    const G8 y = message(p, s[NR - 1]);
-#pragma unroll
-    for (int j = 0; j < NR; ++j) store_group<DT>(bufs.p[j], e, nv, y);
-    wave_lds_sync();  // every lane of the wavefront has read its state from LDS
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      u32x4 lo4, hi4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo4[i] = __float_as_uint(s[j].v[i]);
-        hi4[i] = __float_as_uint(s[j].v[4 + i]);
-      }
-      *(u32x4*)&lds_state[j * kTileElems + mine] = lo4;
-      *(u32x4*)&lds_state[j * kTileElems + mine + 4] = hi4;
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const int q = rank_of(j);
-      gstore_quad(st.p[q], qa, na, *(const u32x4*)&lds_state[j * kTileElems + qa]);
-      gstore_quad(st.p[q], qb, nb, *(const u32x4*)&lds_state[j * kTileElems + qb]);
-    }
-  } else {
+  {
     G8 p = ld(first);
     int r = first;
     for (int k = 2; k <= N; ++k) {
@@ -596,6 +504,184 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_kernel(RankPtrs 
     const G8 y = message(p, s);
     st_state((int)c, s);
     for (int d = 0; d < N; ++d) store_group<DT>(bufs.p[d], e, nv, y);
+  }
+}
+
+// Stateful fused ring, quad layout (N = 4 or 8 ranks known at compile
+// time, every rank's inputs and state loaded before the chain): the
+// arithmetic of bfp_ring_fold_state_kernel element for element, with the
+// lanes laid out as in bfp_ring_fold_f32q_kernel.  A wavefront owns
+// 512 consecutive elements; lane l holds [4l, 4l+4) ("A") and [256+4l,
+// 256+4l+4) ("B"), so each load or store instruction covers contiguous
+// memory for the 16-bit inputs (8 bytes a lane) and for the binary32 state
+// (16 bytes a lane) alike, with no LDS staging.  A block of b <= 256
+// elements is b/4 consecutive lanes of one set; a 512-element block is the
+// whole wavefront.
+template <int DT, int NR, int LPBQ, int FB>
+__global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_q_kernel(RankPtrs bufs, RankPtrs st, uint64_t count,
+                                                                          uint64_t L, int block, int mbits) {
+  constexpr int N = NR;
+  constexpr int ES = DtypeSize<DT>::value;
+  const uint32_t c = blockIdx.x % (uint32_t)N;
+  const uint32_t t = blockIdx.x / (uint32_t)N;
+  const uint64_t lo = (uint64_t)c * L;
+  if (lo >= count) return;
+  const uint64_t hi = lo + L < count ? lo + L : count;
+  const uint64_t tile0 = lo + (uint64_t)t * kThreads * kGroupElems;
+  if (tile0 >= hi) return;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t eA = tile0 + (uint64_t)(threadIdx.x >> 6) * 512 + 4 * lane, eB = eA + 256;
+  auto nq = [&](uint64_t e) { return e >= hi ? 0 : (hi - e >= 4 ? 4 : (int)(hi - e)); };
+  const int nA = nq(eA), nB = nq(eB);
+  const int lpbq = LPBQ > 0 ? LPBQ : (block >= 256 ? 64 : block / 4);
+  const bool whole = block == 512;
+  const float qmax = (float)((1 << (mbits - 1)) - 1);
+
+  // raw quads: 16-bit inputs as 2 words, binary32 (inputs or state) as 4
+  typedef typename std::conditional<ES == 2, u32x2, u32x4>::type XQ;
+  auto ld_x = [&](int rank, uint64_t e, int nv) -> XQ {
+    const char* base = bufs.p[rank];
+    XQ w = {};
+    if (nv == 4) {
+      if constexpr (ES == 2) w = __builtin_nontemporal_load((const u32x2*)(base + e * 2));
+      else w = ld16<true>(base + e * 4);
+    } else if constexpr (ES == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nv) w[i >> 1] |= (uint32_t)((const uint16_t*)base)[e + i] << (16 * (i & 1));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nv) w[i] = ((const uint32_t*)base)[e + i];
+    }
+    return w;
+  };
+  auto x_val = [&](const XQ& w, int i) -> float {
+    if constexpr (ES == 2) return widen16<DT>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+    else return __uint_as_float(w[i]);
+  };
+  auto ld_s = [&](int rank, uint64_t e, int nv) -> u32x4 {
+    const char* base = st.p[rank];
+    if (nv == 4) return ld16<true>(base + e * 4);
+    u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < nv) w[i] = ((const uint32_t*)base)[e + i];
+    return w;
+  };
+  auto st_f32 = [&](char* base, uint64_t e, int nv, const float* v) {
+    if (nv == 4) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+      st16<true>(base + e * 4, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nv) ((float*)base)[e + i] = v[i];
+    }
+  };
+  auto st_s = [&](int rank, uint64_t e, int nv, const float* v) { st_f32(st.p[rank], e, nv, v); };
+  auto st_y = [&](int rank, uint64_t e, int nv, const float* v) {
+    char* base = bufs.p[rank];
+    if constexpr (ES == 2) {
+      if (nv == 4) {
+        u32x2 w;
+        w[0] = narrow16<DT>(v[0]) | narrow16<DT>(v[1]) << 16;
+        w[1] = narrow16<DT>(v[2]) | narrow16<DT>(v[3]) << 16;
+        __builtin_nontemporal_store(w, (u32x2*)(base + e * 2));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nv) ((uint16_t*)base)[e + i] = (uint16_t)narrow16<DT>(v[i]);
+      }
+    } else {
+      st_f32(base, e, nv, v);
+    }
+  };
+  // Encode v = p +- s, update the sender's state s in place, return what the
+  // receiver takes (the hop of bfp_ring_fold_state_kernel).
+  auto message = [&](const Q8& p, Q8& s) -> Q8 {
+    Q8 v, out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v.v[i] = FB == 1 ? p.v[i] + s.v[i] : p.v[i] - s.v[i];
+    uint32_t ma = 0, mb = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ma = max(ma, absbits(v.v[i]));
+      mb = max(mb, absbits(v.v[4 + i]));
+    }
+    if (whole) {
+      ma = mb = group_max_u32<64>(max(ma, mb));
+    } else {
+      ma = group_max_sel<LPBQ>(ma, lpbq);
+      mb = group_max_sel<LPBQ>(mb, lpbq);
+    }
+    const BfpScale sa = bfp_scale(ma, mbits), sb = bfp_scale(mb, mbits);
+    const float nanv = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const BfpScale& sc = i < 4 ? sa : sb;
+      const float d = sc.nan ? nanv : bfp_dq(bfp_q(v.v[i], sc.k, qmax), sc.k);
+      if (FB == 1) {
+        s.v[i] = v.v[i] - d;
+        out.v[i] = d;
+      } else {
+        s.v[i] = s.v[i] + d;
+        out.v[i] = s.v[i];
+      }
+    }
+    return out;
+  };
+  // ring order of chunk c: ranks c+1, ..., c+N-1 send their partials in the
+  // reduce-scatter, c is the receiver of the last hop and the allgather owner
+  const int first = (int)c + 1 < N ? (int)c + 1 : 0;
+  auto rank_of = [&](int j) { return first + j < N ? first + j : first + j - N; };
+  XQ xa[NR], xb[NR];
+  u32x4 sa[NR], sb[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int q = rank_of(j);
+    xa[j] = ld_x(q, eA, nA);
+    xb[j] = ld_x(q, eB, nB);
+    sa[j] = ld_s(q, eA, nA);
+    sb[j] = ld_s(q, eB, nB);
+  }
+  auto state_of = [&](int j) -> Q8 {
+    Q8 s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s.v[i] = __uint_as_float(sa[j][i]);
+      s.v[4 + i] = __uint_as_float(sb[j][i]);
+    }
+    return s;
+  };
+  Q8 p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p.v[i] = x_val(xa[0], i);
+    p.v[4 + i] = x_val(xb[0], i);
+  }
+#pragma unroll
+  for (int j = 1; j < NR; ++j) {
+    Q8 s = state_of(j - 1);
+    const Q8 d = message(p, s);
+    st_s(rank_of(j - 1), eA, nA, s.v);
+    st_s(rank_of(j - 1), eB, nB, s.v + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p.v[i] = round_to<DT>(x_val(xa[j], i) + d.v[i]);
+      p.v[4 + i] = round_to<DT>(x_val(xb[j], i) + d.v[4 + i]);
+    }
+  }
+  Q8 s = state_of(NR - 1);
+  const Q8 y = message(p, s);
+  st_s(rank_of(NR - 1), eA, nA, s.v);
+  st_s(rank_of(NR - 1), eB, nB, s.v + 4);
+#pragma unroll
+  for (int d = 0; d < N; ++d) {
+    st_y(d, eA, nA, y.v);
+    st_y(d, eB, nB, y.v + 4);
   }
 }
 
@@ -683,10 +769,13 @@ void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, i
   }
 }
 
-// Workgroups per CU of the stateful fold.  Each lane holds N inputs and N
-// state groups in flight (N = 8, fp16: 384 bytes); two workgroups per CU
-// measured best on MI355X (2.47 ms vs 2.60 uncapped and 2.52 at three for
-// N = 8, 128M fp16 with 128M-float state per rank).
+// Workgroups per CU of the stateful fold.  Each lane of the quad-layout
+// kernel holds N inputs and N state quads in flight (N = 8, fp16: 384
+// bytes, 96 KiB a workgroup).  Two workgroups per CU measured best on
+// MI355X (N = 8, 128M fp16 with 128M-float state per rank: 2.24-2.25 ms,
+// 0.715-0.720 of 8 TB/s; 3.0-3.1 ms at one, 2.28 ms at three, 2.32 ms
+// uncapped at four), and so for the generic-N kernel (2.47 ms vs 2.60
+// uncapped and 2.52 at three, measured with an earlier LDS-staged layout).
 int state_fold_wgs_per_cu() { return 2; }
 
 template <int DT, int NR, int FB>
@@ -695,17 +784,22 @@ void fold_state_dispatch_nr(const RankPtrs& bufs, const RankPtrs& st, int n, uin
   const uint64_t tile = (uint64_t)kThreads * kGroupElems;
   const uint64_t tiles = (L + tile - 1) / tile;
   dim3 grid((unsigned)((uint64_t)n * tiles));
-  // NR > 0 stages the tile's state through LDS (NR * 8 KiB), which also
-  // bounds the workgroups per CU
-  size_t lds = residency_lds(state_fold_wgs_per_cu());
-  if (NR > 0 && lds < (size_t)NR * kThreads * kGroupElems * sizeof(float))
-    lds = (size_t)NR * kThreads * kGroupElems * sizeof(float);
-  if (block == 128)
-    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, NR, 16, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
-                       n, count, L, 16, mbits);
-  else
-    hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, NR, 0, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
-                       n, count, L, block / 8, mbits);
+  const size_t lds = residency_lds(state_fold_wgs_per_cu());
+  if constexpr (NR > 0) {
+    if (block == 128)
+      hipLaunchKernelGGL((bfp_ring_fold_state_q_kernel<DT, NR, 32, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
+                         count, L, block, mbits);
+    else
+      hipLaunchKernelGGL((bfp_ring_fold_state_q_kernel<DT, NR, 0, FB>), grid, dim3(kThreads), lds, stream, bufs, st,
+                         count, L, block, mbits);
+  } else {
+    if (block == 128)
+      hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, 16, FB>), grid, dim3(kThreads), lds, stream, bufs, st, n,
+                         count, L, 16, mbits);
+    else
+      hipLaunchKernelGGL((bfp_ring_fold_state_kernel<DT, 0, FB>), grid, dim3(kThreads), lds, stream, bufs, st, n,
+                         count, L, block / 8, mbits);
+  }
 }
 
 template <int DT, int FB>
