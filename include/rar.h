@@ -431,11 +431,13 @@ int rar_ring_allreduce_ft(void* const* bufs, int nranks, size_t count, int dtype
 size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t cap_bytes,
                        int* bucket_of);
 
-/* Workspace for rar_bucketed_allreduce(_ex) (0 on bad args).
+/* Workspace for rar_bucketed_allreduce(_ex) and rar_bucketed_prepare (0 on
+ * bad args).
  * FUSED: the launch table, 8 * (2 + 5*nbuckets + (2 + nranks)*ntensors)
- * bytes rounded up to 256, then 16 bytes per workgroup of the fold launch
- * (nranks * ceil(L_b / tile) per bucket b, L_b its chunk length; tile =
- * 2048 elements for f32 and bf16, 4096 for f16), rounded up to 256.
+ * bytes rounded up to 256, then a descriptor of roundup(16 + 8*nranks, 16)
+ * bytes per workgroup of the fold launch (nranks * ceil(L_b / tile) per
+ * bucket b, L_b its chunk length; tile = 2048 elements for f32 and bf16,
+ * 4096 for f16), rounded up to 256.
  * STEPWISE: nranks flat buffers of the largest padded bucket. */
 size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
                                     size_t cap_bytes);
@@ -458,6 +460,37 @@ int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t nt
 int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t ntensors,
                               int nranks, int dtype, size_t cap_bytes, int algo, void* workspace,
                               size_t ws_bytes, void* stream);
+
+/* A bucketed allreduce prepared once and launched many times (a training
+ * loop reduces the same gradient tensors every step).  Plain data owned by
+ * the caller; filled by rar_bucketed_prepare. */
+typedef struct {
+  void* workspace;                /* the prepared workspace */
+  uint64_t desc_offset;           /* bytes from workspace to the fold descriptors */
+  uint64_t grid;                  /* fold workgroups (0: nothing to launch) */
+  uint64_t ntensors;
+  int nranks;
+  int dtype;
+  uint64_t sent[RAR_MAX_RANKS];   /* byte counters of one call (rar_last_traffic) */
+  uint64_t recv[RAR_MAX_RANKS];
+} rar_bucketed_plan;
+
+/* FUSED bucketed allreduce in two parts.  rar_bucketed_prepare checks the
+ * arguments as rar_bucketed_allreduce does, writes the launch table and the
+ * per-workgroup descriptors (the N ranks' addresses of each tile) into the
+ * workspace with work enqueued on `stream`, and fills *plan; the tensors'
+ * values are not read.  rar_bucketed_launch enqueues the fold alone: every
+ * bucket allreduced in place, the same bits as rar_bucketed_allreduce, and
+ * rar_last_traffic reports the plan's byte counters.  Between the two, and
+ * for as long as the plan is launched, the tensors must keep their
+ * addresses and sizes and nothing may write the workspace; launches on a
+ * stream other than the preparing one must be ordered after the
+ * preparation by the caller.  RAR_EINVAL for a NULL plan or one whose
+ * fields are out of range. */
+int rar_bucketed_prepare(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,
+                         int dtype, size_t cap_bytes, void* workspace, size_t ws_bytes,
+                         rar_bucketed_plan* plan, void* stream);
+int rar_bucketed_launch(const rar_bucketed_plan* plan, void* stream);
 
 /* ---------------------------------------------------------------------- */
 

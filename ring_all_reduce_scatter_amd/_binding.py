@@ -44,6 +44,13 @@ class FtReport(ctypes.Structure):
                 ("waited_ms", ctypes.c_longlong), ("hash", ctypes.c_uint64 * 64)]
 
 
+class BucketedPlan(ctypes.Structure):
+    """rar_bucketed_plan: a prepared FUSED bucketed allreduce."""
+    _fields_ = [("workspace", ctypes.c_void_p), ("desc_offset", ctypes.c_uint64), ("grid", ctypes.c_uint64),
+                ("ntensors", ctypes.c_uint64), ("nranks", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("sent", ctypes.c_uint64 * 64), ("recv", ctypes.c_uint64 * 64)]
+
+
 class CompressCfg(ctypes.Structure):
     """Mirror of rar_compress_cfg."""
     _fields_ = [
@@ -107,6 +114,9 @@ _SIGS = {
     "rar_bucketed_workspace_bytes_ex": (_c_size, [_c_vp, _c_size, _c_int, _c_int, _c_size, _c_int]),
     "rar_bucketed_allreduce_ex": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_int, _c_vp,
                                            _c_size, _c_vp]),
+    "rar_bucketed_prepare": (_c_int, [_c_vp, _c_vp, _c_size, _c_int, _c_int, _c_size, _c_vp, _c_size,
+                                      ctypes.POINTER(BucketedPlan), _c_vp]),
+    "rar_bucketed_launch": (_c_int, [ctypes.POINTER(BucketedPlan), _c_vp]),
     "rar_status_string": (ctypes.c_char_p, [_c_int]),
     "rar_version": (ctypes.c_char_p, []),
 }
@@ -477,16 +487,19 @@ def bucketed_workspace_bytes(counts, nranks: int, dtype: int, cap_bytes: int, al
 
 
 class BucketedAllreduce:
-    """A bucketed allreduce over fixed gradient tensors, marshalled once.
+    """A bucketed allreduce over fixed gradient tensors, prepared once.
 
     tensors[r][t] is rank r's tensor t (device tensors, updated in place on
-    every call).  Validating and collecting N x T device pointers costs
-    milliseconds of Python for a model's worth of tensors, so, as a training
-    loop reuses its gradient tensors every step, the pointer table is built
-    here once and each call only launches.  The tensors and the workspace must
-    stay alive and keep their storage while this object is used."""
+    every call).  A training loop reduces the same gradient tensors every
+    step, so the pointers are collected and checked here once; with the
+    FUSED algorithm the library also writes the launch table and the fold
+    descriptors into the workspace here (rar_bucketed_prepare, on `stream`,
+    synchronised before returning) and each call launches the fold alone
+    (rar_bucketed_launch).  The tensors and the workspace must stay alive and
+    keep their storage, and nothing else may write the workspace, while this
+    object is used."""
 
-    def __init__(self, tensors, cap_bytes: int, workspace, algo: int = ALGO_FUSED):
+    def __init__(self, tensors, cap_bytes: int, workspace, algo: int = ALGO_FUSED, stream=None):
         n, nt = len(tensors), len(tensors[0])
         t0 = tensors[0][0]
         counts = [x.numel() for x in tensors[0]]
@@ -502,8 +515,22 @@ class BucketedAllreduce:
                       _dptr(workspace) if workspace is not None else None,
                       workspace.numel() * workspace.element_size() if workspace is not None else 0)
         self._t0 = t0
+        self._plan = None
+        if algo == ALGO_FUSED:
+            plan = BucketedPlan()
+            st = _stream(stream, t0)
+            rc = lib().rar_bucketed_prepare(self._ptrs, self._counts, nt, n, dtype_code(t0), cap_bytes,
+                                            self._args[5], self._args[6], ctypes.byref(plan), st)
+            _check(rc, "rar_bucketed_prepare")
+            import torch
+            torch.cuda.synchronize(t0.device)  # later calls may come on any stream
+            self._plan = plan
 
     def __call__(self, stream=None):
+        if self._plan is not None:
+            _check(lib().rar_bucketed_launch(ctypes.byref(self._plan), _stream(stream, self._t0)),
+                   "rar_bucketed_launch")
+            return
         rc = lib().rar_bucketed_allreduce_ex(self._ptrs, self._counts, *self._args, _stream(stream, self._t0))
         _check(rc, "rar_bucketed_allreduce_ex")
 
@@ -535,5 +562,19 @@ def rank_tensors(nranks: int, counts, dtype, device="cuda", align_elems: int = 2
 
 
 def bucketed_allreduce(tensors, cap_bytes: int, workspace, stream=None, algo: int = ALGO_FUSED):
-    """tensors[r][t]: rank r's gradient tensor t (device tensors, in place)."""
-    BucketedAllreduce(tensors, cap_bytes, workspace, algo)(stream)
+    """tensors[r][t]: rank r's gradient tensor t (device tensors, in place);
+    one call of rar_bucketed_allreduce_ex (table, descriptors and fold)."""
+    n, nt = len(tensors), len(tensors[0])
+    t0 = tensors[0][0]
+    counts = [x.numel() for x in tensors[0]]
+    flat = [x for row in tensors for x in row]
+    if any(len(row) != nt for row in tensors) or any([x.numel() for x in row] != counts for row in tensors):
+        raise ValueError("tensor t must have the same size on every rank")
+    if any(x.dtype != t0.dtype for x in flat) or not all(x.is_contiguous() for x in flat):
+        raise ValueError("tensors must share one dtype and be contiguous")
+    ptrs = (ctypes.c_void_p * len(flat))(*[_dptr(x) for x in flat])
+    rc = lib().rar_bucketed_allreduce_ex(ptrs, _sizes(counts), nt, n, dtype_code(t0), cap_bytes, algo,
+                                         _dptr(workspace) if workspace is not None else None,
+                                         workspace.numel() * workspace.element_size() if workspace is not None
+                                         else 0, _stream(stream, t0))
+    _check(rc, "rar_bucketed_allreduce_ex")

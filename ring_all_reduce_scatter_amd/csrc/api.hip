@@ -1251,7 +1251,8 @@ size_t rar_bucketed_workspace_bytes_ex(const size_t* counts, size_t ntensors, in
     std::vector<uint64_t> tab;
     uint64_t grid = 0;
     bucket_table(counts, ntensors, nranks, dtype, cap_bytes, nullptr, tab, &grid, nullptr);
-    return round_up(tab.size() * sizeof(uint64_t), kAlign) + round_up((size_t)grid * 16, kAlign);
+    return round_up(tab.size() * sizeof(uint64_t), kAlign) +
+           round_up((size_t)grid * (size_t)bucket_desc_stride(nranks), kAlign);
   }
   if (algo != RAR_ALGO_STEPWISE) return 0;
   std::vector<int> plan;
@@ -1321,9 +1322,9 @@ static int bucketed_packed(void* const* tensors, const size_t* counts, size_t nt
   return RAR_OK;
 }
 
-int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,
-                              int dtype, size_t cap_bytes, int algo, void* workspace, size_t ws_bytes,
-                              void* stream) {
+// Argument checks of the bucketed calls (both algorithms).
+static int bucketed_check(void* const* tensors, const size_t* counts, size_t ntensors, int nranks, int dtype,
+                          size_t cap_bytes, int algo, void* workspace, size_t ws_bytes) {
   if (nranks < 1 || nranks > RAR_MAX_RANKS) return RAR_EINVAL;
   if (!dt_ok(dtype)) return RAR_EDTYPE;
   if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_STEPWISE) return RAR_EINVAL;
@@ -1340,28 +1341,79 @@ int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t
   const size_t need = rar_bucketed_workspace_bytes_ex(counts, ntensors, nranks, dtype, cap_bytes, algo);
   if (!workspace || ws_bytes < need) return RAR_EWORKSPACE;
   if ((uintptr_t)workspace & 15u) return RAR_EALIGN;
-  {  // every tensor of every rank and the workspace: pairwise disjoint
-    std::vector<std::pair<uintptr_t, size_t>> a;
-    a.reserve((size_t)nranks * ntensors + 1);
-    for (int r = 0; r < nranks; ++r)
-      for (size_t t = 0; t < ntensors; ++t) a.emplace_back((uintptr_t)tensors[(size_t)r * ntensors + t], counts[t] * es);
-    a.emplace_back((uintptr_t)workspace, need);
-    const int rc = check_disjoint(a);
-    if (rc) return rc;
-  }
+  // every tensor of every rank and the workspace: pairwise disjoint
+  std::vector<std::pair<uintptr_t, size_t>> a;
+  a.reserve((size_t)nranks * ntensors + 1);
+  for (int r = 0; r < nranks; ++r)
+    for (size_t t = 0; t < ntensors; ++t) a.emplace_back((uintptr_t)tensors[(size_t)r * ntensors + t], counts[t] * es);
+  a.emplace_back((uintptr_t)workspace, need);
+  return check_disjoint(a);
+}
+
+int rar_bucketed_prepare(void* const* tensors, const size_t* counts, size_t ntensors, int nranks, int dtype,
+                         size_t cap_bytes, void* workspace, size_t ws_bytes, rar_bucketed_plan* plan,
+                         void* stream) {
+  if (!plan) return RAR_EINVAL;
+  int rc = bucketed_check(tensors, counts, ntensors, nranks, dtype, cap_bytes, RAR_ALGO_FUSED, workspace, ws_bytes);
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if (algo == RAR_ALGO_STEPWISE) return bucketed_packed(tensors, counts, ntensors, nranks, dtype, cap_bytes, workspace, st);
   std::vector<uint64_t> tab;
   uint64_t grid = 0;
   Traffic tr;
   tr.reset(nranks);
   bucket_table(counts, ntensors, nranks, dtype, cap_bytes, tensors, tab, &grid, &tr);
-  g_last = tr;
-  if (nranks == 1 || grid == 0) return RAR_OK;
-  int rc = hip_rc(launch_fill_u64((uint64_t*)workspace, tab.data(), (int)tab.size(), st));
+  rar_bucketed_plan p{};
+  p.workspace = workspace;
+  p.desc_offset = round_up(tab.size() * sizeof(uint64_t), kAlign);
+  p.grid = nranks == 1 ? 0 : grid;  // one rank: nothing to reduce
+  p.ntensors = ntensors;
+  p.nranks = nranks;
+  p.dtype = dtype;
+  for (int r = 0; r < nranks; ++r) {
+    p.sent[r] = tr.sent[r];
+    p.recv[r] = tr.recv[r];
+  }
+  if (p.grid) {
+    if ((rc = hip_rc(launch_fill_u64((uint64_t*)workspace, tab.data(), (int)tab.size(), st)))) return rc;
+    char* desc = (char*)workspace + p.desc_offset;
+    if ((rc = hip_rc(launch_bucket_desc((const uint64_t*)workspace, desc, nranks, ntensors, grid, dtype, st))))
+      return rc;
+  }
+  *plan = p;
+  return RAR_OK;
+}
+
+int rar_bucketed_launch(const rar_bucketed_plan* plan, void* stream) {
+  if (!plan || plan->nranks < 1 || plan->nranks > RAR_MAX_RANKS || !dt_ok(plan->dtype)) return RAR_EINVAL;
+  if (plan->grid && (!plan->workspace || ((uintptr_t)plan->workspace & 15u) || (plan->desc_offset & 15u) ||
+                     plan->desc_offset == 0))
+    return RAR_EINVAL;
+  g_last.reset(plan->nranks);
+  for (int r = 0; r < plan->nranks; ++r) {
+    g_last.sent[r] = plan->sent[r];
+    g_last.recv[r] = plan->recv[r];
+  }
+  if (plan->grid == 0) return RAR_OK;
+  const uint64_t* tab = (const uint64_t*)plan->workspace;
+  const char* desc = (const char*)plan->workspace + plan->desc_offset;
+  return hip_rc(launch_bucket_fold(tab, desc, plan->nranks, plan->ntensors, plan->grid, plan->dtype,
+                                   (hipStream_t)stream));
+}
+
+int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,
+                              int dtype, size_t cap_bytes, int algo, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  if (algo == RAR_ALGO_STEPWISE) {
+    const int rc = bucketed_check(tensors, counts, ntensors, nranks, dtype, cap_bytes, algo, workspace, ws_bytes);
+    if (rc) return rc;
+    return bucketed_packed(tensors, counts, ntensors, nranks, dtype, cap_bytes, workspace, (hipStream_t)stream);
+  }
+  if (algo != RAR_ALGO_FUSED) return RAR_EINVAL;
+  rar_bucketed_plan plan;
+  const int rc = rar_bucketed_prepare(tensors, counts, ntensors, nranks, dtype, cap_bytes, workspace, ws_bytes,
+                                      &plan, stream);
   if (rc) return rc;
-  char* desc = (char*)workspace + round_up(tab.size() * sizeof(uint64_t), kAlign);
-  return hip_rc(launch_bucket_fold((const uint64_t*)workspace, desc, nranks, ntensors, grid, dtype, st));
+  return rar_bucketed_launch(&plan, stream);
 }
 
 int rar_bucketed_allreduce(void* const* tensors, const size_t* counts, size_t ntensors, int nranks, int dtype,

@@ -77,8 +77,9 @@ hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream) {
 //   per bucket b at hdr+4b:   padded length, chunk length L, first tensor, tensors
 //   per tensor t at ten+2t:   flat offset inside its bucket, element count
 //   pointers at ptr + r*nt+t: rank r's copy of tensor t
-// followed (256-byte aligned) by 16 bytes of descriptor per fold workgroup,
-// written on the device by bucket_desc_kernel.
+// followed (256-byte aligned) by one descriptor per fold workgroup
+// (bucket_desc_stride(N) bytes each), written on the device by
+// bucket_desc_kernel.
 namespace rar {
 namespace {
 
@@ -127,22 +128,27 @@ __device__ __forceinline__ TileLoc locate_tile(const uint64_t* tab, int N, uint6
   return loc;
 }
 
-// Per-workgroup descriptor of the fold, 16 bytes: word 0 the tensor index
-// of a whole tile inside one tensor (or kDescEmpty / kDescSlow), word 1 the
-// chunk, words 2-3 the tile's first element inside that tensor.  Computed
-// once per call by bucket_desc_kernel, so a fold workgroup starts its loads
-// after two dependent scalar loads (descriptor, then the N tensor pointers)
-// instead of the searches through the bucket and tensor tables.
+// Per-workgroup descriptor of the fold: 16 bytes of header (word 0 the
+// tensor index of a whole tile inside one tensor, or kDescEmpty /
+// kDescSlow; word 1 the chunk; words 2-3 the tile's first element inside
+// that tensor), then for a whole tile the N ranks' addresses of that first
+// element.  Computed by bucket_desc_kernel when the plan is prepared, so a
+// fold workgroup issues its loads after one round of independent scalar
+// loads (header and addresses together) instead of the searches through the
+// bucket and tensor tables.
 constexpr uint32_t kDescEmpty = 0xffffffffu;
 constexpr uint32_t kDescSlow = 0xfffffffeu;
 
 __global__ __launch_bounds__(kThreads) void bucket_desc_kernel(const uint64_t* __restrict__ tab, int N,
                                                                 uint64_t ntensors, uint64_t grid, uint64_t kTile,
-                                                                u32x4* __restrict__ desc) {
+                                                                uint64_t es, char* __restrict__ descs,
+                                                                uint64_t dstride) {
   const uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   if (g >= grid) return;
   const uint64_t nb = ld_u64(tab);
   const uint64_t* ten = tab + 2 + 5 * nb;
+  const uint64_t* ptr = ten + 2 * ntensors;
+  char* dp = descs + g * dstride;
   const TileLoc loc = locate_tile(tab, N, g, kTile);
   u32x4 d = {kDescEmpty, 0u, 0u, 0u};
   if (!loc.empty) {
@@ -159,20 +165,23 @@ __global__ __launch_bounds__(kThreads) void bucket_desc_kernel(const uint64_t* _
       d[0] = (uint32_t)t;
       d[2] = (uint32_t)e;
       d[3] = (uint32_t)(e >> 32);
+      uint64_t* addr = (uint64_t*)(dp + 16);
+      for (int r = 0; r < N; ++r) addr[r] = ld_u64(ptr + (uint64_t)r * ntensors + t) + e * es;
     }
   }
-  desc[g] = d;
+  *(u32x4*)dp = d;
 }
 
 template <int DT, int NR, int V>
 __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* __restrict__ tab,
-                                                                const u32x4* __restrict__ desc, int nranks,
-                                                                uint64_t ntensors) {
+                                                                const char* __restrict__ descs, uint64_t dstride,
+                                                                int nranks, uint64_t ntensors) {
   constexpr int E = Vec<DT>::E;
   constexpr int ES = DtypeSize<DT>::value;
   constexpr uint64_t kTile = (uint64_t)kThreads * E * V;
   const int N = NR > 0 ? NR : nranks;
-  const u32x4 dsc = desc[blockIdx.x];
+  const char* dp = descs + (uint64_t)blockIdx.x * dstride;
+  const u32x4 dsc = *(const u32x4*)dp;
   if (dsc[0] == kDescEmpty) return;
   const uint64_t nb = ld_u64(tab);
   const uint64_t* ten = tab + 2 + 5 * nb;
@@ -181,17 +190,17 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* _
   const int first = c + 1 < N ? c + 1 : 0;
 
   if (dsc[0] != kDescSlow) {
-    // The whole tile lies in tensor t: uniform pointers, vector loads.
-    const uint64_t t = dsc[0];
-    const uint64_t e0 = (uint64_t)dsc[2] | ((uint64_t)dsc[3] << 32);
-    auto elem = [&](int v) -> uint64_t { return e0 + ((uint64_t)v * kThreads + threadIdx.x) * E; };
+    // The whole tile lies in one tensor: the N ranks' addresses of its first
+    // element come with the descriptor; uniform pointers, vector loads.
+    const uint64_t* addr = (const uint64_t*)(dp + 16);
+    auto elem = [&](int v) -> uint64_t { return ((uint64_t)v * kThreads + threadIdx.x) * E; };
     Vec<DT> acc[V];
     if constexpr (NR > 0) {
       u32x4 x[NR][V];
       int r = first;
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
-        const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+        const char* p = (const char*)addr[r];
 #pragma unroll
         for (int v = 0; v < V; ++v) x[k][v] = ld16<true>(p + elem(v) * ES);
         r = r + 1 == NR ? 0 : r + 1;
@@ -208,12 +217,12 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* _
       }
     } else {
       int r = first;
-      const char* p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+      const char* p = (const char*)addr[r];
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[v] = unpack16<DT>(ld16<true>(p + elem(v) * ES));
       for (int k = 1; k < N; ++k) {
         r = r + 1 == N ? 0 : r + 1;
-        p = (const char*)ld_u64(ptr + (uint64_t)r * ntensors + t);
+        p = (const char*)addr[r];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const Vec<DT> y = unpack16<DT>(ld16<true>(p + elem(v) * ES));
@@ -225,8 +234,7 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* _
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const u32x4 out = pack16<DT>(acc[v]);
-      for (int d = 0; d < N; ++d)
-        st16<true>((char*)ld_u64(ptr + (uint64_t)d * ntensors + t) + elem(v) * ES, out);
+      for (int d = 0; d < N; ++d) st16<true>((char*)addr[d] + elem(v) * ES, out);
     }
     return;
   }
@@ -277,21 +285,21 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const uint64_t* _
 }
 
 template <int DT, int NR>
-hipError_t bucket_fold_dispatch(const uint64_t* tab, const u32x4* desc, int n, uint64_t ntensors, uint64_t grid,
-                                hipStream_t stream) {
+hipError_t bucket_fold_dispatch(const uint64_t* tab, const char* desc, uint64_t dstride, int n, uint64_t ntensors,
+                                uint64_t grid, hipStream_t stream) {
   constexpr int V = DT == DT_BF16 ? 1 : 2;
   hipLaunchKernelGGL((bucket_fold_kernel<DT, NR, V>), dim3((unsigned)grid), dim3(kThreads),
-                     residency_lds(fold_wgs_per_cu(DT, n)), stream, tab, desc, n, ntensors);
+                     residency_lds(fold_wgs_per_cu(DT, n)), stream, tab, desc, dstride, n, ntensors);
   return launch_status(stream);
 }
 
 template <int DT>
-hipError_t bucket_fold_n(const uint64_t* tab, const u32x4* desc, int n, uint64_t ntensors, uint64_t grid,
-                         hipStream_t stream) {
+hipError_t bucket_fold_n(const uint64_t* tab, const char* desc, uint64_t dstride, int n, uint64_t ntensors,
+                         uint64_t grid, hipStream_t stream) {
   switch (n) {
-    case 8: return bucket_fold_dispatch<DT, 8>(tab, desc, n, ntensors, grid, stream);
-    case 16: return bucket_fold_dispatch<DT, 16>(tab, desc, n, ntensors, grid, stream);
-    default: return bucket_fold_dispatch<DT, 0>(tab, desc, n, ntensors, grid, stream);
+    case 8: return bucket_fold_dispatch<DT, 8>(tab, desc, dstride, n, ntensors, grid, stream);
+    case 16: return bucket_fold_dispatch<DT, 16>(tab, desc, dstride, n, ntensors, grid, stream);
+    default: return bucket_fold_dispatch<DT, 0>(tab, desc, dstride, n, ntensors, grid, stream);
   }
 }
 
@@ -301,19 +309,27 @@ uint64_t bucket_fold_tile_elems(int dt) {
   return (uint64_t)kThreads * (dt == DT_F32 ? 4 : 8) * (dt == DT_BF16 ? 1 : 2);
 }
 
-hipError_t launch_bucket_fold(const uint64_t* dev_table, void* dev_desc, int n, uint64_t ntensors, uint64_t grid,
+uint64_t bucket_desc_stride(int n) { return (16 + 8 * (uint64_t)n + 15) / 16 * 16; }
+
+hipError_t launch_bucket_desc(const uint64_t* dev_table, void* dev_desc, int n, uint64_t ntensors, uint64_t grid,
                               int dt, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
-  u32x4* desc = (u32x4*)dev_desc;
   const uint64_t dgrid = (grid + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(bucket_desc_kernel, dim3((unsigned)dgrid), dim3(kThreads), 0, stream, dev_table, n, ntensors,
-                     grid, bucket_fold_tile_elems(dt), desc);
-  const hipError_t e = launch_status(stream);
-  if (e != hipSuccess) return e;
+                     grid, bucket_fold_tile_elems(dt), (uint64_t)(dt == DT_F32 ? 4 : 2), (char*)dev_desc,
+                     bucket_desc_stride(n));
+  return launch_status(stream);
+}
+
+hipError_t launch_bucket_fold(const uint64_t* dev_table, const void* dev_desc, int n, uint64_t ntensors,
+                              uint64_t grid, int dt, hipStream_t stream) {
+  if (grid == 0) return hipSuccess;
+  const char* desc = (const char*)dev_desc;
+  const uint64_t dstride = bucket_desc_stride(n);
   switch (dt) {
-    case DT_F32: return bucket_fold_n<DT_F32>(dev_table, desc, n, ntensors, grid, stream);
-    case DT_F16: return bucket_fold_n<DT_F16>(dev_table, desc, n, ntensors, grid, stream);
-    default: return bucket_fold_n<DT_BF16>(dev_table, desc, n, ntensors, grid, stream);
+    case DT_F32: return bucket_fold_n<DT_F32>(dev_table, desc, dstride, n, ntensors, grid, stream);
+    case DT_F16: return bucket_fold_n<DT_F16>(dev_table, desc, dstride, n, ntensors, grid, stream);
+    default: return bucket_fold_n<DT_BF16>(dev_table, desc, dstride, n, ntensors, grid, stream);
   }
 }
 

@@ -176,11 +176,16 @@ hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream);
 
 // Elements per workgroup tile of the zero-copy bucket fold (per chunk).
 uint64_t bucket_fold_tile_elems(int dt);
-// All buckets in one launch, in place on the tensors, driven by a device
-// table (layout in bucket_kernels.hip); grid = total workgroups.  dev_desc
-// receives 16 bytes per workgroup (computed by a first, small launch).
-hipError_t launch_bucket_fold(const uint64_t* dev_table, void* dev_desc, int n, uint64_t ntensors, uint64_t grid,
+// Bytes of one fold workgroup's descriptor: 16 of header, 8 per rank.
+uint64_t bucket_desc_stride(int n);
+// Descriptors of the grid fold workgroups (bucket_desc_stride(n) bytes each
+// at dev_desc), from the device table (layout in bucket_kernels.hip).
+hipError_t launch_bucket_desc(const uint64_t* dev_table, void* dev_desc, int n, uint64_t ntensors, uint64_t grid,
                               int dt, hipStream_t stream);
+// All buckets in one launch, in place on the tensors, from the table and the
+// descriptors; grid = total workgroups.
+hipError_t launch_bucket_fold(const uint64_t* dev_table, const void* dev_desc, int n, uint64_t ntensors,
+                              uint64_t grid, int dt, hipStream_t stream);
 
 // Fused compressed ring with per-rank binary32 state (feedback 1 = error
 // feedback, 2 = delta coding); state.p[r] holds count floats.

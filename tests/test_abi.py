@@ -88,10 +88,10 @@ def test_bucket_plan_matches_oracle(orc):
 def test_bucketed_workspace_sizes():
     counts = [10, 20, 5, 100, 3, 3]
     # fused: table of 2 + 5*4 + (2 + 8)*6 words, rounded to 256 bytes, then
-    # 16 bytes per workgroup: 4 buckets, each one 2048-element tile per chunk
-    # for 8 ranks
+    # a descriptor of 16 + 8*8 = 80 bytes per workgroup: 4 buckets, each one
+    # 2048-element tile per chunk for 8 ranks
     table = (2 + 20 + 60) * 8 // 256 * 256 + 256
-    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == table + 4 * 8 * 16  # 512, a multiple of 256
+    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == table + 4 * 8 * 80  # 2560, a multiple of 256
     # stepwise: 8 flat buffers of the largest padded bucket (100 bf16 -> 208 bytes -> 256)
     assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60, rar.ALGO_STEPWISE) == 8 * 256
 
@@ -349,3 +349,27 @@ def test_bucketed_refuses_overlapping_tensors_and_workspace():
     assert call([base, base + 2048, base + 4096, base + region + 2048], ws) == 7
     assert call(ok, base + region + 2048 + 16) == 7  # workspace inside rank 1's tensor 1
     assert call(ok, 0) == 4
+
+
+def test_bucketed_plan_argument_errors():
+    """rar_bucketed_prepare / rar_bucketed_launch refuse a missing or
+    malformed plan before touching the device; a plan with nothing to fold
+    launches nothing and reports its byte counters."""
+    import ctypes
+    from ring_all_reduce_scatter_amd import _binding as b
+    L = b.lib()
+    assert L.rar_bucketed_launch(None, None) == 1  # RAR_EINVAL
+    plan = b.BucketedPlan()
+    assert L.rar_bucketed_launch(ctypes.byref(plan), None) == 1  # RAR_EINVAL: nranks 0
+    plan.nranks, plan.dtype = 4, rar.BF16
+    plan.grid = 5  # workgroups to launch but no workspace
+    assert L.rar_bucketed_launch(ctypes.byref(plan), None) == 1  # RAR_EINVAL
+    plan.workspace, plan.desc_offset = 4096, 8  # descriptors not 16-byte aligned
+    assert L.rar_bucketed_launch(ctypes.byref(plan), None) == 1  # RAR_EINVAL
+    plan.grid, plan.workspace, plan.desc_offset = 0, None, 0
+    for r in range(4):
+        plan.sent[r], plan.recv[r] = 10 * r + 1, 10 * r + 2
+    assert L.rar_bucketed_launch(ctypes.byref(plan), None) == 0
+    assert rar.last_traffic(4) == ([1, 11, 21, 31], [2, 12, 22, 32])
+    counts = (ctypes.c_size_t * 1)(8)
+    assert L.rar_bucketed_prepare(None, counts, 1, 2, rar.BF16, 64, None, 0, None, None) == 1  # RAR_EINVAL

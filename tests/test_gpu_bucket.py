@@ -150,3 +150,36 @@ def test_prepared_bucketed_allreduce_repeats():
             got = to_host(dev[r], "bf16")
             for t in range(len(sizes)):
                 assert_bits_equal(got[t], want[r][t], f"call {call} rank {r} tensor {t}")
+
+
+@pytest.mark.parametrize("dt,n", [("bf16", 16), ("f32", 3), ("f16", 8)])
+def test_prepared_plan_launches_match_oracle(dt, n):
+    """rar_bucketed_prepare once, rar_bucketed_launch twice on restored
+    inputs, then a second, smaller tensor set prepared into the same
+    workspace and launched: every launch gives the oracle's bits and the
+    oracle's byte counters."""
+    def run_set(sizes, salt, ws):
+        th = inputs.bucket_tensors(n, sizes, dtype=dt, salt=salt)
+        ref = [[t.copy() for t in th[r]] for r in range(n)]
+        osent, orecv = oracle.bucketed_allreduce(ref, cap, dt=DT_NAMES[dt])
+        dev = [to_dev(th[r], dt) for r in range(n)]
+        pristine = [to_dev(th[r], dt) for r in range(n)]
+        step = rar.BucketedAllreduce(dev, cap, ws)
+        for call in range(2):
+            for r in range(n):
+                for t, p in zip(dev[r], pristine[r]):
+                    t.copy_(p)
+            step()
+            assert rar.last_traffic(n) == (osent, orecv)
+            for r in range(n):
+                got = to_host(dev[r], dt)
+                for t in range(len(sizes)):
+                    assert_bits_equal(got[t], ref[r][t], f"set {salt} call {call} rank {r} tensor {t}")
+
+    cap = 48 << 10
+    big = inputs.bucket_sizes(50, lo_exp=3, hi_exp=15, salt=20 + n)
+    small = inputs.bucket_sizes(12, lo_exp=3, hi_exp=12, salt=40 + n)
+    need = max(rar.bucketed_workspace_bytes(s, n, DT_NAMES[dt], cap) for s in (big, small))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    run_set(big, 20 + n, ws)
+    run_set(small, 40 + n, ws)
