@@ -64,7 +64,7 @@ COUNTER_KERNELS = {
         "algorithmic": 2 * 8 * 256 * MIB,
         "sources": [_CSRC + "bfp_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp"]},
     "bfp_ring_fold_state_f16_n8": {
-        "match": "::bfp_ring_fold_state_kernel<1, 8, 16, 1>",
+        "match": "::bfp_ring_fold_state_q_kernel<1, 8, 32, 1>",
         "workload": "N=8 x 128M fp16, BFP-8, error feedback (128M fp32 state per rank)",
         "algorithmic": 2 * 8 * 256 * MIB + 2 * 8 * 512 * MIB,
         "sources": [_CSRC + "bfp_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp"]},
@@ -75,7 +75,8 @@ COUNTER_KERNELS = {
         "match": "::bfp_pipe_h16_kernel<8, 1, true>", "workload": "N=8 x 128M fp16, BFP-8, pipelined, 4 MiB units",
         # inputs read once, outputs written once, every message (N per chunk and unit) written once
         "algorithmic": 2 * 8 * 256 * MIB + 8 * 8 * 8 * (16384 + 2 * MIB),
-        "sources": [_CSRC + "pipe_kernels.hip", _CSRC + "bfp_device.hpp", _CSRC + "common.hpp"]},
+        "sources": [_CSRC + "pipe_kernels.hip", _CSRC + "h16_codec.hpp", _CSRC + "bfp_device.hpp",
+                    _CSRC + "common.hpp"]},
     "bucket_fold_bf16_n16": {
         "match": "::bucket_fold_kernel<2, 16,", "workload": "N=16 bf16, 200 gradient tensors in 25 MiB buckets",
         # every rank's copy of every gradient element read once and written once
@@ -100,8 +101,8 @@ PIPELINE_COUNTERS = {
     "sparse_bfp4_allreduce_pipelined": {
         "matches": ["::sparse_pipe_kernel<", "zero_u64_kernel"], "calls": 3,
         "workload": "pipelined sparse + BFP-4 allreduce, N=8 x 64M fp16, ranks 0-3 95% zeros",
-        "sources": [_CSRC + "sparse_pipe_kernels.hip", _CSRC + "block_scan.hpp", _CSRC + "bfp_device.hpp",
-                    _CSRC + "common.hpp", _CSRC + "api.hip"]},
+        "sources": [_CSRC + "sparse_pipe_kernels.hip", _CSRC + "block_scan.hpp", _CSRC + "h16_codec.hpp",
+                    _CSRC + "bfp_device.hpp", _CSRC + "common.hpp", _CSRC + "api.hip"]},
 }
 
 
@@ -707,8 +708,9 @@ def extra_legs(args):
     del th
     ws = torch.empty(rar.bucketed_workspace_bytes(sizes, wk["n"], rar.BF16, wk["cap_bytes"]), dtype=torch.uint8,
                      device="cuda:0")
-    # the gradient tensors are fixed, so the pointer table is marshalled once (as
-    # a training loop would) and each timed step only launches
+    # the gradient tensors are fixed, so the plan (pointer table and fold
+    # descriptors) is prepared once, as a training loop would, and each timed
+    # step launches the fold alone
     step = rar.BucketedAllreduce(dev, wk["cap_bytes"], ws)
     ms, k, _ = time_leg(lambda d: step(), [dev, dev], 1, min(steps, 5))
     S3 = sum(sizes) * 2
