@@ -28,6 +28,9 @@ hipError_t launch_status(hipStream_t stream);
 size_t residency_lds(int wgs_per_cu);
 // Workgroups per CU for a fused fold of dtype dt over n ranks (0 = no cap).
 int fold_wgs_per_cu(int dt, int n);
+// Consecutive tiles of one chunk that consecutive fused-fold workgroups take
+// (1 = chunk fastest), for a chunk of `tiles` tiles.
+uint64_t fold_tile_group(int dt, int n, uint64_t tiles);
 
 // -------------------------------------------------------------- ring (ring_kernels.hip)
 

@@ -45,14 +45,25 @@ __device__ __forceinline__ void chunk_tile(int N, uint32_t* c, uint32_t* t) {
   *t = blockIdx.x / (uint32_t)N;
 }
 
+// Workgroup -> (chunk, tile) for the fused fold: K consecutive workgroups
+// take K consecutive tiles of one chunk, then the next chunk (K = 1 is
+// chunk_tile's order; K = the tiles per chunk makes tiles fastest).  The
+// grid covers tiles rounded up to a multiple of K; the extra workgroups
+// find their tile past the chunk's end and return.
+__device__ __forceinline__ void chunk_tile_k(int N, uint32_t K, uint32_t* c, uint32_t* t) {
+  const uint32_t b = blockIdx.x;
+  *c = (b / K) % (uint32_t)N;
+  *t = (b / (K * (uint32_t)N)) * K + b % K;
+}
+
 template <int DT, int NR, int V, bool STORE_ALL>
 __global__ __launch_bounds__(kThreads) void ring_fold_kernel(RankPtrs bufs, int nranks,
-                                                              uint64_t count, uint64_t L) {
+                                                              uint64_t count, uint64_t L, uint32_t K) {
   constexpr int E = Vec<DT>::E;
   constexpr int ES = DtypeSize<DT>::value;
   const int N = NR > 0 ? NR : nranks;
   uint32_t c, t;
-  chunk_tile(N, &c, &t);
+  chunk_tile_k(N, K, &c, &t);
   const uint64_t lo = (uint64_t)c * L;
   if (lo >= count) return;
   const uint64_t hi = lo + L < count ? lo + L : count;
@@ -318,12 +329,16 @@ hipError_t fold_dispatch_store(const RankPtrs& bufs, int n, uint64_t count, uint
   constexpr int V = FoldVecs<DT>::value;
   const uint64_t tile = (uint64_t)kThreads * Vec<DT>::E * V;
   const uint64_t tiles = (L + tile - 1) / tile;
-  dim3 grid((unsigned)((uint64_t)n * tiles)), block(kThreads);
+  const uint64_t K = fold_tile_group(DT, n, tiles);
+  const uint64_t ktiles = (tiles + K - 1) / K * K;
+  dim3 grid((unsigned)((uint64_t)n * ktiles)), block(kThreads);
   const size_t lds = residency_lds(fold_wgs_per_cu(DT, n));
   if (store_all)
-    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, true>), grid, block, lds, stream, bufs, n, count, L);
+    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, true>), grid, block, lds, stream, bufs, n, count, L,
+                       (uint32_t)K);
   else
-    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, false>), grid, block, lds, stream, bufs, n, count, L);
+    hipLaunchKernelGGL((ring_fold_kernel<DT, NR, V, false>), grid, block, lds, stream, bufs, n, count, L,
+                       (uint32_t)K);
   return launch_status(stream);
 }
 
@@ -397,6 +412,18 @@ hipError_t pair_dispatch(const RankPtrs& bufs, const PairJobs& pairs, uint64_t c
 // (6.35), N = 8 -> 3 (8 x 128M: 728 us against 766 at 2), N = 16 -> 2.
 // Rank counts without a specialised kernel
 // (runtime loop, loads not hoisted) -> 2 (N = 5: 5.11 against 4.57 at 1).
+// Tile order of the fused fold (chunk_tile_k's K).  Which XCD streams which
+// chunk changes the HBM rate more than any per-workgroup change, differently
+// per rank count and dtype (MI355X, contiguous rank buffers a power of two
+// apart, fraction of 8 TB/s): N = 8 keeps one chunk per XCD (K = 1: bf16
+// 0.73, fp32 0.72-0.73; K = 2..32: 0.67-0.70 bf16); N = 16 bf16 (64M per
+// rank) 0.68 at K = 1, 0.718 at K = 32, 0.64-0.66 tiles fastest; N = 16 fp32
+// (32M per rank) 0.67 at K = 1, 0.60-0.67 at K = 2..32, 0.727 tiles fastest.
+uint64_t fold_tile_group(int dt, int n, uint64_t tiles) {
+  if (n == 16) return dt == DT_F32 ? (tiles > 0 ? tiles : 1) : 32;
+  return 1;
+}
+
 int fold_wgs_per_cu(int dt, int n) {
   const bool b16 = dt == DT_BF16;
   switch (n) {

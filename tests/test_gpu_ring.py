@@ -41,6 +41,25 @@ def test_allreduce_matches_oracle(dt, n, count, algo):
     assert sent == osent and recv == orecv
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_fused_fold_tile_orders_at_16_ranks(dt):
+    """At 16 ranks the fused fold hands consecutive workgroups runs of
+    consecutive tiles of one chunk (32 tiles for 16-bit data, the whole
+    chunk for binary32): with 46 tiles per chunk and a ragged end, every
+    element still equals the oracle's."""
+    n = 16
+    count = n * 92_460 + 77
+    xs = _inputs(n, count, dt, salt=46)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce(ref, dt=_oracle_dt(dt))
+    bufs = to_dev(xs, dt)
+    rar.ring_allreduce(bufs)
+    assert rar.last_traffic(n) == (osent, orecv)
+    got = to_host(bufs, dt)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [2, 3, 8])
 @pytest.mark.parametrize("algo", ["fused", "stepwise"])
