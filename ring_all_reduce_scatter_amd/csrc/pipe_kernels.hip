@@ -22,7 +22,8 @@
 //
 // HBM bytes per element position (N ranks, es bytes per element, message
 // bytes m per element): N*es read + N*es written + N*m of messages written;
-// the messages are read back while still in the L2.  (The fused fold
+// most messages are read back while still in the L2 (N = 8 x 128M fp16,
+// 8-bit: 0.29 of the 1.08 GB of messages came back from HBM).  (The fused fold
 // writes no messages; the hop-per-launch forwarding schedule also reads
 // every message back from HBM.)
 #include "bfp_device.hpp"

@@ -9,7 +9,7 @@
 // part of the message, and a sparse unit's tiles need the non-zeros of the
 // tiles before them to place their values and indices.  A gang of
 // workgroups therefore carries one unit through all N hops, holding each
-// tile's partial sum in registers:
+// tile's partial sum in LDS:
 //   hop h: (h > 1) load the tile's part of message h-1 back from its slot,
 //          decode it, add the receiver's own copy (rank c+h);
 //          count the tile's non-zeros, publish the count, learn the unit's
