@@ -433,11 +433,15 @@ size_t rar_bucket_plan(const size_t* counts, size_t ntensors, int dtype, size_t 
 
 /* Workspace for rar_bucketed_allreduce(_ex) and rar_bucketed_prepare (0 on
  * bad args).
- * FUSED: the launch table, 8 * (2 + 5*nbuckets + (2 + nranks)*ntensors)
- * bytes rounded up to 256, then a descriptor of roundup(16 + 8*nranks, 16)
- * bytes per workgroup of the fold launch (nranks * ceil(L_b / tile) per
- * bucket b, L_b its chunk length; tile = 2048 elements for f32 and bf16,
- * 4096 for f16), rounded up to 256.
+ * FUSED: the launch table, 8 * (3 + nbuckets*(1 + nranks) + 4*nruns +
+ * nranks*ntensors) bytes rounded up to 256, then roundup(16 + 8*nranks, 16)
+ * bytes of descriptor per workgroup of the fold launch, rounded up to 256.
+ * A run is the elements [a, b) of a tensor that lie in one chunk of its
+ * bucket (chunk length L = roundup(ceil(P/nranks), 128) for a bucket of P
+ * padded elements) and has ceil((b - floor(a/64)*64) / tile) tiles, tile =
+ * 2048 elements for f32 and bf16, 4096 for f16; a bucket takes nranks
+ * times the largest tile count of its chunks' runs (summed per chunk)
+ * workgroups.
  * STEPWISE: nranks flat buffers of the largest padded bucket. */
 size_t rar_bucketed_workspace_bytes(const size_t* counts, size_t ntensors, int nranks, int dtype,
                                     size_t cap_bytes);

@@ -1204,39 +1204,62 @@ static size_t bucket_flat_bytes(const size_t* counts, size_t nt, int dtype, size
 }
 
 // Zero-copy plan: table words (see bucket_kernels.hip) and the launch grid.
+// A run is the elements [a, b) of tensor t that lie in chunk c of its
+// bucket; the fold tiles it from a rounded down to kRunAlign.  A bucket
+// takes N times its largest chunk's tile count workgroups, chunk fastest.
 static void bucket_table(const size_t* counts, size_t nt, int n, int dtype, size_t cap, void* const* tensors,
                          std::vector<uint64_t>& tab, uint64_t* grid, Traffic* tr) {
   const size_t es = es_of(dtype);
   std::vector<int> plan(nt ? nt : 1, 0);
   const size_t nb = rar_bucket_plan(counts, nt, dtype, cap, plan.data());
   const uint64_t tile = bucket_fold_tile_elems(dtype);
-  tab.assign(2 + 5 * nb + 2 * nt + (size_t)n * nt, 0);
-  tab[0] = nb;
-  uint64_t* start = &tab[1];
-  uint64_t* hdr = &tab[2 + nb];
-  uint64_t* ten = &tab[2 + 5 * nb];
-  uint64_t* ptr = &tab[2 + 5 * nb + 2 * nt];
+  struct Run {
+    uint64_t t, a, b, before;
+  };
+  std::vector<Run> runs;
+  std::vector<uint64_t> crun((size_t)nb * n + 1, 0), start(nb + 1, 0);
   uint64_t wg = 0;
   size_t t = 0;
-  for (size_t b = 0; b < nb; ++b) {
+  for (size_t bk = 0; bk < nb; ++bk) {
     const size_t t0 = t;
     uint64_t total = 0;
-    while (t < nt && plan[t] == (int)b) {
-      ten[2 * t] = total;
-      ten[2 * t + 1] = counts[t];
-      total += padded_elems(counts[t], es);
-      ++t;
-    }
+    while (t < nt && plan[t] == (int)bk) total += padded_elems(counts[t++], es);
     const uint64_t L = chunk_len_aligned(total, n, 128);
-    hdr[4 * b] = total;
-    hdr[4 * b + 1] = L;
-    hdr[4 * b + 2] = t0;
-    hdr[4 * b + 3] = t - t0;
-    start[b] = wg;
-    wg += (uint64_t)n * ((L + tile - 1) / tile);
+    std::vector<uint64_t> tiles((size_t)n, 0);  // per chunk, so far
+    uint64_t off = 0;
+    int cprev = -1;
+    for (size_t k = t0; k < t; ++k) {
+      const uint64_t end = off + counts[k];
+      for (uint64_t pos = off; pos < end;) {
+        const uint64_t c = pos / L, stop = std::min<uint64_t>(end, (c + 1) * L);
+        while (cprev < (int)c) crun[bk * n + (size_t)++cprev] = runs.size();  // chunks cprev+1 .. c start here
+        const uint64_t a = pos - off, b = stop - off;
+        runs.push_back(Run{k, a, b, tiles[c]});
+        tiles[c] += (b - a / kRunAlign * kRunAlign + tile - 1) / tile;
+        pos = stop;
+      }
+      off += padded_elems(counts[k], es);
+    }
+    while (cprev < n - 1) crun[bk * n + (size_t)++cprev] = runs.size();
+    start[bk] = wg;
+    wg += (uint64_t)n * *std::max_element(tiles.begin(), tiles.end());
     if (tr) ring_pass_traffic(*tr, n, total, L, es, 0), ring_pass_traffic(*tr, n, total, L, es, 1);
   }
   start[nb] = wg;
+  crun[(size_t)nb * n] = runs.size();
+  const size_t nr = runs.size();
+  tab.assign(3 + nb + (size_t)nb * n + 4 * nr + (size_t)n * nt, 0);
+  tab[0] = nb;
+  std::copy(start.begin(), start.end(), tab.begin() + 1);
+  std::copy(crun.begin(), crun.end(), tab.begin() + 2 + nb);
+  uint64_t* run = &tab[3 + nb + (size_t)nb * n];
+  uint64_t* ptr = run + 4 * nr;
+  for (size_t j = 0; j < nr; ++j) {
+    run[4 * j] = runs[j].t;
+    run[4 * j + 1] = runs[j].a;
+    run[4 * j + 2] = runs[j].b;
+    run[4 * j + 3] = runs[j].before;
+  }
   if (tensors)
     for (int r = 0; r < n; ++r)
       for (size_t k = 0; k < nt; ++k) ptr[(size_t)r * nt + k] = (uint64_t)(uintptr_t)tensors[(size_t)r * nt + k];
@@ -1247,7 +1270,7 @@ size_t rar_bucketed_workspace_bytes_ex(const size_t* counts, size_t ntensors, in
                                        size_t cap_bytes, int algo) {
   if (nranks < 1 || nranks > RAR_MAX_RANKS || !dt_ok(dtype) || (ntensors && !counts)) return 0;
   if (algo == RAR_ALGO_FUSED) {
-    // launch table, then 16 bytes of descriptor per workgroup
+    // launch table, then one descriptor per workgroup
     std::vector<uint64_t> tab;
     uint64_t grid = 0;
     bucket_table(counts, ntensors, nranks, dtype, cap_bytes, nullptr, tab, &grid, nullptr);
@@ -1394,10 +1417,8 @@ int rar_bucketed_launch(const rar_bucketed_plan* plan, void* stream) {
     g_last.recv[r] = plan->recv[r];
   }
   if (plan->grid == 0) return RAR_OK;
-  const uint64_t* tab = (const uint64_t*)plan->workspace;
   const char* desc = (const char*)plan->workspace + plan->desc_offset;
-  return hip_rc(launch_bucket_fold(tab, desc, plan->nranks, plan->ntensors, plan->grid, plan->dtype,
-                                   (hipStream_t)stream));
+  return hip_rc(launch_bucket_fold(desc, plan->nranks, plan->grid, plan->dtype, (hipStream_t)stream));
 }
 
 int rar_bucketed_allreduce_ex(void* const* tensors, const size_t* counts, size_t ntensors, int nranks,

@@ -177,18 +177,22 @@ struct SegJobs {
 };
 hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream);
 
-// Elements per workgroup tile of the zero-copy bucket fold (per chunk).
+// Elements per workgroup tile of the zero-copy bucket fold.
 uint64_t bucket_fold_tile_elems(int dt);
-// Bytes of one fold workgroup's descriptor: 16 of header, 8 per rank.
+// The fold tiles each run (the elements one tensor shares with one chunk)
+// from the run's first element rounded down to a multiple of kRunAlign
+// elements of its tensor.
+constexpr uint64_t kRunAlign = 64;
+// Bytes of one fold workgroup's descriptor: 16 of header, 8 per rank,
+// rounded up to 16.
 uint64_t bucket_desc_stride(int n);
 // Descriptors of the grid fold workgroups (bucket_desc_stride(n) bytes each
 // at dev_desc), from the device table (layout in bucket_kernels.hip).
 hipError_t launch_bucket_desc(const uint64_t* dev_table, void* dev_desc, int n, uint64_t ntensors, uint64_t grid,
                               int dt, hipStream_t stream);
-// All buckets in one launch, in place on the tensors, from the table and the
-// descriptors; grid = total workgroups.
-hipError_t launch_bucket_fold(const uint64_t* dev_table, const void* dev_desc, int n, uint64_t ntensors,
-                              uint64_t grid, int dt, hipStream_t stream);
+// All buckets in one launch, in place on the tensors, from the descriptors;
+// grid = total workgroups.
+hipError_t launch_bucket_fold(const void* dev_desc, int n, uint64_t grid, int dt, hipStream_t stream);
 
 // Fused compressed ring with per-rank binary32 state (feedback 1 = error
 // feedback, 2 = delta coding); state.p[r] holds count floats.

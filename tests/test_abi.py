@@ -87,11 +87,13 @@ def test_bucket_plan_matches_oracle(orc):
 
 def test_bucketed_workspace_sizes():
     counts = [10, 20, 5, 100, 3, 3]
-    # fused: table of 2 + 5*4 + (2 + 8)*6 words, rounded to 256 bytes, then
-    # a descriptor of 16 + 8*8 = 80 bytes per workgroup: 4 buckets, each one
-    # 2048-element tile per chunk for 8 ranks
-    table = (2 + 20 + 60) * 8 // 256 * 256 + 256
-    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == table + 4 * 8 * 80  # 2560, a multiple of 256
+    # fused: 4 buckets; every tensor lies in chunk 0 of its bucket (chunks
+    # of 128 elements), so 6 runs of one 2048-element tile each and 8
+    # workgroups per tile of the fullest chunk (2, 1, 1, 2 tiles); a table of
+    # 3 + 4*(1 + 8) + 4*6 + 8*6 = 111 words, rounded to 256 bytes, then a
+    # descriptor of 16 + 8*8 = 80 bytes per workgroup
+    table = 111 * 8 // 256 * 256 + 256
+    assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60) == table + 8 * 6 * 80  # 3840, a multiple of 256
     # stepwise: 8 flat buffers of the largest padded bucket (100 bf16 -> 208 bytes -> 256)
     assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60, rar.ALGO_STEPWISE) == 8 * 256
 
