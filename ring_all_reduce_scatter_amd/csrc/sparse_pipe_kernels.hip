@@ -484,7 +484,12 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 // adds on that word); 32768-element tiles (two workgroups per CU) 1.07 ms,
 // 12288-element tiles (six per CU) 0.89 ms; a unit's BFP allgather spread
 // over the workgroup's next unit, one group per hop between the count and
-// the decision, 0.787 ms (no gain).
+// the decision, 0.787 ms (no gain); counting one hop ahead (the next
+// receiver's copy loaded into the partials while the message is written,
+// its count taken with the message as it will decode, so the gang's counts
+// gather during the receive) 0.851 ms: a sparse unit still waits for the
+// gang's slowest count, which the short sparse receive does not cover, and
+// the copy's loads no longer overlap the message's.
 template <int DT>
 struct SpGroups {
   static constexpr int value = DT == DT_F32 ? 4 : 8;
