@@ -81,7 +81,7 @@ COUNTER_KERNELS = {
         "match": "::bucket_fold_kernel<2, 16,", "workload": "N=16 bf16, 200 gradient tensors in 25 MiB buckets",
         # every rank's copy of every gradient element read once and written once
         "algorithmic": lambda: 2 * 16 * 2 * _bucket_elements(),
-        "sources": [_CSRC + "bucket_kernels.hip", _CSRC + "common.hpp"]},
+        "sources": [_CSRC + "bucket_kernels.hip", _CSRC + "common.hpp", _CSRC + "api.hip"]},
 }
 
 
