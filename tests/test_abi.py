@@ -98,6 +98,59 @@ def test_bucketed_workspace_sizes():
     assert rar.bucketed_workspace_bytes(counts, 8, rar.BF16, 60, rar.ALGO_STEPWISE) == 8 * 256
 
 
+def _fused_workspace_from_header(counts, n, dt, cap):
+    """The FUSED workspace size as include/rar.h states it, from the bucket
+    plan: a table of 3 + nb*(1 + n) + 4*nruns + n*nt words, then a
+    descriptor of roundup(16 + 8n, 16) bytes per fold workgroup."""
+    es = {rar.F32: 4, rar.F16: 2, rar.BF16: 2}[dt]
+    tile = {rar.F32: 2048, rar.BF16: 2048, rar.F16: 4096}[dt]
+    nb, plan = rar.bucket_plan(counts, dt, cap)
+    padded = [-(-c * es // 16) * 16 // es for c in counts]
+    nruns = wg = 0
+    for b in range(nb):
+        ts = [t for t in range(len(counts)) if plan[t] == b]
+        total = sum(padded[t] for t in ts)
+        L = -(-(-(-total // n)) // 128) * 128
+        tiles = [0] * n
+        off = 0
+        for t in ts:
+            pos, end = off, off + counts[t]
+            while pos < end:  # the tensor's elements in chunk pos // L
+                c = pos // L
+                stop = min(end, (c + 1) * L)
+                a, e = pos - off, stop - off
+                tiles[c] += -(-(e - a // 64 * 64) // tile)
+                nruns += 1
+                pos = stop
+            off += padded[t]
+        wg += n * max(tiles)
+    words = 3 + nb * (1 + n) + 4 * nruns + n * len(counts)
+    stride = -(-(16 + 8 * n) // 16) * 16
+    return -(-words * 8 // 256) * 256 + -(-wg * stride // 256) * 256
+
+
+@pytest.mark.parametrize("dt", [rar.BF16, rar.F32, rar.F16])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+def test_bucketed_workspace_follows_header_formula(dt, n):
+    """Tensor sets with tensors across chunk ends, tensors smaller than a
+    vector and empty tensors: the library's size equals the header's rule."""
+    sets = [inputs.bucket_sizes(40, lo_exp=0, hi_exp=16, salt=n),
+            [0, 5, 0, 300, 0, 0, 2049, 7, 0, 4096 * 3 + 1, 0, 16, 0],
+            [70_001, 3, 250_000, 128, 99_999, 1 << 17]]
+    for counts in sets:
+        for cap in (4096, 48 << 10, 1 << 20):
+            want = _fused_workspace_from_header(counts, n, dt, cap)
+            assert rar.bucketed_workspace_bytes(counts, n, dt, cap) == want, (counts[:4], cap)
+
+
+def test_bucketed_workspace_of_the_buckets_workload():
+    w = inputs.WORKLOADS["buckets"]
+    counts = inputs.bucket_sizes(w["ntensors"])
+    got = rar.bucketed_workspace_bytes(counts, w["n"], rar.BF16, w["cap_bytes"])
+    assert got == _fused_workspace_from_header(counts, w["n"], rar.BF16, w["cap_bytes"])
+    assert got < 32 << 20  # 115,088 descriptors of 144 bytes and the table
+
+
 class _FakeTensor:
     """Stands in for a device tensor in argument-error tests (never launched)."""
 
