@@ -489,7 +489,16 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 // its count taken with the message as it will decode, so the gang's counts
 // gather during the receive) 0.851 ms: a sparse unit still waits for the
 // gang's slowest count, which the short sparse receive does not cover, and
-// the copy's loads no longer overlap the message's.
+// the copy's loads no longer overlap the message's.  Hops split in two
+// phases (count and publish; then decide and write), a workgroup carrying
+// several units with their phases interleaved so that one unit's decision
+// gathers while the workgroup works on another: with the partials
+// recomputed in the second phase instead of held, 1.20 ms at two units and
+// 1.08 ms at four (the second read comes from DRAM: 2.47 GB read per call
+// against 1.36 GB); with each unit's partials held in its share of the
+// LDS, 0.883 ms at two units (8192-element tiles) and 2.27 ms at four
+// (4096): a unit's tiles multiply, and with them the counts, the adds and
+// the look-back reads.
 template <int DT>
 struct SpGroups {
   static constexpr int value = DT == DT_F32 ? 4 : 8;
