@@ -233,8 +233,10 @@ typedef enum rar_sched {
                             workspace + 1024 + (((h-1)*N + c) *
                             units_per_chunk + u) * slot, with slot the
                             unit's largest message (BFP: rar_bfp_bytes;
-                            SPARSE_AUTO: the larger of 16 + BFP and the
-                            all-non-zero sparse message) rounded up to 256.
+                            SPARSE_AUTO: 16 + BFP rounded up to 16, then
+                            room for the all-non-zero sparse body, where a
+                            sparse message's body starts) rounded up to
+                            256.
                             SPARSE_AUTO: block 128 only (other blocks run
                             STAGED); the tiles of a unit decide its format
                             together, so one launch holds whole units on

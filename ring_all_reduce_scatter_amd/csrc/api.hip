@@ -268,8 +268,9 @@ void plan_sizes(CompPlan* pl, int n, size_t count, int dt) {
   pl->upc = pl->L ? (pl->L + pl->U - 1) / pl->U : 0;
   size_t slot = bfp_msg_bytes(pl->U, pl->block, pl->mbits);
   if (pl->method == RAR_COMP_SPARSE_AUTO) {
-    const size_t sparse_max = 16 + round_up(pl->U * pl->es, 16) + 4 * pl->U;
-    slot = std::max(16 + slot, sparse_max);
+    const size_t body_max = round_up(pl->U * pl->es, 16) + 4 * pl->U;  // all non-zero
+    // pipelined: a sparse message's body follows the BFP area in its slot
+    slot = pl->sched == RAR_SCHED_PIPELINED ? 16 + round_up(slot, 16) + body_max : std::max(16 + slot, 16 + body_max);
   }
   pl->slot = round_up(slot, kAlign);
 }

@@ -30,9 +30,10 @@
 // every workgroup of the grid is resident at once and a gang's members wait
 // only for each other, so the waits end.
 //
-// Message layout (16-byte header {nnz, kind, len, 0} first): kind 1 = values
-// in the element type, zero padding to 16 bytes, uint32 indices ascending
-// and unit-relative; kind 0 = the unit's BFP layout.  The sparse values are
+// Message layout (16-byte header {nnz, kind, len, 0} first): kind 0 = the
+// unit's BFP layout; kind 1 = values in the element type, zero padding to 16
+// bytes, uint32 indices ascending and unit-relative, this body starting
+// after the slot's BFP area (16 + the BFP bytes rounded up to 16).  The sparse values are
 // placed in tile order, lane order inside a tile and group order inside a
 // lane's span, which is ascending index order.
 #include "bfp_device.hpp"
@@ -175,6 +176,10 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
     };
     const bool full = (uint64_t)(k + 1) * kTile <= ulen;  // every group of every lane holds 8 elements
     const uint64_t nb = (ulen + block - 1) / block, eb = round16(nb);
+    // a sparse message's body (values, padding, indices) follows the BFP
+    // area of the slot: a tile may write its BFP part before it learns that
+    // the unit goes sparse (see below), and the two must not overlap
+    const uint64_t spoff = 16 + round16(bfp_msg_bytes(ulen, (int)block, mbits));
     uint8_t* msg1 = a.slots + (uint64_t)uid * a.slot;
     auto load = [&](int rank, int g) -> Raw8<DT> {
       if (full) return load_raw8<DT, true>(a.bufs.p[rank], ulo + off(g));
@@ -231,8 +236,8 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
     // four per lane at a time; their indices are distinct, so no two lanes
     // touch one element.  Every lane calls this between two barriers.
     auto scatter_sparse = [&](const uint8_t* m, bool acc) {
-      const uint8_t* vals = m + 16;
-      const uint32_t* idx = (const uint32_t*)(m + 16 + round16((uint64_t)tot_prev * ES));
+      const uint8_t* vals = m + spoff;
+      const uint32_t* idx = (const uint32_t*)(m + spoff + round16((uint64_t)tot_prev * ES));
       const uint32_t base = k * (uint32_t)kTile;  // unit-relative first element of the tile
       for (uint32_t j0 = threadIdx.x; j0 < tile_cnt; j0 += 4 * kThreads) {
         uint32_t raw[4], e[4];
@@ -294,106 +299,7 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
       uint32_t tile_nnz, unused;
       block_sum2(lane_nnz, 0u, &tile_nnz, &unused);
       const uint64_t fi = (uint64_t)(h - 1) * nunits + uid;
-      if (threadIdx.x == 0) {
-        // zeros > theta * len fails for every running sum at or past lim_nnz
-        const double lim = (double)a.theta * (double)ulen;
-        st_agent32(&a.tilecnt[fi * a.kmax + k], tile_nnz + 1);
-        const uint64_t old = __hip_atomic_fetch_add(&a.unitw[fi], (1ull << 32) | (uint64_t)tile_nnz,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t arrived = (uint32_t)(old >> 32) + 1u, sum = (uint32_t)old + tile_nnz;
-        uint32_t kind = 0, total = 0;
-        if ((double)(ulen - sum) <= lim) {
-          // BFP: zeros only shrink as counts arrive.  The add that crossed publishes it.
-          if (!((double)(ulen - (uint32_t)old) <= lim)) st_agent64(&a.decw[fi], 1ull);
-        } else if (arrived >= Ku) {
-          // the last count, and the threshold never crossed: sparse, with the exact total
-          kind = 1;
-          total = sum;
-          st_agent64(&a.decw[fi], ((uint64_t)sum << 8) | 2ull);
-        } else {
-          // wait for the tile that crosses the threshold or for the last one
-          for (uint32_t it = 0;; ++it) {
-            const uint64_t d = ld_agent64(&a.decw[fi]);
-            if (d != 0) {
-              kind = (d & 0xffu) == 2u ? 1u : 0u;
-              total = (uint32_t)(d >> 8);
-              break;
-            }
-            if (it >= kSpinLimit || ((it & 255u) == 255u && ld_agent32(a.abort) != 0u)) {
-              __hip_atomic_store(a.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
-        s_dec[0] = kind;
-        s_dec[1] = total;
-      }
-      __syncthreads();
-      const bool sparse = s_dec[0] != 0;
-      const uint32_t total = s_dec[1];
-      if (k == 0 && threadIdx.x == 0) {
-        uint32_t* hdr = (uint32_t*)msg;
-        hdr[0] = sparse ? total : 0u;
-        hdr[1] = sparse ? 1u : 0u;
-        hdr[2] = (uint32_t)ulen;
-        hdr[3] = 0u;
-        const uint64_t bytes = sparse ? 16 + round16((uint64_t)total * ES) + 4ull * total
-                                      : 16 + bfp_msg_bytes(ulen, (int)block, mbits);
-        // message h < N goes from rank c+h to c+h+1; message N (the owner's)
-        // is relayed around the ring, from c+s-1 to c+s for s = 1..N-1
-        const int s0 = h < N ? h : 1, s1 = h < N ? h : N - 1;
-        for (int s = s0; s <= s1; ++s) {
-          const int from = h < N ? ring(c, s) : ring(c, s - 1);
-          const int to = from + 1 == N ? 0 : from + 1;
-          atomicAdd((unsigned long long*)&a.traffic[from], (unsigned long long)bytes);
-          atomicAdd((unsigned long long*)&a.traffic[kMaxRanks + to], (unsigned long long)bytes);
-        }
-      }
-      if (sparse) {
-        // non-zeros of the unit's tiles before this one
-        uint32_t before_part = 0;
-        for (uint32_t j = threadIdx.x; j < k; j += kThreads) {
-          uint32_t v = 0;
-          for (uint32_t it = 0; (v = ld_agent32(&a.tilecnt[fi * a.kmax + j])) == 0u; ++it) {
-            if (it >= kSpinLimit || ((it & 255u) == 255u && ld_agent32(a.abort) != 0u)) {
-              __hip_atomic_store(a.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              v = 1;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-          before_part += v - 1;
-        }
-        uint32_t before;
-        block_sum2(before_part, 0u, &before, &unused);
-        uint8_t* vals = msg + 16;
-        uint32_t* idx = (uint32_t*)(msg + 16 + round16((uint64_t)total * ES));
-        uint32_t rel = 0;  // entries of this tile written so far
-        for (int g = 0; g < GP; ++g) {
-          const G8 x = unpack8<DT>(P[slot(g)]);
-          uint32_t m = nz_mask<DT>(x, nvof(g));
-          uint32_t gtot;
-          const uint32_t lpos = rel + block_exclusive_scan((uint32_t)__builtin_popcount(m), &gtot);
-          uint32_t q = before + lpos;
-          const uint32_t o = (uint32_t)off(g);
-          for (; m; m &= m - 1, ++q) {  // ascending element order
-            const int i = __builtin_ctz(m);
-            const uint32_t raw = lds_elem<DT>(&P[slot(g)], i);
-            if constexpr (ES == 4) ((uint32_t*)vals)[q] = raw;
-            else ((uint16_t*)vals)[q] = (uint16_t)raw;
-            idx[q] = o + (uint32_t)i;
-          }
-          rel += gtot;
-        }
-        tile_first = before;
-        tile_cnt = rel;
-        if (k == 0 && threadIdx.x < 16) {
-          // zero padding between the values and the indices
-          const uint64_t pad0 = 16 + (uint64_t)total * ES, pad1 = 16 + round16((uint64_t)total * ES);
-          if (pad0 + threadIdx.x < pad1) msg[pad0 + threadIdx.x] = 0;
-        }
-      } else {
+      auto write_bfp = [&]() {
         uint8_t* payload = msg + 16;
         if (k == 0 && threadIdx.x < eb - nb) payload[nb + threadIdx.x] = 0;  // exponent padding
 #pragma unroll 2
@@ -417,7 +323,124 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
             encode_group<DT, LPB>(unpack8<DT>(P[slot(g)]), nvof(g), off(g), payload, payload + eb, lpb, mbits, qmax);
           }
         }
+      };
+      auto write_sparse = [&](uint32_t total) {
+        // non-zeros of the unit's tiles before this one
+        uint32_t before_part = 0;
+        for (uint32_t j = threadIdx.x; j < k; j += kThreads) {
+          uint32_t v = 0;
+          for (uint32_t it = 0; (v = ld_agent32(&a.tilecnt[fi * a.kmax + j])) == 0u; ++it) {
+            if (it >= kSpinLimit || ((it & 255u) == 255u && ld_agent32(a.abort) != 0u)) {
+              __hip_atomic_store(a.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              v = 1;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          before_part += v - 1;
+        }
+        uint32_t before;
+        block_sum2(before_part, 0u, &before, &unused);
+        uint8_t* vals = msg + spoff;
+        uint32_t* idx = (uint32_t*)(msg + spoff + round16((uint64_t)total * ES));
+        uint32_t rel = 0;  // entries of this tile written so far
+        for (int g = 0; g < GP; ++g) {
+          const G8 x = unpack8<DT>(P[slot(g)]);
+          uint32_t m = nz_mask<DT>(x, nvof(g));
+          uint32_t gtot;
+          const uint32_t lpos = rel + block_exclusive_scan((uint32_t)__builtin_popcount(m), &gtot);
+          uint32_t q = before + lpos;
+          const uint32_t o = (uint32_t)off(g);
+          for (; m; m &= m - 1, ++q) {  // ascending element order
+            const int i = __builtin_ctz(m);
+            const uint32_t raw = lds_elem<DT>(&P[slot(g)], i);
+            if constexpr (ES == 4) ((uint32_t*)vals)[q] = raw;
+            else ((uint16_t*)vals)[q] = (uint16_t)raw;
+            idx[q] = o + (uint32_t)i;
+          }
+          rel += gtot;
+        }
+        tile_first = before;
+        tile_cnt = rel;
+        if (k == 0 && threadIdx.x < 16) {
+          // zero padding between the values and the indices
+          const uint64_t pad0 = spoff + (uint64_t)total * ES, pad1 = spoff + round16((uint64_t)total * ES);
+          if (pad0 + threadIdx.x < pad1) msg[pad0 + threadIdx.x] = 0;
+        }
+      };
+      // A tile whose own zeros would leave its unit BFP writes its BFP part
+      // while its count's add is in flight and learns the unit's decision
+      // afterwards: most messages are BFP, and the add's round trip then
+      // overlaps the write.  If the unit goes sparse after all, the tile
+      // writes its sparse part too (into the slot's sparse body, which the
+      // BFP area does not overlap).  Other tiles learn the decision first.
+      const uint64_t tlen = ulen - (uint64_t)k * kTile < kTile ? ulen - (uint64_t)k * kTile : kTile;
+      const bool spec = (double)(tlen - tile_nnz) <= (double)a.theta * (double)tlen;  // uniform
+      uint32_t kind = 0, total = 0;  // thread 0
+      bool known = false;
+      if (threadIdx.x == 0) {
+        // zeros > theta * len fails for every running sum at or past lim_nnz
+        const double lim = (double)a.theta * (double)ulen;
+        st_agent32(&a.tilecnt[fi * a.kmax + k], tile_nnz + 1);
+        const uint64_t old = __hip_atomic_fetch_add(&a.unitw[fi], (1ull << 32) | (uint64_t)tile_nnz,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t arrived = (uint32_t)(old >> 32) + 1u, sum = (uint32_t)old + tile_nnz;
+        if ((double)(ulen - sum) <= lim) {
+          // BFP: zeros only shrink as counts arrive.  The add that crossed publishes it.
+          if (!((double)(ulen - (uint32_t)old) <= lim)) st_agent64(&a.decw[fi], 1ull);
+          known = true;
+        } else if (arrived >= Ku) {
+          // the last count, and the threshold never crossed: sparse, with the exact total
+          kind = 1;
+          total = sum;
+          st_agent64(&a.decw[fi], ((uint64_t)sum << 8) | 2ull);
+          known = true;
+        }
       }
+      if (spec) write_bfp();
+      if (threadIdx.x == 0) {
+        if (!known) {
+          // wait for the tile that crosses the threshold or for the last one
+          for (uint32_t it = 0;; ++it) {
+            const uint64_t d = ld_agent64(&a.decw[fi]);
+            if (d != 0) {
+              kind = (d & 0xffu) == 2u ? 1u : 0u;
+              total = (uint32_t)(d >> 8);
+              break;
+            }
+            if (it >= kSpinLimit || ((it & 255u) == 255u && ld_agent32(a.abort) != 0u)) {
+              __hip_atomic_store(a.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        s_dec[0] = kind;
+        s_dec[1] = total;
+      }
+      __syncthreads();
+      const bool sparse = s_dec[0] != 0;
+      total = s_dec[1];
+      if (k == 0 && threadIdx.x == 0) {
+        uint32_t* hdr = (uint32_t*)msg;
+        hdr[0] = sparse ? total : 0u;
+        hdr[1] = sparse ? 1u : 0u;
+        hdr[2] = (uint32_t)ulen;
+        hdr[3] = 0u;
+        const uint64_t bytes = sparse ? 16 + round16((uint64_t)total * ES) + 4ull * total
+                                      : 16 + bfp_msg_bytes(ulen, (int)block, mbits);
+        // message h < N goes from rank c+h to c+h+1; message N (the owner's)
+        // is relayed around the ring, from c+s-1 to c+s for s = 1..N-1
+        const int s0 = h < N ? h : 1, s1 = h < N ? h : N - 1;
+        for (int s = s0; s <= s1; ++s) {
+          const int from = h < N ? ring(c, s) : ring(c, s - 1);
+          const int to = from + 1 == N ? 0 : from + 1;
+          atomicAdd((unsigned long long*)&a.traffic[from], (unsigned long long)bytes);
+          atomicAdd((unsigned long long*)&a.traffic[kMaxRanks + to], (unsigned long long)bytes);
+        }
+      }
+      if (sparse) write_sparse(total);
+      else if (!spec) write_bfp();
       sp_prev = sparse;
       tot_prev = total;
     }

@@ -177,7 +177,8 @@ def test_pipelined_sparse_messages_match_oracle(dt):
     """Every message the pipelined SPARSE_AUTO schedule leaves in its slots
     (hop h of chunk c, unit u) equals the oracle's encode of that hop's
     partial: built hop by hop from the oracle's sparse and BFP primitives,
-    with the unit's format chosen by the oracle's threshold rule."""
+    with the unit's format chosen by the oracle's threshold rule.  In a
+    slot, a sparse message's body follows the BFP area."""
     n, U, mbits, theta = 4, 8192, 4, 0.5
     es = 4 if dt == "f32" else 2
     count = n * 2 * U + 3000
@@ -191,7 +192,9 @@ def test_pipelined_sparse_messages_match_oracle(dt):
     host = ws.cpu().numpy()
     L = rar.compressed_chunk_len(count, n, 128)
     upc = -(-L // U)
-    slot = -(-max(16 + rar.bfp_bytes(U, 128, mbits), 16 + (-(-U * es // 16) * 16) + 4 * U) // 256) * 256
+    # a slot: header, the BFP area, then room for the all-non-zero sparse
+    # body, which starts after the BFP area
+    slot = -(-(16 + -(-rar.bfp_bytes(U, 128, mbits) // 16) * 16 + (-(-U * es // 16) * 16) + 4 * U) // 256) * 256
     odt = DT_NAMES[dt]
     checked = 0
     for c in range(n):
@@ -214,7 +217,11 @@ def test_pipelined_sparse_messages_match_oracle(dt):
                                                      (ln >> 16) & 0xff, ln >> 24, 0, 0, 0, 0], np.uint8), body])
                     kind = 0
                 base = 1024 + (((h - 1) * n + c) * upc + u) * slot
-                got = host[base:base + want.size]
+                if kind == 1:
+                    spoff = 16 + -(-rar.bfp_bytes(ln, 128, mbits) // 16) * 16
+                    got = np.concatenate([host[base:base + 16], host[base + spoff:base + spoff + want.size - 16]])
+                else:
+                    got = host[base:base + want.size]
                 bad = np.flatnonzero(got != want)
                 assert bad.size == 0, f"hop {h} chunk {c} unit {u} kind {kind}: {bad.size} bytes differ at {bad[:4]}"
                 checked += 1
