@@ -488,7 +488,8 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 // 0.888 ms with the binary32 codec and each lane decoding its own sparse
 // entries one dependent load at a time, 0.845 ms with the packed binary16
 // codec (77 instead of 112 VGPRs), 0.786 ms with the workgroup decoding the
-// sparse entries together.  Per hop of a unit (timestamps of the first
+// sparse entries together, 0.764 ms with a dense tile writing its BFP part
+// before it learns the unit's decision.  Per hop of a unit (timestamps of the first
 // unit of each tile): decode 7-10 us, learning the decision 2.4-3.3 us
 // (BFP) or 7-12 us (sparse: every count must be in), message write 3-7 us;
 // the allgather 34 us.  Holding the next receiver's copy in
