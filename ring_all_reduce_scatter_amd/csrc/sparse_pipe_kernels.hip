@@ -522,7 +522,9 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 // against 1.36 GB); with each unit's partials held in its share of the
 // LDS, 0.883 ms at two units (8192-element tiles) and 2.27 ms at four
 // (4096): a unit's tiles multiply, and with them the counts, the adds and
-// the look-back reads.
+// the look-back reads.  Loading the first two groups of the receiver's
+// copy before the wait for the message stores: 0.771 against 0.760 ms
+// (96 VGPRs; all eight groups: 215).
 template <int DT>
 struct SpGroups {
   static constexpr int value = DT == DT_F32 ? 4 : 8;
