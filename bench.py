@@ -136,10 +136,11 @@ CALIBRATION = {"match": "copy_jobs_kernel", "bytes": 256 * MIB}
 # 128-byte requests, so FETCH_SIZE charges them 64 bytes and reads half.
 PMC_COUNTERS = ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "TCC_EA0_RDREQ_128B_sum",
                 "TCC_BUBBLE_sum"]
+# R = the repository root, OUT = any directory for the profiler's files
 PMC_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc " + " ".join(PMC_COUNTERS) +
-    " --output-format csv -d $R/gpurun_out/pmc_dram -o pmc -- python -u $R/bench.py --counters",
-    "python bench.py --ingest-counters gpurun_out/pmc_dram/pmc_counter_collection.csv",
+    " --output-format csv -d $OUT/pmc_dram -o pmc -- python -u $R/bench.py --counters",
+    "python bench.py --ingest-counters $OUT/pmc_dram/pmc_counter_collection.csv",
 ]
 
 
