@@ -778,7 +778,11 @@ void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, i
 // uncapped and 2.52 at three, measured with an earlier LDS-staged layout).
 // Workgroups take the chunk fastest, as in the ring fold at 8 ranks;
 // groups of K consecutive tiles per chunk measured 0.716 at K = 2, 0.680 at
-// 4, 0.700 at 16 and 0.634 at 64 against 0.716-0.719.
+// 4, 0.700 at 16 and 0.634 at 64 against 0.716-0.719.  Loading the 16-bit
+// inputs as 16-byte lanes and moving them to the quad layout with cross-lane
+// permutes (and the results back for 16-byte stores) measured 0.698-0.702
+// against 0.713-0.715: the permutes cost more than the halved load and
+// store counts save.
 int state_fold_wgs_per_cu() { return 2; }
 
 template <int DT, int NR, int FB>
