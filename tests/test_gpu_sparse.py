@@ -273,3 +273,38 @@ def test_pipelined_sparse_special_values_match_oracle(dt, mbits):
         assert np.array_equal(nan_mask(got[r], dt), nan), f"rank {r} NaN positions"
         assert_bits_equal(got[r][~nan], ref[r][~nan], f"rank {r}")
     assert sent == osent and recv == orecv
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("pattern", ["one_dense_tile", "one_zero_tile"])
+def test_pipelined_sparse_tiles_unlike_their_unit_match_oracle(dt, pattern):
+    """Units of four tiles of the pipelined kernel in which one tile differs
+    from the rest: a dense tile in a unit that goes sparse (the tile's own
+    count says BFP, so it writes its BFP part before it learns the unit's
+    decision and then writes its sparse part), or an all-zero tile in a unit
+    that goes BFP.  Every hop's message has that shape; results and byte
+    counters equal the oracle's."""
+    n, mbits = 4, 4
+    tile = 16384 if dt != "f32" else 8192  # elements per workgroup tile of the pipelined kernel
+    U = 4 * tile
+    count = n * 2 * U + 777
+    L = rar.compressed_chunk_len(count, n, 128)
+    g = np.random.default_rng(7)
+    special = np.zeros(count, dtype=bool)  # the differing tile of every unit
+    for c in range(n):
+        for u in range(-(-L // U)):
+            a = c * L + u * U
+            special[min(a, count):min(a + tile, count, (c + 1) * L)] = True
+    xs = []
+    for r in range(n):
+        x = (g.standard_normal(count) * 1e-2).astype(np.float32)
+        x[x == 0] = np.float32(1e-3)  # no accidental zeros in the dense parts
+        x[~special if pattern == "one_dense_tile" else special] = 0.0
+        xs.append(inputs.cast(x, dt))
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=mbits, unit=U,
+                                                    dt=DT_NAMES[dt])
+    got, sent, recv = _run_auto(xs, dt, mbits=mbits, unit_elems=U, sched="pipelined")
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+    assert sent == osent and recv == orecv
