@@ -93,6 +93,26 @@ __device__ __forceinline__ void st16(char* p, u32x4 v) {
   else *(u32x4*)p = v;
 }
 
+// Write-through stores for streaming outputs: 16-byte lane stores that are
+// nontemporal and at device scope (the nt and sc1 cache-policy bits), so
+// each output line goes on towards HBM as it is written instead of sitting
+// dirty in the L2 until an eviction writes it back among the reads.  Global
+// stores take no such bits, so these go through a buffer descriptor over a
+// workgroup-uniform byte range [base, base + bytes) (scalar registers),
+// each lane giving its byte offset in the range; a store past the range is
+// dropped by the hardware.  Measured on the fused fold pattern (8 ranks x
+// 256 MiB fp32, one launch): 680 us with these stores against 709 us with
+// nontemporal stores alone (0.79 against 0.76 of 8 TB/s); device scope
+// alone, without nt, gained nothing.
+typedef __amdgpu_buffer_rsrc_t WtRange;
+__device__ __forceinline__ WtRange wt_range(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st16_wt(WtRange r, uint32_t off, u32x4 v) {
+  constexpr int kNtSc1 = 2 | 16;  // cache-policy operand: nt (bit 1), sc1 (bit 4)
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNtSc1);
+}
+
 // Raw 8-element group as stored (fp32: 8 words; 16-bit: 4 words).
 template <int DT>
 struct Raw8 {

@@ -113,13 +113,16 @@ __global__ __launch_bounds__(kThreads) void ring_fold_kernel(RankPtrs bufs, int 
         }
       }
     }
+    // write-through stores over the tile's range in each rank
+    constexpr uint32_t kTileBytes = (uint32_t)(kTile * ES);
+    auto lane_off = [&](int v) -> uint32_t { return ((uint32_t)v * kThreads + threadIdx.x) * E * ES; };
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const u32x4 out = pack16<DT>(acc[v]);
       if constexpr (STORE_ALL) {
-        for (int d = 0; d < N; ++d) st16<true>(bufs.p[d] + elem(v) * ES, out);
+        for (int d = 0; d < N; ++d) st16_wt(wt_range(bufs.p[d] + tile0 * ES, kTileBytes), lane_off(v), out);
       } else {
-        st16<true>(bufs.p[c] + elem(v) * ES, out);
+        st16_wt(wt_range(bufs.p[c] + tile0 * ES, kTileBytes), lane_off(v), out);
       }
     }
     return;
