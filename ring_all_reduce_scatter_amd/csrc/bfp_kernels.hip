@@ -265,7 +265,9 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_kernel(RankPtrs bufs, 
       const u32x4 y = qdq_h16x8<LPB>(ph[g], lpb, mbits, lo, hi);
       const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
       if (full) {
-        for (int d = 0; d < N; ++d) st16<true>(bufs.p[d] + e * 2, y);
+        // write-through stores over the tile's range in each rank
+        for (int d = 0; d < N; ++d)
+          st16_wt(wt_range(bufs.p[d] + tile0 * 2, (uint32_t)(kTile * 2)), (uint32_t)((e - tile0) * 2), y);
       } else if (nv[g] > 0) {
         Raw8<DT> yr;
         yr.w[0] = y;
@@ -302,7 +304,9 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_kernel(RankPtrs bufs, 
     const uint64_t e = e0 + (uint64_t)g * kThreads * kGroupElems;
     if (full) {
       Raw8<DT> out = pack8<DT>(y);
-      for (int d = 0; d < N; ++d) store_raw8<DT, true>(bufs.p[d], e, out);
+      constexpr int ES = DtypeSize<DT>::value;
+      for (int d = 0; d < N; ++d)
+        store_raw8_wt<DT>(wt_range(bufs.p[d] + tile0 * ES, (uint32_t)(kTile * ES)), (uint32_t)((e - tile0) * ES), out);
     } else if (nv[g] > 0) {
       for (int d = 0; d < N; ++d) store_part8<DT>(bufs.p[d], e, nv[g], y);
     }
@@ -421,6 +425,22 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_f32q_kernel(RankPtrs b
     }
   }
   const Q8 y = qdq(p);
+  if (tile0 + (uint64_t)kThreads * kGroupElems <= hi) {
+    // a whole tile: write-through stores over its range in each rank
+    u32x4 wa, wb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wa[i] = __float_as_uint(y.v[i]);
+      wb[i] = __float_as_uint(y.v[4 + i]);
+    }
+    constexpr uint32_t kBytes = (uint32_t)kThreads * kGroupElems * 4;
+    for (int d = 0; d < N; ++d) {
+      const WtRange rg = wt_range(bufs.p[d] + tile0 * 4, kBytes);
+      st16_wt(rg, (uint32_t)((eA - tile0) * 4), wa);
+      st16_wt(rg, (uint32_t)((eB - tile0) * 4), wb);
+    }
+    return;
+  }
   for (int d = 0; d < N; ++d) {
     stq(bufs.p[d], eA, nA, y.v);
     stq(bufs.p[d], eB, nB, y.v + 4);
@@ -581,11 +601,28 @@ __global__ __launch_bounds__(kThreads) void bfp_ring_fold_state_q_kernel(RankPtr
         if (i < nv) ((float*)base)[e + i] = v[i];
     }
   };
-  auto st_s = [&](int rank, uint64_t e, int nv, const float* v) { st_f32(st.p[rank], e, nv, v); };
+  // a whole tile stores write-through over its range in each rank
+  const bool wt = tile0 + (uint64_t)kThreads * kGroupElems <= hi;  // uniform
+  constexpr uint32_t kTileElems = (uint32_t)kThreads * kGroupElems;
+  auto st_s = [&](int rank, uint64_t e, int nv, const float* v) {
+    if (wt) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+      st16_wt(wt_range(st.p[rank] + tile0 * 4, kTileElems * 4), (uint32_t)((e - tile0) * 4), w);
+    } else {
+      st_f32(st.p[rank], e, nv, v);
+    }
+  };
   auto st_y = [&](int rank, uint64_t e, int nv, const float* v) {
     char* base = bufs.p[rank];
     if constexpr (ES == 2) {
-      if (nv == 4) {
+      if (wt) {
+        u32x2 w;
+        w[0] = narrow16<DT>(v[0]) | narrow16<DT>(v[1]) << 16;
+        w[1] = narrow16<DT>(v[2]) | narrow16<DT>(v[3]) << 16;
+        st8_wt(wt_range(base + tile0 * 2, kTileElems * 2), (uint32_t)((e - tile0) * 2), w);
+      } else if (nv == 4) {
         u32x2 w;
         w[0] = narrow16<DT>(v[0]) | narrow16<DT>(v[1]) << 16;
         w[1] = narrow16<DT>(v[2]) | narrow16<DT>(v[3]) << 16;

@@ -110,12 +110,12 @@ __device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) { return *p; }
 // instructions: a uniform address becomes the scalar base of the load, and
 // the scalar loads of further addresses do not wait for the data (a flat
 // load counts against the scalar counter too, so each wait for an address
-// would also wait for the load before it).
+// would also wait for the load before it).  Whole vectors are stored
+// write-through (st16_wt) over the tile's range in each rank.
 typedef __attribute__((address_space(1))) char gchar;
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
 __device__ __forceinline__ gchar* gptr(uint64_t a) { return (gchar*)a; }
 __device__ __forceinline__ u32x4 gld16(const gchar* p) { return __builtin_nontemporal_load((const gu32x4*)p); }
-__device__ __forceinline__ void gst16(gchar* p, u32x4 v) { __builtin_nontemporal_store(v, (gu32x4*)p); }
 template <int DT>
 __device__ __forceinline__ float gload_elem(const gchar* base, uint64_t i) {
   typedef __attribute__((address_space(1))) const float gf32;
@@ -237,6 +237,7 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const char* __res
                                                                 int nranks) {
   constexpr int E = Vec<DT>::E;
   constexpr int ES = DtypeSize<DT>::value;
+  constexpr uint32_t kTileBytes = (uint32_t)kThreads * E * V * ES;  // the tile's range in each rank
   const int N = NR > 0 ? NR : nranks;
   const char* dp = descs + (uint64_t)blockIdx.x * dstride;
   const u32x4 dsc = *(const u32x4*)dp;
@@ -248,10 +249,11 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const char* __res
   Vec<DT> acc[V];
   if (dsc[0] == kDescWhole) {
     fold_vectors<DT, NR, V>(addr, N, off, acc);
+    // write-through stores over the tile's range in each rank
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const u32x4 out = pack16<DT>(acc[v]);
-      for (int k = 0; k < N; ++k) gst16(gptr(addr[k]) + off[v] * ES, out);
+      for (int k = 0; k < N; ++k) st16_wt(wt_range((const char*)addr[k], kTileBytes), off[v] * ES, out);
     }
     return;
   }
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const char* __res
   for (int v = 0; v < V; ++v) {
     if (!full[v]) continue;
     const u32x4 out = pack16<DT>(acc[v]);
-    for (int k = 0; k < N; ++k) gst16(gptr(addr[k]) + off[v] * ES, out);
+    for (int k = 0; k < N; ++k) st16_wt(wt_range((const char*)addr[k], kTileBytes), off[v] * ES, out);
   }
 #pragma unroll
   for (int v = 0; v < V; ++v) {

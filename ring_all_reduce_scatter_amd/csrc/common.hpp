@@ -105,12 +105,22 @@ __device__ __forceinline__ void st16(char* p, u32x4 v) {
 // nontemporal stores alone (0.79 against 0.76 of 8 TB/s); device scope
 // alone, without nt, gained nothing.
 typedef __amdgpu_buffer_rsrc_t WtRange;
+// base must be the same in every lane of the wavefront (it is taken from the
+// first active lane, so the compiler keeps the descriptor in scalar
+// registers where it cannot prove that itself).
 __device__ __forceinline__ WtRange wt_range(const char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+  const uint64_t b = (uint64_t)base;
+  // (readfirstlane returns int: zero-extend each half through uint32_t)
+  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                     (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, (int)bytes, 0x00020000);
 }
+constexpr int kNtSc1 = 2 | 16;  // cache-policy operand: nt (bit 1), sc1 (bit 4)
 __device__ __forceinline__ void st16_wt(WtRange r, uint32_t off, u32x4 v) {
-  constexpr int kNtSc1 = 2 | 16;  // cache-policy operand: nt (bit 1), sc1 (bit 4)
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNtSc1);
+}
+__device__ __forceinline__ void st8_wt(WtRange r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kNtSc1);
 }
 
 // Raw 8-element group as stored (fp32: 8 words; 16-bit: 4 words).
@@ -118,6 +128,13 @@ template <int DT>
 struct Raw8 {
   u32x4 w[DT == DT_F32 ? 2 : 1];
 };
+
+// A whole group stored write-through at byte offset off of range r.
+template <int DT>
+__device__ __forceinline__ void store_raw8_wt(WtRange r, uint32_t off, const Raw8<DT>& v) {
+  st16_wt(r, off, v.w[0]);
+  if constexpr (DT == DT_F32) st16_wt(r, off + 16, v.w[1]);
+}
 
 template <int DT, bool NT>
 __device__ __forceinline__ Raw8<DT> load_raw8(const char* base, uint64_t elem) {

@@ -202,7 +202,9 @@ __device__ __forceinline__ void pipe_h16_tile(const PipeArgs& a, int N, uint32_t
   for (int g = 0; g < G; ++g) {
     const u32x4 y = load_msg(N, g);
     if constexpr (FULL) {
-      for (int d = 0; d < N; ++d) st16<true>(a.bufs.p[d] + eoff[g], y);
+      // write-through stores over the tile's range in each rank
+      constexpr uint32_t kBytes = (uint32_t)kThreads * kGroupElems * G * 2;
+      for (int d = 0; d < N; ++d) st16_wt(wt_range(a.bufs.p[d] + tile0 * 2, kBytes), (uint32_t)(eoff[g] - tile0 * 2), y);
     } else if (nv[g] > 0) {
       Raw8<DT_F16> yr;
       yr.w[0] = y;

@@ -226,10 +226,12 @@ __global__ __launch_bounds__(kThreads) void tree_fold_kernel(RankPtrs bufs, uint
         for (int v = 0; v < V; ++v)
 #pragma unroll
           for (int i = 0; i < E; ++i) x[rel][v].v[i] = round_to<DT>(x[rel][v].v[i] + x[rel + span][v].v[i]);
+    // write-through stores over the tile's range in each rank
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const u32x4 out = pack16<DT>(x[0][v]);
-      for (int d = 0; d < NR; ++d) st16<true>(bufs.p[d] + elem(v) * ES, out);
+      const uint32_t off = ((uint32_t)v * kThreads + threadIdx.x) * E * ES;
+      for (int d = 0; d < NR; ++d) st16_wt(wt_range(bufs.p[d] + tile0 * ES, (uint32_t)(kTile * ES)), off, out);
     }
     return;
   }
@@ -318,11 +320,13 @@ __global__ __launch_bounds__(kThreads) void copy_jobs_kernel(CopyJobs jobs, uint
     ok[i] = b + 16 <= ahi;
     if (ok[i]) v[i] = ld16<true>(src + b);
   }
+  // write-through stores over the tile's range in each destination
+  const uint64_t tb = alo + (uint64_t)t * kTileBytes;  // the tile's first byte
   for (uint64_t m = mask; m; m &= m - 1) {
-    char* dst = jobs.ptrs.p[__builtin_ctzll(m)];
+    const WtRange rg = wt_range(jobs.ptrs.p[__builtin_ctzll(m)] + tb, (uint32_t)kTileBytes);
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i)
-      if (ok[i]) st16<true>(dst + b0 + (uint64_t)i * kThreads * 16, v[i]);
+      if (ok[i]) st16_wt(rg, (uint32_t)(b0 - tb + (uint64_t)i * kThreads * 16), v[i]);
   }
 }
 

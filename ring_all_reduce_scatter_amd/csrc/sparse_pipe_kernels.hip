@@ -464,7 +464,10 @@ __global__ __launch_bounds__(kThreads) void sparse_pipe_kernel(SpPipeArgs a) {
       const int nv = nvof(g);
       const Raw8<DT> yr = sp_prev ? P[slot(g)] : decode_own(last, g, Raw8<DT>{}, false);
       if (full) {
-        for (int d = 0; d < N; ++d) store_raw8<DT, true>(a.bufs.p[d], ulo + off(g), yr);
+        // write-through stores over the tile's range in each rank
+        const uint64_t t0 = ulo + (uint64_t)k * kTile;
+        for (int d = 0; d < N; ++d)
+          store_raw8_wt<DT>(wt_range(a.bufs.p[d] + t0 * ES, (uint32_t)(kTile * ES)), (uint32_t)((ulo + off(g) - t0) * ES), yr);
       } else if (nv > 0) {
         const G8 y = unpack8<DT>(yr);
         for (int d = 0; d < N; ++d) store_part8<DT>(a.bufs.p[d], ulo + off(g), nv, y);
