@@ -78,14 +78,20 @@ hipError_t launch_seg_copy(const SegJobs& jobs, hipStream_t stream) {
 // of the 200-tensor workload, 0.663 of 8 TB/s against 0.693 with tensor
 // sizes rounded to 64 elements.)
 //
-// Workgroups go chunk fastest, as in the ring fold: workgroup N*i + c of a
-// bucket takes the i-th tile of chunk c (tiles of a chunk in the order of
-// its elements), so the workgroups resident at one time spread over all
-// chunks of the bucket.  (Taking the tiles in the order of the elements
-// instead, with every resident workgroup inside one chunk, measured 0.57 of
-// 8 TB/s on the 200-tensor workload.)  A bucket has N times its largest
-// chunk's tile count workgroups; the slots past a smaller chunk's tiles
-// stay empty.
+// A bucket has N*M workgroup slots, M its largest chunk's tile count (the
+// slots past a smaller chunk's tiles stay empty); a chunk's tiles go in the
+// order of its elements.  The chip hands workgroups to its 8 XCDs in turn
+// (workgroup w to XCD w mod 8), and the HBM rate depends on how many
+// separate ranges each XCD streams at once.  With N a multiple of 8 (every
+// bucket then starts on a multiple of 8 slots) slot 8j + x goes to chunk
+// x + 8*(j / M), tile j mod M: XCD x streams chunk x to its end, then chunk
+// x + 8, and so on.  Otherwise slot N*i + c takes the i-th tile of chunk c
+// (chunk fastest; the same order as above for N = 8).  On 16 bf16 ranks of
+// the 200-tensor workload, fraction of 8 TB/s: 0.735 with the XCD-major
+// order; 0.709 chunk fastest (each XCD alternating between chunks x and
+// x + 8); 0.63 with the chunk rotated by one per tile row (every XCD over
+// every chunk); 0.57 in the order of the elements (every resident
+// workgroup inside one chunk).
 //
 // Device table (uint64 words, written by the host before the launch):
 //   [0]                       number of buckets nb
@@ -169,7 +175,13 @@ __global__ __launch_bounds__(kThreads) void bucket_desc_kernel(const uint64_t* _
   char* dp = descs + g * dstride;
   const uint64_t bk = upper_index(0, nb, g, [&](uint64_t i) { return ld_u64(start + i); });
   const uint64_t local = g - ld_u64(start + bk);
-  const uint64_t c = local % (uint64_t)N, i = local / (uint64_t)N;
+  uint64_t c = local % (uint64_t)N, i = local / (uint64_t)N;
+  if (N % 8 == 0) {  // XCD-major
+    const uint64_t m = (ld_u64(start + bk + 1) - ld_u64(start + bk)) / (uint64_t)N;  // M
+    const uint64_t x = local % 8, j = local / 8;
+    c = x + 8 * (j / m);
+    i = j % m;
+  }
   const uint64_t r0 = ld_u64(crun + bk * N + c), r1 = ld_u64(crun + bk * N + c + 1);
   u32x4 d = {kDescEmpty, 0u, 0u, 0u};
   if (r0 < r1) {
