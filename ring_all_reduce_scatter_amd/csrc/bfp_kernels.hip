@@ -819,7 +819,13 @@ void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, i
 // inputs as 16-byte lanes and moving them to the quad layout with cross-lane
 // permutes (and the results back for 16-byte stores) measured 0.698-0.702
 // against 0.713-0.715: the permutes cost more than the halved load and
-// store counts save.
+// store counts save; regrouping only the output (eight permutes a tile, then
+// 16-byte stores) measured 0.708-0.711 against 0.710-0.712.  Other tile
+// orders: all tiles of one chunk before the next 0.675, the chunk rotated by
+// one per tile row 0.677, each chunk starting at tile c*tiles/N 0.710-0.714.
+// Stores: write-through state and output 0.714-0.717, plain nontemporal
+// output 0.705-0.712, plain nontemporal state 0.693-0.696, both plain
+// 0.711-0.716.
 int state_fold_wgs_per_cu() { return 2; }
 
 template <int DT, int NR, int FB>

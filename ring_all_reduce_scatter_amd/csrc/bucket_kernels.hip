@@ -303,8 +303,9 @@ __global__ __launch_bounds__(kThreads) void bucket_fold_kernel(const char* __res
 }
 
 // Workgroups per CU of the bucket fold: the ring fold's, except 16 bf16
-// ranks at one (the 200-tensor workload, fraction of 8 TB/s: 0.709 at 1,
-// 0.702 at 2, 0.699 at 3, 0.691 at 4; 4096-element tiles: 0.703 at 1).
+// ranks at one (the 200-tensor workload, fraction of 8 TB/s, XCD-major
+// order: 0.742 at 1, 0.732 at 2, 0.716 at 3; chunk fastest: 0.709 at 1,
+// 0.702 at 2, 0.699 at 3, 0.691 at 4, and 4096-element tiles 0.703 at 1).
 int bucket_fold_wgs_per_cu(int dt, int n) { return n == 16 && dt == DT_BF16 ? 1 : fold_wgs_per_cu(dt, n); }
 
 template <int DT, int NR>

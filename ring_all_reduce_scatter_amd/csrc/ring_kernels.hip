@@ -437,7 +437,10 @@ hipError_t pair_dispatch(const RankPtrs& bufs, const PairJobs& pairs, uint64_t c
 // apart, fraction of 8 TB/s): N = 8 keeps one chunk per XCD (K = 1: bf16
 // 0.73, fp32 0.72-0.73; K = 2..32: 0.67-0.70 bf16); N = 16 bf16 (64M per
 // rank) 0.68 at K = 1, 0.718 at K = 32, 0.64-0.66 tiles fastest; N = 16 fp32
-// (32M per rank) 0.67 at K = 1, 0.60-0.67 at K = 2..32, 0.727 tiles fastest.
+// (32M per rank) 0.67 at K = 1, 0.60-0.67 at K = 2..32, 0.727 tiles fastest;
+// at N = 16 each XCD x streaming chunk x to its end and then chunk x + 8
+// measured 0.708 bf16 and 0.707 fp32.  Starting chunk c's tiles at tile
+// c*tiles/N (N = 8 fp32, K = 1) measured 0.751-0.755 against 0.767-0.770.
 uint64_t fold_tile_group(int dt, int n, uint64_t tiles) {
   if (n == 16) return dt == DT_F32 ? (tiles > 0 ? tiles : 1) : 32;
   return 1;
