@@ -825,7 +825,9 @@ void fold_dispatch_nr(const RankPtrs& bufs, int n, uint64_t count, uint64_t L, i
 // one per tile row 0.677, each chunk starting at tile c*tiles/N 0.710-0.714.
 // Stores: write-through state and output 0.714-0.717, plain nontemporal
 // output 0.705-0.712, plain nontemporal state 0.693-0.696, both plain
-// 0.711-0.716.
+// 0.711-0.716.  One quad set per lane (1024-element tiles, half the
+// registers) at three, four and six workgroups per CU: 0.704-0.707,
+// 0.704-0.706 and 0.694-0.698 against 0.707-0.709 on the same box.
 int state_fold_wgs_per_cu() { return 2; }
 
 template <int DT, int NR, int FB>
