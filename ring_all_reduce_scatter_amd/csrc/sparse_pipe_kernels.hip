@@ -530,7 +530,10 @@ __global__ void zero_u64_kernel(uint64_t* p, uint64_t n) {
 // (96 VGPRs; all eight groups: 215).  A tile whose own count is sparse
 // writing its entries before the decision as well (indices at a fixed
 // offset, so that only the header waits for the unit's total): 0.764-0.771
-// against 0.764-0.768 ms.
+// against 0.764-0.768 ms.  Odd gangs starting 3, 6 or 12 us late, so that
+// their decision waits would fall in the other gangs' decodes: 0.761-0.764,
+// 0.761-0.764 and 0.768 ms against 0.758-0.760 (the gangs do not leave
+// the memory idle together; each unit's chain of hops is the bound).
 template <int DT>
 struct SpGroups {
   static constexpr int value = DT == DT_F32 ? 4 : 8;
