@@ -41,6 +41,24 @@ def test_bucketed_matches_oracle(dt, n, algo):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [24, 32, 64])
+def test_bucketed_fold_multiple_of_8_ranks_matches_oracle(dt, n):
+    """Rank counts that are multiples of 8 above 16: the fold's workgroup
+    slots map XCD-major, each XCD taking N/8 chunks one after the other;
+    every chunk's tiles must still be folded exactly once."""
+    sizes = inputs.bucket_sizes(24, lo_exp=3, hi_exp=14, salt=n)
+    th = inputs.bucket_tensors(n, sizes, dtype=dt, salt=n)
+    ref = [[t.copy() for t in th[r]] for r in range(n)]
+    cap = 48 << 10
+    osent, orecv = oracle.bucketed_allreduce(ref, cap, dt=DT_NAMES[dt])
+    got, sent, recv = _run(th, dt, cap)
+    for r in range(n):
+        for t in range(len(sizes)):
+            assert_bits_equal(got[r][t], ref[r][t], f"rank {r} tensor {t}")
+    assert sent == osent and recv == orecv
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("algo", [rar.ALGO_FUSED, rar.ALGO_STEPWISE])
 def test_bucketed_with_empty_tensors_matches_oracle(dt, algo):
     """Zero-length tensors between, before and after others (they share a
