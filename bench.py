@@ -528,6 +528,20 @@ def sparse_leg(args):
     same = bool(torch.equal(firsts["pipelined"].view(torch.int16), firsts["staged"].view(torch.int16)))
     del sets, pristine, firsts
     torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = count // 4
+        log(f"[bench] sparse leg: oracle on a sample of T={sample} per rank")
+        xs_s = inputs.sparse_mix(n, sample, salt=1)
+        dt, tot, core = oracle_runs(lambda: [x.copy() for x in xs_s], lambda b: oracle.ring_allreduce_compressed(
+            b, method=oracle.COMP_SPARSE_AUTO, block=128, mbits=w["mbits"], theta=w["theta"],
+            unit=w["unit_bytes"] // 2), 3)
+        del xs_s
+        out["pipelined"]["cpu_baseline"] = {
+            "value": round(busbw(sample * 2, n, dt * 1e3), 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"N={n}, T={sample} fp16 per rank (1/4 of the workload, same recipe; each chunk one "
+                      f"{w['unit_bytes'] >> 20} MiB unit), median of 3 single-thread runs ({dt:.1f} s each, "
+                      f"{tot:.1f} s in all) pinned to host core {core}"}
     return {"metric": "sparse + BFP-4 compressed all-reduce effective bus GB/s (2T(N-1)/N fp16 bytes per rank)",
             "config": {"workload": f"sparsity-aware compressed ring allreduce, N={n} ranks, T={count} fp16 per rank, "
                                    f"ranks 0-{n // 2 - 1} 95% zeros, threshold {w['theta']}, dense messages BFP "
@@ -562,6 +576,21 @@ def sampled_bfp_parity(xs, got0, L, mbits, per_chunk=64):
             if not np.array_equal(a, e):
                 return "MISMATCH"
     return f"bit-exact on {n * K} sampled blocks"
+
+
+def oracle_runs(make, call, runs):
+    """Single-thread oracle calls on a pinned host core, each on fresh inputs
+    from make() (prepared outside the timed part): median seconds, total
+    seconds, the core."""
+    times = []
+    with pinned_core() as pin:
+        for _ in range(runs):
+            a = make()
+            t = time.perf_counter()
+            call(a)
+            times.append(time.perf_counter() - t)
+    times.sort()
+    return times[len(times) // 2], sum(times), pin.core
 
 
 def extra_legs(args):
@@ -669,6 +698,22 @@ def extra_legs(args):
     ck = COUNTER_KERNELS["bfp_ring_fold_state_f16_n8"]
     out["bfp8_allreduce_fused_error_feedback"]["traffic"] = counter_traffic("bfp_ring_fold_state_f16_n8",
                                                                             ck["sources"])
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = wb["count"] // 16
+        log(f"[bench] stateful leg: oracle on a sample of T={sample} per rank")
+        xs_s = inputs.block_scaled(wb["n"], sample, salt=1)
+        dt, tot, core = oracle_runs(
+            lambda: ([x.copy() for x in xs_s], [np.zeros(sample, dtype=np.float32) for _ in range(wb["n"])]),
+            lambda a: oracle.ring_allreduce_compressed_state(a[0], a[1], oracle.FB_ERROR, block=128, mbits=8,
+                                                             unit=wb["unit_bytes"] // 2), 3)
+        del xs_s
+        out["bfp8_allreduce_fused_error_feedback"]["cpu_baseline"] = {
+            "value": round(busbw(sample * 2, wb["n"], dt * 1e3), 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"N={wb['n']}, T={sample} fp16 per rank with zero binary32 state (1/16 of the workload, "
+                      f"same value recipe), median of 3 single-thread runs ({dt:.1f} s each, {tot:.1f} s in all) "
+                      f"pinned to host core {core}"}
     del sets, pristine, ws, state
     torch.cuda.empty_cache()
     w5 = inputs.WORKLOADS["sparse_bfp4"]
@@ -723,6 +768,20 @@ def extra_legs(args):
                                                                 COUNTER_KERNELS["bucket_fold_bf16_n16"]["sources"])}
     del dev, arena, ws, step
     torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        import oracle
+        k = int(np.searchsorted(np.cumsum(sizes), 32 << 20))  # the first tensors, up to 32M elements
+        sub = sizes[:k]
+        log(f"[bench] bucketed leg: oracle on the first {k} tensors")
+        th_s = inputs.bucket_tensors(wk["n"], sub)
+        dt, _, core = oracle_runs(lambda: th_s, lambda a: oracle.bucketed_allreduce(a, wk["cap_bytes"],
+                                                                                   dt=oracle.BF16), 1)
+        del th_s
+        out["buckets_bf16_allreduce"]["cpu_baseline"] = {
+            "value": round(busbw(sum(sub) * 2, wk["n"], dt * 1e3), 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the workload's first {k} tensors ({sum(sub)} bf16 elements per rank, N={wk['n']}, "
+                      f"same draws), one single-thread run ({dt:.1f} s) pinned to host core {core}"}
     # [P2] exercise: ring vs tree wall-clock on 4 ranks at 1 KB, 1 MB and 16 MB
     rvt = {}
     for nbytes in (1 << 10, 1 << 20, 16 << 20):
