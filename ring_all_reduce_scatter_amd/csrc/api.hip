@@ -1207,7 +1207,9 @@ static size_t bucket_flat_bytes(const size_t* counts, size_t nt, int dtype, size
 // Zero-copy plan: table words (see bucket_kernels.hip) and the launch grid.
 // A run is the elements [a, b) of tensor t that lie in chunk c of its
 // bucket; the fold tiles it from a rounded down to kRunAlign.  A bucket
-// takes N times its largest chunk's tile count workgroups, chunk fastest.
+// takes N times its largest chunk's tile count workgroups, in the order
+// bucket_desc_kernel gives them (XCD-major when N is a multiple of 8, else
+// chunk fastest).
 static void bucket_table(const size_t* counts, size_t nt, int n, int dtype, size_t cap, void* const* tensors,
                          std::vector<uint64_t>& tab, uint64_t* grid, Traffic* tr) {
   const size_t es = es_of(dtype);

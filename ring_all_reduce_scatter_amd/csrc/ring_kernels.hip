@@ -38,8 +38,9 @@ constexpr int kStepVecs = 4;  // ... in rs_step
 constexpr int kCopyVecs = 4;  // ... in copy_jobs
 
 // Workgroup -> (chunk, tile) with the chunk fastest: workgroups resident at
-// the same time cover every chunk (and the ring rotation of every chunk), and
-// the launch order spreads each chunk over all XCDs alike.
+// the same time cover every chunk (and the ring rotation of every chunk).
+// Workgroup w goes to XCD w mod 8, so at N = 8 each XCD streams one chunk;
+// rank counts prime to 8 spread each chunk over all XCDs alike.
 __device__ __forceinline__ void chunk_tile(int N, uint32_t* c, uint32_t* t) {
   *c = blockIdx.x % (uint32_t)N;
   *t = blockIdx.x / (uint32_t)N;
