@@ -799,6 +799,35 @@ def extra_legs(args):
         rvt[f"{nbytes}B"] = row
         del sets, pristine
     out["ring_vs_tree_4ranks_fp32"] = rvt
+    # ring_int: N=4, 1M integer-valued fp32 per rank (32 MiB moved per call), the
+    # exact-sum parity case; small enough that the host's submission of a call
+    # (binding, checks, launch) takes longer than the GPU's work.  Eager: calls
+    # back to back as the host issues them.  Queued: the same calls enqueued
+    # behind a GPU spin of about 2 ms, so they run back to back on the GPU and
+    # the events give the GPU time per call.
+    wi = inputs.WORKLOADS["ring_int"]
+    xi = inputs.integers(wi["n"], wi["count"])
+    pristine = [torch.from_numpy(x).to("cuda:0") for x in xi]
+    sets = make_sets(pristine, 1 + 24)
+    Si = wi["count"] * 4
+    tl = time_leg(lambda b: rar.ring_allreduce(b), sets, 4, 24)
+    stream = torch.cuda.current_stream()
+    qs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(24)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(5_000_000)
+    for i, (a, b) in enumerate(qs):
+        a.record(stream)
+        rar.ring_allreduce(sets[1 + i % 24])
+        b.record(stream)
+    torch.cuda.synchronize()
+    qev = sorted(a.elapsed_time(b) for a, b in qs)
+    qmed = qev[len(qev) // 2]
+    out["ring_int_fp32_4x1M_fused"] = {
+        "eager_us_per_call": round(tl[0] * 1e3, 2), "eager_event_us_median": round(tl.median_ms * 1e3, 2),
+        "queued_event_us_median": round(qmed * 1e3, 2), "queued_event_us_min": round(qev[0] * 1e3, 2),
+        "frac_of_roofline_queued": round(2 * wi["n"] * Si / (qmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, pristine
+    torch.cuda.empty_cache()
     for name, fn, cnt in (("fp32_broadcast_fused", lambda b: rar.broadcast(b, 0), w5["bcast_count"]),
                           ("fp32_allgather_fused", lambda b: rar.allgather(b), w5["ag_shard"] * 8)):
         xf = inputs.filler(8, cnt)
