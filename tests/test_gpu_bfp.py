@@ -126,6 +126,22 @@ def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
     assert sent == osent and recv == orecv
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("n", [6, 16])
+@pytest.mark.parametrize("sched", ["fused", "staged", "forward", "pipelined"])
+def test_compressed_allreduce_more_ranks_matches_oracle(dt, n, sched):
+    """Rank counts without a specialised kernel (6) and the largest common
+    one (16): the generic-N hop chains of every schedule."""
+    count = n * 4096 * 2 + 777
+    xs = inputs.block_scaled(n, count, dtype=dt, salt=n * 10 + 3)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce_compressed(ref, mbits=8, unit=4096, dt=DT_NAMES[dt])
+    got, sent, recv = _run_compressed(xs, dt, sched, mbits=8)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+    assert sent == osent and recv == orecv
+
+
 @pytest.mark.parametrize("block", [16, 64, 256, 512])
 @pytest.mark.parametrize("sched", ["fused", "staged", "forward", "pipelined"])
 def test_compressed_allreduce_other_blocks(block, sched):

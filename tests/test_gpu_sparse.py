@@ -47,6 +47,23 @@ def test_sparse_auto_matches_oracle(dt, n, mbits, sched):
 
 
 @pytest.mark.parametrize("sched", ["staged", "pipelined"])
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+@pytest.mark.parametrize("n", [6, 16])
+def test_sparse_auto_more_ranks_matches_oracle(dt, n, sched):
+    """SPARSE_AUTO over 6 and 16 ranks: the pipelined gang protocol with more
+    hops per unit, half the ranks sparse."""
+    count = n * 4096 * 2 + 1500
+    xs = inputs.sparse_mix(n, count, dtype=dt, salt=100 + n)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce_compressed(ref, method=oracle.COMP_SPARSE_AUTO, mbits=4, unit=4096,
+                                                    dt=DT_NAMES[dt])
+    got, sent, recv = _run_auto(xs, dt, mbits=4, sched=sched)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+    assert sent == osent and recv == orecv
+
+
+@pytest.mark.parametrize("sched", ["staged", "pipelined"])
 @pytest.mark.parametrize("n", [2, 4, 8])
 def test_all_sparse_equals_uncompressed_ring(n, sched):
     count = n * 8192
