@@ -1,6 +1,6 @@
 """GPU parity of the uncompressed collectives against the CPU oracle, bit for
 bit, through the C-ABI (fused and stepwise schedules, all three dtypes,
-ranks 1..16, ragged and empty chunks), and the byte counters against the
+ranks 1..64, ragged and empty chunks), and the byte counters against the
 oracle's."""
 import numpy as np
 import pytest
@@ -131,6 +131,49 @@ def test_broadcast_matches_oracle(n, root, count, algo):
     got = to_host(bufs, "f32")
     for r in range(n):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [32, 64])
+@pytest.mark.parametrize("count", [1000, 70_001])
+@pytest.mark.parametrize("algo", ["fused", "stepwise"])
+def test_allreduce_many_ranks_matches_oracle(dt, n, count, algo):
+    """Up to the largest ring the boundary takes (64 ranks): the fold's
+    run-time rank loop, and 2(N-1) step launches."""
+    xs = _inputs(n, count, dt, salt=count + n)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.ring_allreduce(ref, dt=_oracle_dt(dt))
+    bufs = to_dev(xs, dt)
+    rar.ring_allreduce_ex(bufs, ALGOS[algo])
+    sent, recv = rar.last_traffic(n)
+    got = to_host(bufs, dt)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+    assert sent == osent and recv == orecv
+
+
+@pytest.mark.parametrize("n", [32, 64])
+@pytest.mark.parametrize("algo", ["fused", "stepwise"])
+def test_broadcast_and_allgather_many_ranks_match_oracle(n, algo):
+    """A fan-out to 63 destinations (the whole 64-bit destination mask)."""
+    xs = inputs.filler(n, 5003, salt=n)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.broadcast(ref, root=n - 1)
+    bufs = to_dev(xs, "f32")
+    rar.broadcast_ex(bufs, n - 1, ALGOS[algo])
+    assert rar.last_traffic(n) == (osent, orecv)
+    got = to_host(bufs, "f32")
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"broadcast rank {r}")
+    xs = inputs.filler(n, n * 1001, salt=n + 1)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.allgather(ref, dt=_oracle_dt("f32"))
+    bufs = to_dev(xs, "f32")
+    rar.allgather_ex(bufs, ALGOS[algo])
+    assert rar.last_traffic(n) == (osent, orecv)
+    got = to_host(bufs, "f32")
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"allgather rank {r}")
 
 
 def test_unaligned_shards_copy_exactly():
