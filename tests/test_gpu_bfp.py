@@ -127,11 +127,11 @@ def test_compressed_allreduce_matches_oracle(dt, n, sched, mbits):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("n", [6, 16])
+@pytest.mark.parametrize("n", [6, 16, 64])
 @pytest.mark.parametrize("sched", ["fused", "staged", "forward", "pipelined"])
 def test_compressed_allreduce_more_ranks_matches_oracle(dt, n, sched):
-    """Rank counts without a specialised kernel (6) and the largest common
-    one (16): the generic-N hop chains of every schedule."""
+    """Rank counts without a specialised kernel (6), 16 and the largest the
+    boundary takes (64): the generic-N hop chains of every schedule."""
     count = n * 4096 * 2 + 777
     xs = inputs.block_scaled(n, count, dtype=dt, salt=n * 10 + 3)
     ref = [x.copy() for x in xs]

@@ -48,10 +48,10 @@ def test_sparse_auto_matches_oracle(dt, n, mbits, sched):
 
 @pytest.mark.parametrize("sched", ["staged", "pipelined"])
 @pytest.mark.parametrize("dt", ["f16", "f32"])
-@pytest.mark.parametrize("n", [6, 16])
+@pytest.mark.parametrize("n", [6, 16, 64])
 def test_sparse_auto_more_ranks_matches_oracle(dt, n, sched):
-    """SPARSE_AUTO over 6 and 16 ranks: the pipelined gang protocol with more
-    hops per unit, half the ranks sparse."""
+    """SPARSE_AUTO over 6, 16 and 64 ranks: the pipelined gang protocol with
+    more hops per unit, half the ranks sparse."""
     count = n * 4096 * 2 + 1500
     xs = inputs.sparse_mix(n, count, dtype=dt, salt=100 + n)
     ref = [x.copy() for x in xs]
