@@ -52,6 +52,14 @@ def test_stateful_ring_matches_oracle(fb, dt, n, block, mbits):
 
 
 @pytest.mark.parametrize("fb", ["error", "delta"])
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+@pytest.mark.parametrize("n", [16, 64])
+def test_stateful_ring_many_ranks_matches_oracle(fb, dt, n):
+    """The generic-N stateful fold at 16 and 64 ranks."""
+    _run(dt, n, n * 300 + 517, 128, 8, fb, calls=2)
+
+
+@pytest.mark.parametrize("fb", ["error", "delta"])
 def test_stateful_ring_ragged_and_multi_unit(fb):
     """Chunks longer than one 4 MiB unit, ragged tail, empty trailing chunk."""
     _run("f16", 5, (1 << 21) * 5 + 2049, 128, 8, fb, calls=2, kind="scaled")

@@ -30,6 +30,23 @@ def test_tree_matches_oracle(dt, n, count, algo):
         assert_bits_equal(got[r], ref[r], f"rank {r}")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [32, 64])
+@pytest.mark.parametrize("algo", ["fused", "stepwise"])
+def test_tree_many_ranks_matches_oracle(dt, n, algo):
+    """32 and 64 ranks: rank counts past the fused tree kernel's table."""
+    count = 50_001
+    xs = inputs.gradient_like(n, count, dtype=dt, salt=count + 3 * n)
+    ref = [x.copy() for x in xs]
+    osent, orecv = oracle.tree_allreduce(ref, dt=DT_NAMES[dt])
+    bufs = to_dev(xs, dt)
+    rar.tree_allreduce_ex(bufs, ALGOS[algo])
+    assert rar.last_traffic(n) == (osent, orecv)
+    got = to_host(bufs, dt)
+    for r in range(n):
+        assert_bits_equal(got[r], ref[r], f"rank {r}")
+
+
 @pytest.mark.parametrize("count,expect", [(1000, rar.ALLREDUCE_TREE), ((1 << 18) - 1, rar.ALLREDUCE_TREE),
                                           (1 << 18, rar.ALLREDUCE_RING), (1 << 20, rar.ALLREDUCE_RING)])
 def test_auto_selects_by_size(count, expect):
