@@ -61,7 +61,7 @@ def test_fused_fold_tile_orders_at_16_ranks(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("n", [2, 3, 8])
+@pytest.mark.parametrize("n", [2, 3, 8, 16, 64])
 @pytest.mark.parametrize("algo", ["fused", "stepwise"])
 def test_reduce_scatter_matches_oracle(dt, n, algo):
     count = 50_000
@@ -79,7 +79,7 @@ def test_reduce_scatter_matches_oracle(dt, n, algo):
             assert_bits_equal(got[r], ref[r], f"rank {r} state")
 
 
-@pytest.mark.parametrize("n", [2, 4, 5, 8])
+@pytest.mark.parametrize("n", [2, 4, 5, 8, 16])
 def test_single_steps_match_oracle_state(n):
     count = 3 * 4096 + 300
     xs = _inputs(n, count, "f32", salt=100 + n)
