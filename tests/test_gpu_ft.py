@@ -40,7 +40,7 @@ def test_rank_hashes_see_a_single_bit_and_sign_of_zero():
     assert rar.rank_hashes(to_dev([z, -z], "f32"), _ws(512)) == [oracle.hash64(z), oracle.hash64(-z)]
 
 
-@pytest.mark.parametrize("n", [2, 3, 5, 8])
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 64])
 def test_shared_state_sync_matches_oracle(n):
     base = inputs.gradient_like(1, 300_001, salt=n)[0]
     host = [base.copy() for _ in range(n)]
@@ -84,7 +84,7 @@ def test_ft_ring_matches_oracle(dt, plan, count):
     assert len({rep["hash"][r] for r in rep["survivors"]}) == 1
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 16])
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 64])
 def test_ft_ring_other_rank_counts(n):
     count = 50_000
     xs = inputs.gradient_like(n, count, salt=n)
